@@ -1,0 +1,213 @@
+"""fp64 CPU oracle of the double-binary factorized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` use it; the library in ``bit_adapters_amd``
+never imports, links or runs anything here, and nothing here imports the
+library.  Inputs come from ``bit_adapters_amd.synth`` (random draws only).
+
+The arithmetic lives in ``dbf_oracle.c`` (plain C, fp64, fixed summation
+order); this module only widens the stored types to fp64 and calls it:
+
+* ``forward``   -- y = sum_i diag(alpha_i) B1_i diag(beta_i) B2_i diag(gamma_i) x,
+  the parametrization of Delta W on the LoRDBA page (section 2, "Arquitetura
+  Central"), which is the DBF approximation (DBF technical summary,
+  section 2) for one term and the multi-kernel sum of the Multi-Boolean page
+  (technical summary, section 2, item 2) for several terms;
+* ``dense``     -- the frozen base W0 x of LoRDBA's unmerged adapter mode
+  (LoRDBA sections 1 and 5);
+* ``forward_int`` -- exact integer sign sums for int8 activations;
+* ``pack`` / ``unpack`` -- the uint32 bit layout written out from its
+  definition, one bit at a time.
+
+Every function is pinned by tests/test_oracle_pins.py against closed forms,
+invariants and brute force; the pack layout is additionally pinned by a
+hand-derived fixture under tests/golden/.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "dbf_oracle.c")
+LIBRARY = os.path.join(_HERE, "libdbf_oracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i8p = ctypes.POINTER(ctypes.c_int8)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i64 = ctypes.c_int64
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (no fast-math, OpenMP for the outer
+    loops)."""
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", source, "-o", output + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+class Oracle:
+    """A loaded oracle library (the default one, or a variant built from
+    another source file, which the mutation tests use)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            build(SOURCE, path)
+        lib = ctypes.CDLL(path)
+        lib.dbf_oracle_forward.restype = ctypes.c_int
+        lib.dbf_oracle_forward.argtypes = [
+            ctypes.c_int, _i64, _i64, _i64, _i64,
+            ctypes.POINTER(_i8p), ctypes.POINTER(_i8p),
+            ctypes.POINTER(_dp), ctypes.POINTER(_dp), ctypes.POINTER(_dp),
+            _dp, _dp]
+        lib.dbf_oracle_dense.restype = None
+        lib.dbf_oracle_dense.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp]
+        lib.dbf_oracle_forward_int.restype = None
+        lib.dbf_oracle_forward_int.argtypes = [
+            ctypes.c_int, _i64, _i64, _i64, _i64,
+            ctypes.POINTER(_i8p), ctypes.POINTER(_i8p), _i8p, _i64p, _i64p]
+        lib.dbf_oracle_packed_words.restype = _i64
+        lib.dbf_oracle_packed_words.argtypes = [_i64, _i64]
+        lib.dbf_oracle_pack.restype = None
+        lib.dbf_oracle_pack.argtypes = [_dp, _i64, _i64, _u32p]
+        lib.dbf_oracle_unpack.restype = None
+        lib.dbf_oracle_unpack.argtypes = [_u32p, _i64, _i64, _i8p]
+        lib.dbf_oracle_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    # -- the layer -------------------------------------------------------
+    def forward(self, terms, x) -> np.ndarray:
+        """y [T x N] in fp64 for fp64 activations x [T x M] and a list of
+        terms (dicts with int8 b1 [N x R], b2 [R x M] and alpha, beta, gamma
+        convertible to fp64)."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        T, M = x.shape
+        L = len(terms)
+        N, R = terms[0]["b1"].shape
+        keep = []
+
+        def arr(a, dt):
+            a = np.ascontiguousarray(a, dtype=dt)
+            keep.append(a)
+            return a
+
+        b1 = [arr(t["b1"], np.int8) for t in terms]
+        b2 = [arr(t["b2"], np.int8) for t in terms]
+        for t in terms:
+            assert t["b1"].shape == (N, R) and t["b2"].shape == (R, M)
+        al = [arr(t["alpha"], np.float64) for t in terms]
+        be = [arr(t["beta"], np.float64) for t in terms]
+        ga = [arr(t["gamma"], np.float64) for t in terms]
+        y = np.empty((T, N), dtype=np.float64)
+        P8 = (_i8p * L)(*[a.ctypes.data_as(_i8p) for a in b1])
+        Q8 = (_i8p * L)(*[a.ctypes.data_as(_i8p) for a in b2])
+        A = (_dp * L)(*[a.ctypes.data_as(_dp) for a in al])
+        B = (_dp * L)(*[a.ctypes.data_as(_dp) for a in be])
+        G = (_dp * L)(*[a.ctypes.data_as(_dp) for a in ga])
+        rc = self.lib.dbf_oracle_forward(L, N, M, R, T, P8, Q8, A, B, G,
+                                         x.ctypes.data_as(_dp),
+                                         y.ctypes.data_as(_dp))
+        if rc != 0:
+            raise MemoryError("oracle scratch allocation failed")
+        return y
+
+    def dense(self, w0, x) -> np.ndarray:
+        """W0 x for every token: [T x N] fp64."""
+        w0 = np.ascontiguousarray(w0, dtype=np.float64)
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        N, M = w0.shape
+        T = x.shape[0]
+        y = np.zeros((T, N), dtype=np.float64)
+        self.lib.dbf_oracle_dense(N, M, T, w0.ctypes.data_as(_dp),
+                                  x.ctypes.data_as(_dp), y.ctypes.data_as(_dp))
+        return y
+
+    def adapter(self, w0, terms, x) -> np.ndarray:
+        """Unmerged adapter mode: Delta W x first, then W0 x added."""
+        y = self.forward(terms, x) if terms else np.zeros(
+            (x.shape[0], w0.shape[0]))
+        return y + self.dense(w0, x)
+
+    def forward_int(self, terms, xq):
+        """Exact int64 sign sums (s1 [L x T x R], s2 [L x T x N]) for int8
+        activations."""
+        xq = np.ascontiguousarray(xq, dtype=np.int8)
+        T, M = xq.shape
+        L = len(terms)
+        N, R = terms[0]["b1"].shape
+        b1 = [np.ascontiguousarray(t["b1"], dtype=np.int8) for t in terms]
+        b2 = [np.ascontiguousarray(t["b2"], dtype=np.int8) for t in terms]
+        s1 = np.empty((L, T, R), dtype=np.int64)
+        s2 = np.empty((L, T, N), dtype=np.int64)
+        P8 = (_i8p * L)(*[a.ctypes.data_as(_i8p) for a in b1])
+        Q8 = (_i8p * L)(*[a.ctypes.data_as(_i8p) for a in b2])
+        self.lib.dbf_oracle_forward_int(L, N, M, R, T, P8, Q8,
+                                        xq.ctypes.data_as(_i8p),
+                                        s1.ctypes.data_as(_i64p),
+                                        s2.ctypes.data_as(_i64p))
+        return s1, s2
+
+    # -- the bit layout -------------------------------------------------
+    def packed_words(self, rows: int, K: int) -> int:
+        return int(self.lib.dbf_oracle_packed_words(rows, K))
+
+    def pack(self, values) -> np.ndarray:
+        """uint32 words of the sign layout; bit = (value >= 0)."""
+        v = np.ascontiguousarray(values, dtype=np.float64)
+        rows, K = v.shape
+        out = np.empty(self.packed_words(rows, K), dtype=np.uint32)
+        self.lib.dbf_oracle_pack(v.ctypes.data_as(_dp), rows, K,
+                                 out.ctypes.data_as(_u32p))
+        return out
+
+    def unpack(self, words, rows: int, K: int) -> np.ndarray:
+        w = np.ascontiguousarray(words, dtype=np.uint32)
+        assert w.size == self.packed_words(rows, K)
+        s = np.empty((rows, K), dtype=np.int8)
+        self.lib.dbf_oracle_unpack(w.ctypes.data_as(_u32p), rows, K,
+                                   s.ctypes.data_as(_i8p))
+        return s
+
+    def threads(self) -> int:
+        return int(self.lib.dbf_oracle_threads())
+
+
+# -- widening of the stored types to fp64 (exact) ------------------------
+def widen_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) to fp64: a bf16 value is the upper half of
+    the fp32 with the same bits."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def widen(a, kind: str) -> np.ndarray:
+    """Stored activations or weights to fp64: kind is 'bf16' (uint16 bit
+    patterns), 'f16', 'f32' or 'i8'."""
+    if kind == "bf16":
+        return widen_bf16(a)
+    return np.asarray(a).astype(np.float64)
+
+
+def terms64(layer) -> list:
+    """The layer's terms with the fp16 scales widened to fp64 (exact)."""
+    return [dict(b1=t["b1"], b2=t["b2"],
+                 alpha=np.asarray(t["alpha"], dtype=np.float64),
+                 beta=np.asarray(t["beta"], dtype=np.float64),
+                 gamma=np.asarray(t["gamma"], dtype=np.float64))
+            for t in layer["terms"]]
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,397 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+None of the pages prints a worked numerical example, so every pin is
+mathematics the parametrization fixes:
+
+* brute force: Delta W materialised with numpy matrix products (a library
+  primitive) from the LoRDBA parametrization (section 2, "Arquitetura
+  Central") and applied to x; on small-integer data both sides are exact and
+  must agree bit for bit;
+* the DBF page's own Hadamard form (technical summary, section 2),
+  (a . A . m^T)(B . b^T), evaluated with broadcasting;
+* closed forms: all-ones signs, rank 1;
+* invariants: flipping a row of B1 negates exactly that output, the gauge
+  flip (row r of B2 with column r of B1) and the column flip (column m of B2
+  against -x_m) change nothing, a consistent permutation of the inner index,
+  power-of-two homogeneity, additivity over terms;
+* the integer path against Python big integers;
+* the dense base against numpy;
+* the bit layout against hand-derived fixtures (tests/golden/) and
+  counting invariants.
+
+``test_mutants_are_caught`` plants plausible mistakes in a copy of the
+oracle's C source, on the CPU, and checks that some pin fails for each.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_layer(N, M, R, L, seed, integer=False):
+    g = np.random.default_rng([7, seed, N, M, R, L])
+    terms = []
+    for _ in range(L):
+        b1 = (g.integers(0, 2, (N, R)) * 2 - 1).astype(np.int8)
+        b2 = (g.integers(0, 2, (R, M)) * 2 - 1).astype(np.int8)
+        if integer:
+            a, b, c = (g.integers(1, 4, n).astype(np.float64) for n in (N, R, M))
+        else:
+            a = g.uniform(0.5, 1.5, N).astype(np.float16).astype(np.float64)
+            b = g.uniform(0.5, 1.5, R).astype(np.float16).astype(np.float64)
+            c = g.uniform(0.5, 1.5, M).astype(np.float16).astype(np.float64)
+        terms.append(dict(b1=b1, b2=b2, alpha=a, beta=b, gamma=c))
+    return terms
+
+
+def _rand_x(T, M, seed, integer=False):
+    g = np.random.default_rng([8, seed, T, M])
+    if integer:
+        return g.integers(-3, 4, (T, M)).astype(np.float64)
+    return g.standard_normal((T, M))
+
+
+def _dense_delta_w(terms):
+    """Delta W = sum_i diag(alpha) B1 diag(beta) B2 diag(gamma), materialised
+    with numpy matrix products."""
+    dw = 0.0
+    for t in terms:
+        left = t["alpha"][:, None] * t["b1"].astype(np.float64)
+        mid = t["beta"][:, None] * t["b2"].astype(np.float64)
+        dw = dw + (left @ mid) * t["gamma"][None, :]
+    return dw
+
+
+SHAPES = [(1, 1, 1, 1), (2, 3, 5, 1), (8, 5, 3, 2), (33, 65, 32, 3),
+          (64, 33, 65, 1), (5, 8, 2, 3)]
+
+
+# --------------------------------------------------------------------------
+# pins; each takes an Oracle and raises AssertionError on a mismatch
+# --------------------------------------------------------------------------
+def pin_bruteforce_real(o):
+    for k, (N, M, R, L) in enumerate(SHAPES):
+        terms = _rand_layer(N, M, R, L, k)
+        x = _rand_x(3, M, k)
+        y = o.forward(terms, x)
+        ref = x @ _dense_delta_w(terms).T
+        err = np.abs(y - ref).max() / max(np.abs(ref).max(), 1e-300)
+        assert err <= 1e-12, (N, M, R, L, err)
+
+
+def pin_bruteforce_exact(o):
+    for k, (N, M, R, L) in enumerate(SHAPES):
+        terms = _rand_layer(N, M, R, L, 100 + k, integer=True)
+        x = _rand_x(2, M, 100 + k, integer=True)
+        y = o.forward(terms, x)
+        ref = x @ _dense_delta_w(terms).T
+        assert np.array_equal(y, ref), (N, M, R, L)
+
+
+def pin_dbf_hadamard_form(o):
+    # DBF: W ~ (a . A . m^T)(B . b^T) with a = alpha, A = B1, m = beta,
+    # B = B2, b = gamma; broadcasting products, one term.
+    for k, (N, M, R, _) in enumerate(SHAPES):
+        t = _rand_layer(N, M, R, 1, 200 + k)[0]
+        a, A, m = t["alpha"], t["b1"].astype(np.float64), t["beta"]
+        B, b = t["b2"].astype(np.float64), t["gamma"]
+        W = (a[:, None] * A * m[None, :]) @ (B * b[None, :])
+        x = _rand_x(2, M, 200 + k)
+        y = o.forward([t], x)
+        ref = x @ W.T
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def pin_all_ones(o):
+    # B1 = B2 = 1:  y_n = sum_i alpha_n (sum_r beta_r) (sum_m gamma_m x_m)
+    for integer in (True, False):
+        terms = _rand_layer(7, 9, 4, 3, 300, integer=integer)
+        for t in terms:
+            t["b1"][:] = 1
+            t["b2"][:] = 1
+        x = _rand_x(2, 9, 300, integer=integer)
+        y = o.forward(terms, x)
+        ref = sum(t["alpha"][None, :] * t["beta"].sum()
+                  * (x * t["gamma"][None, :]).sum(axis=1)[:, None]
+                  for t in terms)
+        if integer:
+            assert np.array_equal(y, ref)
+        else:
+            assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_rank_one(o):
+    # R = 1: Delta W = (alpha . b1) beta (b2 . gamma)^T, an outer product
+    terms = _rand_layer(6, 11, 1, 1, 400)
+    t = terms[0]
+    x = _rand_x(3, 11, 400)
+    y = o.forward(terms, x)
+    left = t["alpha"] * t["b1"][:, 0]
+    right = t["b2"][0, :] * t["gamma"]
+    ref = (x @ right)[:, None] * t["beta"][0] * left[None, :]
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+
+
+def pin_row_flip(o):
+    # flipping row n0 of every B1 negates y[:, n0] exactly, nothing else moves
+    terms = _rand_layer(9, 13, 5, 2, 500)
+    x = _rand_x(2, 13, 500)
+    y = o.forward(terms, x)
+    n0 = 4
+    for t in terms:
+        t["b1"][n0, :] *= -1
+    y2 = o.forward(terms, x)
+    assert np.array_equal(y2[:, n0], -y[:, n0])
+    rest = [n for n in range(9) if n != n0]
+    assert np.array_equal(y2[:, rest], y[:, rest])
+
+
+def pin_gauge(o):
+    # flipping row r0 of B2 together with column r0 of B1 leaves y unchanged
+    terms = _rand_layer(9, 13, 5, 2, 600)
+    x = _rand_x(2, 13, 600)
+    y = o.forward(terms, x)
+    r0 = 2
+    terms[1]["b2"][r0, :] *= -1
+    terms[1]["b1"][:, r0] *= -1
+    assert np.array_equal(o.forward(terms, x), y)
+
+
+def pin_column_flip(o):
+    # flipping column m0 of every B2 is the same as negating x[:, m0]
+    terms = _rand_layer(9, 13, 5, 2, 700)
+    x = _rand_x(2, 13, 700)
+    m0 = 6
+    x2 = x.copy()
+    x2[:, m0] *= -1
+    y = o.forward(terms, x2)
+    for t in terms:
+        t["b2"][:, m0] *= -1
+    assert np.array_equal(o.forward(terms, x), y)
+
+
+def pin_permutation(o):
+    terms = _rand_layer(10, 12, 7, 2, 800)
+    x = _rand_x(2, 12, 800)
+    y = o.forward(terms, x)
+    p = np.random.default_rng(1).permutation(7)
+    for t in terms:
+        t["b1"] = t["b1"][:, p].copy()
+        t["b2"] = t["b2"][p, :].copy()
+        t["beta"] = t["beta"][p].copy()
+    y2 = o.forward(terms, x)
+    assert np.allclose(y2, y, rtol=1e-13, atol=1e-13 * np.abs(y).max())
+
+
+def pin_homogeneity(o):
+    terms = _rand_layer(10, 12, 7, 2, 900)
+    x = _rand_x(2, 12, 900)
+    y = o.forward(terms, x)
+    for t in terms:
+        t["alpha"] = t["alpha"] * 2.0
+        t["beta"] = t["beta"] * 4.0
+        t["gamma"] = t["gamma"] * 0.5
+    y2 = o.forward(terms, x * 8.0)
+    assert np.array_equal(y2, y * 32.0)
+
+
+def pin_additivity(o):
+    terms = _rand_layer(10, 12, 7, 3, 1000)
+    x = _rand_x(3, 12, 1000)
+    y = o.forward(terms, x)
+    parts = [o.forward([t], x) for t in terms]
+    assert np.allclose(y, sum(parts), rtol=1e-14, atol=1e-14 * np.abs(y).max())
+    # and each part is really there: dropping one term changes the result
+    assert not np.allclose(o.forward(terms[:2], x), y)
+
+
+def pin_int_bigint(o):
+    for k, (N, M, R, L) in enumerate(SHAPES):
+        terms = _rand_layer(N, M, R, L, 1100 + k)
+        g = np.random.default_rng([9, k])
+        xq = g.integers(-127, 128, (2, M)).astype(np.int8)
+        s1, s2 = o.forward_int(terms, xq)
+        for i, t in enumerate(terms):
+            for tok in range(2):
+                xs = [int(v) for v in xq[tok]]
+                ref1 = [sum(int(t["b2"][r, m]) * xs[m] for m in range(M))
+                        for r in range(R)]
+                ref2 = [sum(int(t["b1"][n, r]) * ref1[r] for r in range(R))
+                        for n in range(N)]
+                assert list(s1[i, tok]) == ref1
+                assert list(s2[i, tok]) == ref2
+
+
+def pin_int_all_ones(o):
+    terms = _rand_layer(5, 9, 3, 1, 1200)
+    terms[0]["b1"][:] = 1
+    terms[0]["b2"][:] = 1
+    xq = np.random.default_rng(3).integers(-127, 128, (2, 9)).astype(np.int8)
+    s1, s2 = o.forward_int(terms, xq)
+    tot = xq.astype(np.int64).sum(axis=1)
+    assert np.array_equal(s1[0], np.repeat(tot[:, None], 3, axis=1))
+    assert np.array_equal(s2[0], np.repeat(3 * tot[:, None], 5, axis=1))
+
+
+def pin_dense(o):
+    g = np.random.default_rng(11)
+    w0 = g.standard_normal((13, 17)) * 0.02
+    x = g.standard_normal((3, 17))
+    ref = x @ w0.T
+    assert np.allclose(o.dense(w0, x), ref, rtol=1e-13, atol=1e-15)
+    wi = g.integers(-5, 6, (13, 17)).astype(np.float64)
+    xi = g.integers(-5, 6, (3, 17)).astype(np.float64)
+    assert np.array_equal(o.dense(wi, xi), xi @ wi.T)
+
+
+def _read_fixture(name):
+    rows = K = None
+    plus, plusrows, words = [], [], {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].split()
+            if not line:
+                continue
+            if line[0] == "shape":
+                rows, K = int(line[1]), int(line[2])
+            elif line[0] == "plus":
+                plus.append((int(line[1]), int(line[2])))
+            elif line[0] == "plusrow":
+                plusrows.append(int(line[1]))
+            elif line[0] == "word":
+                words[int(line[1])] = int(line[2], 16)
+    S = -np.ones((rows, K))
+    for r, k in plus:
+        S[r, k] = 1.0
+    for r in plusrows:
+        S[r, :] = 1.0
+    return S, words
+
+
+FIXTURES = ["pack_2x40.txt", "pack_65x130.txt", "pack_3x16.txt"]
+FIXTURE_WORDS = {"pack_2x40.txt": 128, "pack_65x130.txt": 1024,
+                 "pack_3x16.txt": 64}
+
+
+def pin_pack_golden(o):
+    for name in FIXTURES:
+        S, words = _read_fixture(name)
+        got = o.pack(S)
+        assert got.size == FIXTURE_WORDS[name], name
+        exp = np.zeros(got.size, dtype=np.uint32)
+        for i, v in words.items():
+            exp[i] = v
+        assert np.array_equal(got, exp), name
+        assert np.array_equal(o.unpack(exp, *S.shape), S.astype(np.int8)), name
+
+
+def pin_pack_counts(o):
+    g = np.random.default_rng(12)
+    for rows, K in [(1, 1), (3, 31), (64, 32), (65, 33), (70, 97), (130, 300),
+                    (16, 4096), (4096, 16)]:
+        v = g.standard_normal((rows, K))
+        w = o.pack(v)
+        pop = int(np.unpackbits(w.view(np.uint8)).sum())
+        assert pop == int((v >= 0).sum()), (rows, K)
+        # all +1: exactly rows*K set bits, the padding stays 0
+        assert int(np.unpackbits(o.pack(np.ones((rows, K))).view(np.uint8)).sum()) == rows * K
+        assert np.array_equal(o.unpack(w, rows, K), np.where(v >= 0, 1, -1))
+    # sign convention: 0 and -0.0 are +1, NaN and negatives are -1
+    v = np.array([[0.0, -0.0, np.nan, -1e-300, 1e-300, -np.inf, np.inf]])
+    assert np.array_equal(o.unpack(o.pack(v), 1, 7), [[1, 1, -1, -1, 1, -1, 1]])
+
+
+PINS = [pin_bruteforce_real, pin_bruteforce_exact, pin_dbf_hadamard_form,
+        pin_all_ones, pin_rank_one, pin_row_flip, pin_gauge, pin_column_flip,
+        pin_permutation, pin_homogeneity, pin_additivity, pin_int_bigint,
+        pin_int_all_ones, pin_dense, pin_pack_golden, pin_pack_counts]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return O.default()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(orc, pin):
+    pin(orc)
+
+
+def test_thread_count_does_not_change_result(orc):
+    terms = _rand_layer(40, 70, 33, 2, 1300)
+    x = _rand_x(3, 70, 1300)
+    y = orc.forward(terms, x)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = ("import numpy as np, sys; sys.path.insert(0, %r); import oracle as O;"
+            "d = np.load(sys.argv[1]); terms=[dict(b1=d['b1%%d'%%i], b2=d['b2%%d'%%i],"
+            "alpha=d['a%%d'%%i], beta=d['b%%d'%%i], gamma=d['g%%d'%%i]) for i in range(2)];"
+            "np.save(sys.argv[2], O.Oracle().forward(terms, d['x']))"
+            % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    with tempfile.TemporaryDirectory() as td:
+        arrs = {"x": x}
+        for i, t in enumerate(terms):
+            arrs.update({"b1%d" % i: t["b1"], "b2%d" % i: t["b2"],
+                         "a%d" % i: t["alpha"], "b%d" % i: t["beta"],
+                         "g%d" % i: t["gamma"]})
+        np.savez(os.path.join(td, "in.npz"), **arrs)
+        subprocess.run(["python", "-c", code, os.path.join(td, "in.npz"),
+                        os.path.join(td, "out.npy")], check=True, env=env)
+        y1 = np.load(os.path.join(td, "out.npy"))
+    assert np.array_equal(y, y1)
+
+
+# (description, original text, planted mistake)
+MUTANTS = [
+    ("gamma dropped", "u[m] = g[m] * xt[m];", "u[m] = xt[m];"),
+    ("beta dropped", "v[r] = be[r] * s;", "v[r] = s;"),
+    ("alpha dropped", "yt[n] += a[n] * s;", "yt[n] += s;"),
+    ("stage-1 sign", "s += (row[m] > 0) ? u[m] : -u[m];",
+     "s += (row[m] > 0) ? u[m] : u[m];"),
+    ("stage-2 sign", "s += (row[r] > 0) ? v[r] : -v[r];",
+     "s += (row[r] > 0) ? -v[r] : v[r];"),
+    ("B2 read transposed", "s += (row[m] > 0) ? u[m] : -u[m];",
+     "s += (b2[m * R + r] > 0) ? u[m] : -u[m];"),
+    ("B1 read transposed", "s += (row[r] > 0) ? v[r] : -v[r];",
+     "s += (b1[r * N + n] > 0) ? v[r] : -v[r];"),
+    ("terms overwrite", "yt[n] += a[n] * s;", "yt[n] = a[n] * s;"),
+    ("last term dropped", "for (i = 0; i < L; ++i)", "for (i = 0; i + 1 < L; ++i)"),
+    ("dense index", "s += row[m] * xt[m];", "s += row[m] * xt[M - 1 - m];"),
+    ("int sign ignored", "s += (row[m] > 0) ? (int64_t)xt[m] : -(int64_t)xt[m];",
+     "s += (int64_t)xt[m];"),
+    ("int stage-2 transposed", "s += (row[q] > 0) ? o1[q] : -o1[q];",
+     "s += (b1[i][q * N + n] > 0) ? o1[q] : -o1[q];"),
+    ("bit order reversed", "|= (uint32_t)1u << (k % 32);",
+     "|= (uint32_t)1u << (31 - k % 32);"),
+    ("sign of zero", "if (v[r * K + k] >= 0.0)", "if (v[r * K + k] > 0.0)"),
+    ("tile column-major", "return tile * 64 * kw + (r % 64) * kw + w;",
+     "return tile * 64 * kw + w * 64 + (r % 64);"),
+    ("unpack inverted", "& 1u) ? 1 : -1;", "& 1u) ? -1 : 1;"),
+]
+
+
+def test_mutants_are_caught():
+    src = open(O.SOURCE).read()
+    with tempfile.TemporaryDirectory() as td:
+        for desc, old, new in MUTANTS:
+            assert src.count(old) >= 1, desc
+            msrc = os.path.join(td, "m.c")
+            with open(msrc, "w") as f:
+                f.write(src.replace(old, new))
+            lib = os.path.join(td, "m_%d.so" % MUTANTS.index((desc, old, new)))
+            O.build(msrc, lib)
+            mo = O.Oracle(lib)
+            failed = []
+            for pin in PINS:
+                try:
+                    pin(mo)
+                except AssertionError:
+                    failed.append(pin.__name__)
+            assert failed, "planted mistake not caught: " + desc
+    assert shutil.which("gcc")
