@@ -1,0 +1,233 @@
+"""Python binding of libdbf, the gfx950 double-binary factorized linear layer.
+
+The functions carry the names of the C entry points in include/dbf.h and do
+argument marshalling only: they take torch tensors that live on the current
+HIP device, pass their data pointers, sizes and the current stream to the
+library, and raise ``DbfError`` on a non-zero status.  Every step of the
+computation runs in the library's kernels; torch provides device memory and
+the stream.  The library is loaded on first use; if ``libdbf.so`` has not been built
+(``python -m bit_adapters_amd.build``) that use raises ImportError: there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libdbf.so")
+
+_i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+DBF_OK, DBF_EINVAL, DBF_EDTYPE, DBF_EALIGN = 0, -1, -2, -3
+DBF_EWORKSPACE, DBF_EDEVICE, DBF_EUNSUPPORTED, DBF_ELAUNCH = -4, -5, -6, -7
+DBF_F16, DBF_BF16, DBF_F32, DBF_I8, DBF_I32 = 1, 2, 3, 4, 5
+DBF_PATH_AUTO, DBF_PATH_DECODE, DBF_PATH_MFMA = 0, 1, 2
+DBF_MAX_TERMS = 8
+
+EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
+           "dbf_packed_bytes", "dbf_pack", "dbf_unpack", "dbf_workspace_bytes",
+           "dbf_linear_forward", "dbf_linear_forward_i8",
+           "lordba_adapter_forward")
+
+
+class _CTerm(ctypes.Structure):
+    _fields_ = [("b1", _vp), ("b2", _vp), ("alpha", _vp), ("beta", _vp),
+                ("gamma", _vp)]
+
+
+_lib_handle = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libdbf.so (loaded on first use; there is no fallback)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIBRARY):
+        raise ImportError(
+            "libdbf.so is not built; run `python -m bit_adapters_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIBRARY)
+    lib.dbf_abi_version.restype = _int
+    lib.dbf_layout_version.restype = _int
+    lib.dbf_last_error.restype = ctypes.c_char_p
+    lib.dbf_packed_bytes.restype = _sz
+    lib.dbf_packed_bytes.argtypes = [_i64, _i64]
+    lib.dbf_pack.restype = _int
+    lib.dbf_pack.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp]
+    lib.dbf_unpack.restype = _int
+    lib.dbf_unpack.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp]
+    lib.dbf_workspace_bytes.restype = _sz
+    lib.dbf_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _i64, _int]
+    lib.dbf_linear_forward.restype = _int
+    lib.dbf_linear_forward.argtypes = [
+        ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _int, _i64, _i64,
+        _vp, _int, _i64, _int, _vp, _sz, _int, _vp]
+    lib.dbf_linear_forward_i8.restype = _int
+    lib.dbf_linear_forward_i8.argtypes = [
+        ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp,
+        _vp, _vp, _int, _i64, _vp, _sz, _vp]
+    lib.lordba_adapter_forward.restype = _int
+    lib.lordba_adapter_forward.argtypes = [
+        _vp, _i64, ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _i64,
+        _i64, _vp, _int, _i64, _vp, _sz, _vp]
+    _lib_handle = lib
+    return lib
+
+
+class DbfError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("dbf status %d: %s" % (code, message))
+        self.code = code
+
+
+class DbfTerm(NamedTuple):
+    """One term: packed b1 (N x R layout), packed b2 (R x M layout), fp16
+    alpha (N), beta (R), gamma (M); None where the entry point allows."""
+    b1: torch.Tensor
+    b2: torch.Tensor
+    alpha: Optional[torch.Tensor]
+    beta: Optional[torch.Tensor]
+    gamma: Optional[torch.Tensor]
+
+
+_DT = {torch.float16: DBF_F16, torch.bfloat16: DBF_BF16,
+       torch.float32: DBF_F32, torch.int8: DBF_I8, torch.int32: DBF_I32}
+
+
+def _check(rc: int) -> None:
+    if rc != DBF_OK:
+        raise DbfError(rc, library().dbf_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _terms(terms: Sequence[DbfTerm]):
+    arr = (_CTerm * max(1, len(terms)))()
+    for i, t in enumerate(terms):
+        arr[i] = _CTerm(_ptr(t.b1), _ptr(t.b2), _ptr(t.alpha), _ptr(t.beta),
+                        _ptr(t.gamma))
+    return arr
+
+
+def dbf_abi_version() -> int:
+    return library().dbf_abi_version()
+
+
+def dbf_layout_version() -> int:
+    return library().dbf_layout_version()
+
+
+def dbf_last_error() -> str:
+    return library().dbf_last_error().decode()
+
+
+def dbf_packed_bytes(rows: int, k: int) -> int:
+    return int(library().dbf_packed_bytes(rows, k))
+
+
+def dbf_workspace_bytes(N: int, M: int, R: int, n_terms: int, T: int,
+                        path: int = DBF_PATH_AUTO) -> int:
+    return int(library().dbf_workspace_bytes(N, M, R, n_terms, T, path))
+
+
+def dbf_pack(src: torch.Tensor, out: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """Pack the signs of src [rows x k] (int8/f16/bf16/f32, device) into the
+    uint32 layout, returned as an int32 tensor of dbf_packed_bytes/4 words."""
+    rows, k = src.shape
+    nbytes = dbf_packed_bytes(rows, k)
+    if out is None:
+        out = torch.empty(nbytes // 4, dtype=torch.int32, device=src.device)
+    _check(library().dbf_pack(_ptr(src), _DT.get(src.dtype, -1), rows, k, _ld(src),
+                         _ptr(out), _stream(stream)))
+    return out
+
+
+def dbf_unpack(packed: torch.Tensor, rows: int, k: int,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int8, device=packed.device)
+    _check(library().dbf_unpack(_ptr(packed), rows, k, _ptr(out), _ld(out),
+                           _stream(stream)))
+    return out
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def dbf_linear_forward(terms: Sequence[DbfTerm], N: int, M: int, R: int,
+                       x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                       y_dtype: torch.dtype = torch.float32,
+                       accumulate: bool = False, ws: Optional[torch.Tensor] = None,
+                       path: int = DBF_PATH_AUTO, stream=None) -> torch.Tensor:
+    """y (+)= sum_i Delta W_i x for x [T x M] (bf16 or f16)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=y_dtype, device=x.device)
+    ws, wsb = _workspace(dbf_workspace_bytes(N, M, R, len(terms), T, path),
+                         x.device, ws)
+    _check(library().dbf_linear_forward(
+        _terms(terms), len(terms), N, M, R, _ptr(x), _DT.get(x.dtype, -1), T,
+        _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), int(accumulate),
+        _ptr(ws), wsb, path, _stream(stream)))
+    return y
+
+
+def dbf_linear_forward_i8(terms: Sequence[DbfTerm], N: int, M: int, R: int,
+                          x: torch.Tensor, s1: Optional[torch.Tensor] = None,
+                          s2: Optional[torch.Tensor] = None,
+                          y: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None, stream=None):
+    """Integer-activation variant; returns (s1, s2, y) as passed in."""
+    T = x.shape[0]
+    ws, wsb = _workspace(dbf_workspace_bytes(N, M, R, len(terms), T,
+                                             DBF_PATH_DECODE), x.device, ws)
+    ydt = _DT.get(y.dtype, -1) if y is not None else DBF_F32
+    ldy = _ld(y) if y is not None else N
+    _check(library().dbf_linear_forward_i8(
+        _terms(terms), len(terms), N, M, R, _ptr(x), T, _ld(x), _ptr(s1),
+        _ptr(s2), _ptr(y), ydt, ldy, _ptr(ws), wsb, _stream(stream)))
+    return s1, s2, y
+
+
+def lordba_adapter_forward(w0: torch.Tensor, terms: Sequence[DbfTerm], N: int,
+                           M: int, R: int, x: torch.Tensor,
+                           y: Optional[torch.Tensor] = None,
+                           y_dtype: torch.dtype = torch.float32,
+                           ws: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """y = W0 x + sum_i Delta W_i x (bf16 W0 [N x M] and x [T x M])."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=y_dtype, device=x.device)
+    nb = dbf_workspace_bytes(N, M, R, len(terms), T, DBF_PATH_DECODE) if terms else 0
+    ws, wsb = _workspace(nb, x.device, ws)
+    _check(library().lordba_adapter_forward(
+        _ptr(w0), _ld(w0), _terms(terms) if terms else None, len(terms), N, M,
+        R, _ptr(x), T, _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y),
+        _ptr(ws), wsb, _stream(stream)))
+    return y

@@ -1,0 +1,271 @@
+// extern "C" boundary of libdbf: argument validation (before any HIP call),
+// the gfx950 device check, path choice and dispatch to the kernels.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dbf_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+// Decode path up to this many tokens when the caller lets the library pick.
+constexpr int64_t kAutoDecodeMaxT = 16;
+
+int resolve_path(int path, int64_t T) {
+  if (path != DBF_PATH_AUTO) return path;
+  return T <= kAutoDecodeMaxT ? DBF_PATH_DECODE : DBF_PATH_MFMA;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(DBF_EDEVICE, "no HIP device is current");
+  if (dev < kMaxDevices) {
+    const int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return DBF_OK;
+    if (st == 2) return fail(DBF_EDEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(DBF_EDEVICE, "cannot query device %d", dev);
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (!ok) return fail(DBF_EDEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return DBF_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(DBF_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return DBF_OK;
+}
+
+bool out_dtype_ok(int dt) { return dt == DBF_F32 || dt == DBF_BF16 || dt == DBF_F16; }
+
+// Shared validation of the term array (packed factors + scales).
+int check_terms(const dbf_term* terms, int n_terms, bool need_gamma,
+                bool need_ab) {
+  if (!terms) return fail(DBF_EINVAL, "terms is NULL");
+  if (n_terms < 1 || n_terms > DBF_MAX_TERMS)
+    return fail(DBF_EINVAL, "n_terms %d outside 1..%d", n_terms, DBF_MAX_TERMS);
+  for (int i = 0; i < n_terms; ++i) {
+    const dbf_term& t = terms[i];
+    if (!t.b1 || !t.b2) return fail(DBF_EINVAL, "term %d: packed factor is NULL", i);
+    if (!aligned16(t.b1) || !aligned16(t.b2))
+      return fail(DBF_EALIGN, "term %d: packed factor not 16-byte aligned", i);
+    if (need_ab && (!t.alpha || !t.beta))
+      return fail(DBF_EINVAL, "term %d: alpha/beta is NULL", i);
+    if (need_gamma && !t.gamma) return fail(DBF_EINVAL, "term %d: gamma is NULL", i);
+    if ((t.alpha && !aligned2(t.alpha)) || (t.beta && !aligned2(t.beta)) ||
+        (t.gamma && !aligned2(t.gamma)))
+      return fail(DBF_EALIGN, "term %d: a scale vector is not 2-byte aligned", i);
+  }
+  return DBF_OK;
+}
+
+dbf::TermPtrs to_ptrs(const dbf_term* terms, int n_terms) {
+  dbf::TermPtrs p{};
+  p.n = n_terms;
+  for (int i = 0; i < n_terms; ++i) {
+    p.b1[i] = terms[i].b1;
+    p.b2[i] = terms[i].b2;
+    p.alpha[i] = static_cast<const uint16_t*>(terms[i].alpha);
+    p.beta[i] = static_cast<const uint16_t*>(terms[i].beta);
+    p.gamma[i] = static_cast<const uint16_t*>(terms[i].gamma);
+  }
+  return p;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DBF_OK;
+  if (!ws) return fail(DBF_EWORKSPACE, "workspace of %zu bytes needed, got NULL", need);
+  if (ws_bytes < need)
+    return fail(DBF_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(DBF_EALIGN, "workspace not 16-byte aligned");
+  return DBF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dbf_abi_version(void) { return DBF_ABI_VERSION; }
+int dbf_layout_version(void) { return DBF_LAYOUT_VERSION; }
+const char* dbf_last_error(void) { return g_err; }
+
+size_t dbf_packed_bytes(int64_t rows, int64_t k) {
+  if (rows <= 0 || k <= 0) return 0;
+  return static_cast<size_t>(dbf::layout_words(rows, k)) * 4u;
+}
+
+int dbf_pack(const void* src, int src_dtype, int64_t rows, int64_t k,
+             int64_t ld, uint32_t* packed, void* stream) {
+  if (rows < 0 || k < 0) return fail(DBF_EINVAL, "negative size");
+  if (src_dtype != DBF_I8 && src_dtype != DBF_F16 && src_dtype != DBF_BF16 &&
+      src_dtype != DBF_F32)
+    return fail(DBF_EDTYPE, "pack source dtype %d unsupported", src_dtype);
+  if (rows == 0 || k == 0) return DBF_OK;
+  if (!src || !packed) return fail(DBF_EINVAL, "NULL pointer");
+  if (ld < k) return fail(DBF_EINVAL, "ld %lld < k %lld", (long long)ld, (long long)k);
+  if (!aligned16(packed)) return fail(DBF_EALIGN, "packed buffer not 16-byte aligned");
+  const int d = check_device();
+  if (d != DBF_OK) return d;
+  return launched(dbf::launch_pack(src, src_dtype, rows, k, ld, packed,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int dbf_unpack(const uint32_t* packed, int64_t rows, int64_t k, int8_t* dst,
+               int64_t ld, void* stream) {
+  if (rows < 0 || k < 0) return fail(DBF_EINVAL, "negative size");
+  if (rows == 0 || k == 0) return DBF_OK;
+  if (!packed || !dst) return fail(DBF_EINVAL, "NULL pointer");
+  if (ld < k) return fail(DBF_EINVAL, "ld %lld < k %lld", (long long)ld, (long long)k);
+  if (!aligned16(packed)) return fail(DBF_EALIGN, "packed buffer not 16-byte aligned");
+  const int d = check_device();
+  if (d != DBF_OK) return d;
+  return launched(dbf::launch_unpack(packed, rows, k, dst, ld,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
+                           int64_t T, int path) {
+  if (N <= 0 || M <= 0 || R <= 0 || n_terms <= 0 || T <= 0) return 0;
+  if (resolve_path(path, T) == DBF_PATH_MFMA)
+    return dbf::mfma_ws_bytes(N, M, R, n_terms, T);
+  return dbf::decode_ws_bytes(N, M, R, n_terms, T);
+}
+
+int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
+                       int64_t M, int64_t R, const void* x, int x_dtype,
+                       int64_t T, int64_t ldx, void* y, int y_dtype,
+                       int64_t ldy, int accumulate, void* ws, size_t ws_bytes,
+                       int path, void* stream) {
+  int e = check_terms(terms, n_terms, true, true);
+  if (e != DBF_OK) return e;
+  if (N < 1 || M < 1 || R < 1) return fail(DBF_EINVAL, "N, M, R must be >= 1");
+  if (T < 0) return fail(DBF_EINVAL, "T < 0");
+  if (x_dtype != DBF_BF16 && x_dtype != DBF_F16)
+    return fail(DBF_EDTYPE, "x dtype %d unsupported (bf16 or f16)", x_dtype);
+  if (!out_dtype_ok(y_dtype)) return fail(DBF_EDTYPE, "y dtype %d unsupported", y_dtype);
+  if (accumulate != 0 && accumulate != 1) return fail(DBF_EINVAL, "accumulate must be 0 or 1");
+  if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_MFMA)
+    return fail(DBF_EINVAL, "unknown path %d", path);
+  if (T == 0) return DBF_OK;
+  if (!x || !y) return fail(DBF_EINVAL, "x or y is NULL");
+  if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
+  if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
+  if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
+  const int p = resolve_path(path, T);
+  e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, n_terms, T, p));
+  if (e != DBF_OK) return e;
+  e = check_device();
+  if (e != DBF_OK) return e;
+  const dbf::TermPtrs tp = to_ptrs(terms, n_terms);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p == DBF_PATH_MFMA)
+    return launched(dbf::launch_mfma(tp, N, M, R, x, x_dtype, T, ldx, y, y_dtype,
+                                     ldy, accumulate, ws, s));
+  return launched(dbf::launch_decode(tp, N, M, R, x, x_dtype, T, ldx, y, y_dtype,
+                                     ldy, accumulate, ws, s));
+}
+
+int dbf_linear_forward_i8(const dbf_term* terms, int n_terms, int64_t N,
+                          int64_t M, int64_t R, const int8_t* x, int64_t T,
+                          int64_t ldx, int32_t* s1, int32_t* s2, void* y,
+                          int y_dtype, int64_t ldy, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int e = check_terms(terms, n_terms, false, false);
+  if (e != DBF_OK) return e;
+  if (N < 1 || M < 1 || R < 1) return fail(DBF_EINVAL, "N, M, R must be >= 1");
+  if (T < 0) return fail(DBF_EINVAL, "T < 0");
+  bool beta_null = terms[0].beta == nullptr;
+  for (int i = 0; i < n_terms; ++i) {
+    if (terms[i].gamma)
+      return fail(DBF_EINVAL, "term %d: gamma must be NULL (fold it into x upstream)", i);
+    if ((terms[i].beta == nullptr) != beta_null)
+      return fail(DBF_EINVAL, "beta must be NULL in all terms or in none");
+  }
+  if (s2 && !beta_null) return fail(DBF_EINVAL, "s2 needs beta == NULL (beta = 1)");
+  if (y && !out_dtype_ok(y_dtype)) return fail(DBF_EDTYPE, "y dtype %d unsupported", y_dtype);
+  if (static_cast<double>(M) * 127.0 >= 2147483648.0)
+    return fail(DBF_EUNSUPPORTED, "M * 127 does not fit int32");
+  if ((s2 || beta_null) && static_cast<double>(R) * static_cast<double>(M) * 127.0 >= 2147483648.0)
+    return fail(DBF_EUNSUPPORTED, "R * M * 127 does not fit int32");
+  if (T == 0) return DBF_OK;
+  if (!x) return fail(DBF_EINVAL, "x is NULL");
+  if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
+  if (y && ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
+  if (!aligned16(x) || (y && !aligned16(y)) || (s1 && !aligned16(s1)) ||
+      (s2 && !aligned16(s2)))
+    return fail(DBF_EALIGN, "x, y, s1 or s2 not 16-byte aligned");
+  e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, n_terms, T, DBF_PATH_DECODE));
+  if (e != DBF_OK) return e;
+  e = check_device();
+  if (e != DBF_OK) return e;
+  return launched(dbf::launch_decode_i8(to_ptrs(terms, n_terms), N, M, R, x, T,
+                                        ldx, s1, s2, y, y_dtype, ldy, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int lordba_adapter_forward(const void* w0, int64_t ldw, const dbf_term* terms,
+                           int n_terms, int64_t N, int64_t M, int64_t R,
+                           const void* x, int64_t T, int64_t ldx, void* y,
+                           int y_dtype, int64_t ldy, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (n_terms < 0 || n_terms > DBF_MAX_TERMS)
+    return fail(DBF_EINVAL, "n_terms %d outside 0..%d", n_terms, DBF_MAX_TERMS);
+  int e = DBF_OK;
+  if (n_terms > 0) {
+    e = check_terms(terms, n_terms, true, true);
+    if (e != DBF_OK) return e;
+    if (R < 1) return fail(DBF_EINVAL, "R must be >= 1");
+  }
+  if (N < 1 || M < 1) return fail(DBF_EINVAL, "N, M must be >= 1");
+  if (T < 0) return fail(DBF_EINVAL, "T < 0");
+  if (!out_dtype_ok(y_dtype)) return fail(DBF_EDTYPE, "y dtype %d unsupported", y_dtype);
+  if (T == 0) return DBF_OK;
+  if (!w0 || !x || !y) return fail(DBF_EINVAL, "w0, x or y is NULL");
+  if (ldw < M) return fail(DBF_EINVAL, "ldw %lld < M %lld", (long long)ldw, (long long)M);
+  if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
+  if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
+  if (!aligned16(w0) || !aligned16(x) || !aligned16(y))
+    return fail(DBF_EALIGN, "w0, x or y not 16-byte aligned");
+  if (n_terms > 0) {
+    e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, n_terms, T, DBF_PATH_DECODE));
+    if (e != DBF_OK) return e;
+  }
+  e = check_device();
+  if (e != DBF_OK) return e;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  dbf::TermPtrs tp{};
+  int ks = 1;
+  if (n_terms > 0) {
+    tp = to_ptrs(terms, n_terms);
+    const hipError_t h = dbf::launch_decode_stage1(tp, M, R, x, DBF_BF16, T, ldx, ws, s);
+    if (h != hipSuccess) return launched(h);
+    ks = dbf::decode_stage1_splits(M, R, n_terms);
+  }
+  return launched(dbf::launch_adapter(static_cast<const uint16_t*>(w0), ldw, tp,
+                                      N, M, n_terms > 0 ? R : 1, x, T, ldx, y,
+                                      y_dtype, ldy, static_cast<const float*>(ws),
+                                      ks, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Internal declarations shared by the HIP translation units of libdbf.
+// Layout: see include/dbf.h (DBF_LAYOUT_VERSION 1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <algorithm>
+
+#include "dbf.h"
+
+namespace dbf {
+
+constexpr int kTileRows = 64;
+
+// Words per row per tile, tiles along K, tiles along rows.
+__host__ __device__ inline int64_t layout_kw(int64_t K) {
+  int64_t w = (K + 31) / 32;
+  return w < 1 ? 1 : (w > 4 ? 4 : w);
+}
+__host__ __device__ inline int64_t layout_nkb(int64_t K) {
+  int64_t kw = layout_kw(K);
+  return (K + 32 * kw - 1) / (32 * kw);
+}
+__host__ __device__ inline int64_t layout_nrt(int64_t rows) {
+  return (rows + kTileRows - 1) / kTileRows;
+}
+__host__ __device__ inline int64_t layout_words(int64_t rows, int64_t K) {
+  return layout_nrt(rows) * layout_nkb(K) * kTileRows * layout_kw(K);
+}
+
+// ---- scalar conversions (device) ------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+// Load element i of an activation array of dtype code dt as fp32.
+__device__ __forceinline__ float load_act(const void* p, int dt, int64_t i) {
+  const uint16_t v = static_cast<const uint16_t*>(p)[i];
+  return dt == DBF_BF16 ? bf16_bits_to_f32(v) : f16_bits_to_f32(v);
+}
+
+// Store fp32 v into y (dtype dt) at i, optionally adding the old value.
+__device__ __forceinline__ void store_out(void* y, int dt, int64_t i, float v,
+                                          int accumulate) {
+  if (dt == DBF_F32) {
+    float* p = static_cast<float*>(y) + i;
+    *p = accumulate ? *p + v : v;
+  } else if (dt == DBF_BF16) {
+    uint16_t* p = static_cast<uint16_t*>(y) + i;
+    float o = accumulate ? bf16_bits_to_f32(*p) + v : v;
+    *p = f32_to_bf16_bits(o);
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(y) + i;
+    float o = accumulate ? f16_bits_to_f32(*p) + v : v;
+    *p = f32_to_f16_bits(o);
+  }
+}
+
+// ---- kernel launchers (host, internal C++) -------------------------------
+// Each returns hipSuccess or the launch error; arguments are already
+// validated by the ABI layer.
+
+hipError_t launch_pack(const void* src, int src_dtype, int64_t rows, int64_t k,
+                       int64_t ld, uint32_t* packed, hipStream_t s);
+hipError_t launch_unpack(const uint32_t* packed, int64_t rows, int64_t k,
+                         int8_t* dst, int64_t ld, hipStream_t s);
+
+// Term arrays as passed to kernels (by value).
+struct TermPtrs {
+  const uint32_t* b1[DBF_MAX_TERMS];
+  const uint32_t* b2[DBF_MAX_TERMS];
+  const uint16_t* alpha[DBF_MAX_TERMS];
+  const uint16_t* beta[DBF_MAX_TERMS];
+  const uint16_t* gamma[DBF_MAX_TERMS];
+  int n;
+};
+
+// Decode path (signed subset-sum tables).  ws holds fp32 w = beta * (B2 u)
+// as [n_terms][T][R_pad].
+size_t decode_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T);
+hipError_t launch_decode(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
+                         const void* x, int x_dtype, int64_t T, int64_t ldx,
+                         void* y, int y_dtype, int64_t ldy, int accumulate,
+                         void* ws, hipStream_t s);
+hipError_t launch_decode_i8(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
+                            const int8_t* x, int64_t T, int64_t ldx,
+                            int32_t* s1, int32_t* s2, void* y, int y_dtype,
+                            int64_t ldy, void* ws, hipStream_t s);
+// Only the first stage (w for every term, into ws); used by the adapter.
+hipError_t launch_decode_stage1(const TermPtrs& t, int64_t M, int64_t R,
+                                const void* x, int x_dtype, int64_t T,
+                                int64_t ldx, void* ws, hipStream_t s);
+// Number of K-split partials launch_decode_stage1 leaves per term.
+int decode_stage1_splits(int64_t M, int64_t R, int n_terms);
+
+// MFMA path.
+size_t mfma_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T);
+hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
+                       const void* x, int x_dtype, int64_t T, int64_t ldx,
+                       void* y, int y_dtype, int64_t ldy, int accumulate,
+                       void* ws, hipStream_t s);
+
+// Adapter: y = W0 x + sum_i alpha_i . B1_i w_i, with w from ws
+// (launch_decode_stage1 layout, ks partials per term).
+hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
+                          int64_t N, int64_t M, int64_t R, const void* x,
+                          int64_t T, int64_t ldx, void* y, int y_dtype,
+                          int64_t ldy, const void* ws, int ks, hipStream_t s);
+
+// Row stride (floats) of the rank-R intermediate in the workspace.
+inline int64_t ws_rstride(int64_t R) { return (R + 63) / 64 * 64; }
+
+}  // namespace dbf

@@ -1,0 +1,204 @@
+/*
+ * dbf.h -- C ABI of the MI355X (gfx950) double-binary factorized linear layer.
+ *
+ * The layer (one token x of M features, N outputs, inner rank R, L terms):
+ *
+ *   y = sum_{i=1..L} diag(alpha_i) B1_i diag(beta_i) B2_i diag(gamma_i) x
+ *
+ * with sign factors B1_i in {+-1}^{N x R}, B2_i in {+-1}^{R x M} and fp16
+ * scale vectors alpha_i (N), beta_i (R), gamma_i (M).  This is the weight
+ * update of "LoRDBA: Low-Rank Double-Binary Adaptation" (section 2,
+ * "Arquitetura Central", the parametrization of Delta W, with L the envelope
+ * rank); with L = 1 it is the double binary factorization of "Addition is
+ * almost all you need" (technical summary, section 2:  W ~ (a . A . m^T)
+ * (B . b^T) with a = alpha, A = B1, m = beta, B = B2, b = gamma); with L > 1
+ * it is the sum of boolean kernels of "Highly Efficient and Effective LLMs
+ * with Multi-Boolean Architectures" (technical summary, section 2, item 2),
+ * here with a double-binary term per kernel.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer except `terms` (host array) is device memory owned by the
+ *     caller.  The library never allocates, frees or keeps device memory; the
+ *     only state it keeps is a per-thread last-error string and a per-device
+ *     record that the device is gfx950.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return; nothing synchronises.  Faults inside a kernel
+ *     show up at the caller's next synchronisation.
+ *   - Activations x are [T x M] row-major with row stride ldx >= M elements;
+ *     outputs y are [T x N] with ldy >= N; the base weight W0 is [N x M]
+ *     (PyTorch's [out, in]) with ldw >= M.
+ *   - Scales are fp16 (bit patterns, `const void*` to 2-byte elements).
+ *   - Every call validates all arguments before the first HIP call and
+ *     returns DBF_OK (0) or a negative dbf_status; dbf_last_error() then
+ *     describes the problem.  No exception crosses the ABI.
+ *   - Non-finite inputs are outside the contract.
+ */
+#ifndef DBF_H
+#define DBF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBF_ABI_VERSION 1
+#define DBF_LAYOUT_VERSION 1
+
+/* status codes */
+#define DBF_OK 0
+#define DBF_EINVAL (-1)       /* a size, stride, count or NULL pointer is wrong */
+#define DBF_EDTYPE (-2)       /* unsupported dtype code for this argument */
+#define DBF_EALIGN (-3)       /* a device pointer is not 16-byte aligned */
+#define DBF_EWORKSPACE (-4)   /* ws is NULL or smaller than dbf_workspace_bytes */
+#define DBF_EDEVICE (-5)      /* current device is not gfx950, or no device */
+#define DBF_EUNSUPPORTED (-6) /* valid but not supported (e.g. int overflow) */
+#define DBF_ELAUNCH (-7)      /* a kernel launch failed */
+
+/* dtype codes */
+#define DBF_F16 1
+#define DBF_BF16 2
+#define DBF_F32 3
+#define DBF_I8 4
+#define DBF_I32 5
+
+/* execution paths for dbf_linear_forward / dbf_workspace_bytes */
+#define DBF_PATH_AUTO 0   /* chosen by T */
+#define DBF_PATH_DECODE 1 /* sign-accumulate over packed bits with 16-entry
+                             signed subset-sum tables (fp32 throughout) */
+#define DBF_PATH_MFMA 2   /* +-1 tiles unpacked from the bits into MFMA
+                             operands (fp16 operands, fp32 accumulation) */
+
+#define DBF_MAX_TERMS 8
+
+/* Version of this ABI and of the packed bit layout below. */
+int dbf_abi_version(void);
+int dbf_layout_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *dbf_last_error(void);
+
+/*
+ * Packed sign layout (DBF_LAYOUT_VERSION 1).  One bit per sign, as LoRDBA
+ * (section 2, "Eficiencia de Armazenamento") and DBF (technical summary,
+ * section 2, sign matrices with fp16 scale vectors) store the factors.
+ * A sign matrix S in {+-1}^{rows x K} -- B1 with rows = N, K = R; B2 with
+ * rows = R, K = M -- is stored as uint32 words:
+ *   bit value 1 is +1, 0 is -1; every padding bit is 0;
+ *   kw  = min(4, ceil(K / 32)) words per row per tile;
+ *   a tile is 64 rows x kw words (64 * kw * 4 bytes, a multiple of 128 B
+ *   when kw = 4), stored row by row;
+ *   tile (rt, kb) is tile number rt * nkb + kb, nkb = ceil(K / (32 kw));
+ *   bit j of word w of row r of tile (rt, kb) holds S[64 rt + r,
+ *   32 kw kb + 32 w + j].
+ * A wavefront reading one tile row per lane moves one contiguous kw*256 B.
+ * dbf_packed_bytes is the size of that buffer, padding included.
+ */
+size_t dbf_packed_bytes(int64_t rows, int64_t k);
+
+/*
+ * Pack the signs of src [rows x k] (row stride ld >= k elements, dtype
+ * DBF_I8, DBF_F16, DBF_BF16 or DBF_F32) into `packed`
+ * (dbf_packed_bytes(rows, k) bytes, 16-byte aligned).  Bit = (v >= 0):
+ * 0 and -0.0 map to +1, NaN to -1 (the binarization B = sign(H) of LoRDBA
+ * section 2, "Pipeline de Treinamento", leaves sign(0) open).  Every word of
+ * the buffer, padding included, is written.
+ */
+int dbf_pack(const void *src, int src_dtype, int64_t rows, int64_t k,
+             int64_t ld, uint32_t *packed, void *stream);
+
+/* Inverse of dbf_pack for the signs only: writes +-1 as int8 to
+ * dst [rows x k] with row stride ld >= k. */
+int dbf_unpack(const uint32_t *packed, int64_t rows, int64_t k, int8_t *dst,
+               int64_t ld, void *stream);
+
+/*
+ * One term of the sum: device pointers to the packed B1 (N x R layout),
+ * the packed B2 (R x M layout) and the fp16 vectors alpha (N), beta (R),
+ * gamma (M).  The array of terms is host memory and is read during the
+ * call only.  Terms may alias the same packed factors.
+ */
+typedef struct dbf_term {
+    const uint32_t *b1;
+    const uint32_t *b2;
+    const void *alpha;
+    const void *beta;
+    const void *gamma;
+} dbf_term;
+
+/* Bytes of device workspace dbf_linear_forward / dbf_linear_forward_i8 /
+ * lordba_adapter_forward need for these sizes and path (the rank-R
+ * intermediate of every term, and per-token scale slots for the MFMA
+ * path).  The caller allocates it; its contents need not be initialised and
+ * are clobbered. */
+size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
+                           int64_t T, int path);
+
+/*
+ * y (+)= sum_i Delta W_i x for T tokens.
+ * The forward of LoRDBA section 2 ("Kernel de Inferencia") and DBF section 2
+ * ("Inferencia"): two sign-accumulate products over the packed bits,
+ * interleaved with the per-channel scales, with no multiplication inside
+ * the inner products on the decode path.
+ *   terms[n_terms]   1 <= n_terms <= DBF_MAX_TERMS; b1, b2, alpha, beta,
+ *                    gamma all non-NULL.
+ *   x                [T x M], x_dtype DBF_BF16 or DBF_F16, row stride ldx.
+ *   y                [T x N], y_dtype DBF_F32, DBF_BF16 or DBF_F16, ldy.
+ *   accumulate       0: y = result; 1: y = y + result (in fp32).
+ *   ws, ws_bytes     workspace of dbf_workspace_bytes(..., path) bytes.
+ *   path             DBF_PATH_AUTO picks the decode path for T <= 16 and the
+ *                    MFMA path above; the others force one (both are
+ *                    correct for every T >= 1).
+ * Accumulation is fp32; the decode path keeps every intermediate in fp32,
+ * the MFMA path rounds gamma*x and the scaled rank-R intermediate to fp16
+ * (with an exact power-of-two scale per token).
+ * T = 0 is valid and does nothing.  Results are bitwise reproducible run
+ * to run (no floating-point atomics).
+ */
+int dbf_linear_forward(const dbf_term *terms, int n_terms, int64_t N,
+                       int64_t M, int64_t R, const void *x, int x_dtype,
+                       int64_t T, int64_t ldx, void *y, int y_dtype,
+                       int64_t ldy, int accumulate, void *ws, size_t ws_bytes,
+                       int path, void *stream);
+
+/*
+ * Integer-activation variant: x is int8 [T x M] with gamma folded into it
+ * upstream (terms[i].gamma must be NULL, since gamma sits on the summed
+ * index and cannot be applied to integer sums).
+ *   s1 (optional, int32 [n_terms x T x R]):  S1_i = B2_i x, exact.
+ *   s2 (optional, int32 [n_terms x T x N]):  S2_i = B1_i S1_i, exact;
+ *       needs every beta == NULL (beta = 1).
+ *   y  (optional, y_dtype DBF_F32/BF16/F16, ldy): sum_i alpha_i .
+ *       B1_i (beta_i . S1_i), fp32 accumulation; a NULL alpha or beta means
+ *       all ones.
+ * Exactness needs |S1| < 2^31 and, for s2 or a NULL beta, R * M * 127 <
+ * 2^31; larger shapes return DBF_EUNSUPPORTED.  Uses the decode path and
+ * its workspace (dbf_workspace_bytes(..., DBF_PATH_DECODE)).
+ */
+int dbf_linear_forward_i8(const dbf_term *terms, int n_terms, int64_t N,
+                          int64_t M, int64_t R, const int8_t *x, int64_t T,
+                          int64_t ldx, int32_t *s1, int32_t *s2, void *y,
+                          int y_dtype, int64_t ldy, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * LoRDBA adapter mode: y = W0 x + sum_i Delta W_i x, the adapter kept
+ * unmerged beside the frozen base (LoRDBA sections 1 and 5).  W0 [N x M]
+ * bf16 row stride ldw, x bf16 [T x M].  n_terms = 0 computes the base only
+ * (terms may then be NULL).  y_dtype DBF_F32, DBF_BF16 or DBF_F16.  The base
+ * product and the adapter's second sign-accumulate run in one kernel over
+ * the same output rows; the rank-R intermediate needs ws of
+ * dbf_workspace_bytes(N, M, R, n_terms, T, DBF_PATH_DECODE) bytes (may be
+ * NULL when n_terms = 0).
+ */
+int lordba_adapter_forward(const void *w0, int64_t ldw, const dbf_term *terms,
+                           int n_terms, int64_t N, int64_t M, int64_t R,
+                           const void *x, int64_t T, int64_t ldx, void *y,
+                           int y_dtype, int64_t ldy, void *ws,
+                           size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DBF_H */

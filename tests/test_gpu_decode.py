@@ -1,0 +1,104 @@
+"""dbf_linear_forward on the decode path against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bit_adapters_amd as D
+import oracle as O
+from bit_adapters_amd import synth as S
+from dbfutil import (DEV, assert_close, device_terms, round_bf16, to_np, x64,
+                     x_dev)
+
+pytestmark = pytest.mark.gpu
+
+PATH = D.DBF_PATH_DECODE
+
+
+def run(layer, x, path=PATH, **kw):
+    terms = device_terms(layer)
+    y = D.dbf_linear_forward(terms, layer["N"], layer["M"], layer["R"], x_dev(x),
+                             path=path, **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("config,T", [(1, 1), (2, 1), (2, 4), (2, 16), (4, 1),
+                                      (4, 8)])
+def test_configs(config, T):
+    print("decode config", config, "T", T, flush=True)
+    layer = S.make_layer(config)
+    x = S.make_x(config, T)
+    y = to_np(run(layer, x))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref, what="config %d T %d" % (config, T))
+
+
+ODD = [(1, 1, 1, 1, 1), (65, 33, 17, 2, 3), (130, 300, 70, 3, 5),
+       (64, 128, 64, 1, 2), (200, 1000, 96, 1, 16), (77, 129, 33, 2, 7),
+       (4096, 64, 16, 1, 2), (33, 4100, 130, 1, 17)]
+
+
+@pytest.mark.parametrize("N,M,R,L,T", ODD)
+@pytest.mark.parametrize("xk", ["bf16", "f16"])
+def test_odd_shapes(N, M, R, L, T, xk):
+    print("decode odd", N, M, R, L, T, xk, flush=True)
+    layer, x = S.make_custom(N, M, R, L, T, seed=N + M + R, x_kind=xk)
+    y = to_np(run(layer, x))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref)
+
+
+def test_output_dtypes_accumulate_and_strides():
+    layer, x = S.make_custom(96, 200, 40, 2, 5, seed=3)
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    terms = device_terms(layer)
+    xd = torch.zeros((5, 208), dtype=torch.bfloat16, device=DEV)
+    xd[:, :200] = x_dev(x)
+    xs = xd[:, :200]                                   # ldx = 208
+    # fp32 output into a strided view with a guard band
+    big = torch.full((5, 100), 7.0, dtype=torch.float32, device=DEV)
+    y = big[:, :96]
+    D.dbf_linear_forward(terms, 96, 200, 40, xs, y=y, path=PATH)
+    torch.cuda.synchronize()
+    assert_close(to_np(y), ref)
+    assert torch.all(big[:, 96:] == 7.0)
+    # accumulate onto a known base
+    base = torch.randn((5, 96), dtype=torch.float32, device=DEV)
+    y2 = base.clone()
+    D.dbf_linear_forward(terms, 96, 200, 40, xs, y=y2, accumulate=True, path=PATH)
+    torch.cuda.synchronize()
+    assert_close(to_np(y2), ref + to_np(base))
+    # bf16 and fp16 outputs, compared with the oracle rounded the same way
+    yb = D.dbf_linear_forward(terms, 96, 200, 40, xs, y_dtype=torch.bfloat16, path=PATH)
+    torch.cuda.synchronize()
+    assert_close(to_np(yb), round_bf16(ref), rel_l2=4e-3)
+    yh = D.dbf_linear_forward(terms, 96, 200, 40, xs, y_dtype=torch.float16, path=PATH)
+    torch.cuda.synchronize()
+    assert_close(to_np(yh), ref.astype(np.float16).astype(np.float64))
+
+
+def test_deterministic():
+    layer = S.make_layer(2)
+    x = S.make_x(2, 4)
+    a = run(layer, x).cpu()
+    b = run(layer, x).cpu()
+    assert torch.equal(a, b)
+
+
+def test_zero_tokens():
+    layer, _ = S.make_custom(8, 8, 8, 1, 1, seed=1)
+    terms = device_terms(layer)
+    x = torch.empty((0, 8), dtype=torch.bfloat16, device=DEV)
+    y = D.dbf_linear_forward(terms, 8, 8, 8, x, path=PATH)
+    assert y.shape == (0, 8)
+
+
+def test_row_flip_on_gpu():
+    # the pages' structure: flipping row n0 of B1 negates output n0 only
+    layer, x = S.make_custom(128, 256, 64, 1, 2, seed=11)
+    y = to_np(run(layer, x))
+    layer["terms"][0]["b1"][5, :] *= -1
+    y2 = to_np(run(layer, x))
+    np.testing.assert_allclose(y2[:, 5], -y[:, 5], rtol=1e-5, atol=1e-5)
+    rest = [n for n in range(128) if n != 5]
+    assert np.array_equal(y2[:, rest], y[:, rest])

@@ -1,0 +1,157 @@
+"""Host checks of the C ABI: the library loads, exports every entry point
+include/dbf.h declares, and rejects bad arguments with the documented status
+before making any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_adapters_amd as D
+import oracle as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "dbf.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = D.library()
+    names = declared_functions()
+    assert set(names) == set(D.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_versions():
+    assert D.dbf_abi_version() == 1
+    assert D.dbf_layout_version() == 1
+
+
+@pytest.mark.parametrize("rows,k", [(1, 1), (3, 31), (64, 32), (65, 33),
+                                    (70, 97), (130, 300), (16, 4096), (4096, 16),
+                                    (11008, 2048), (8192, 6144)])
+def test_packed_bytes_matches_oracle_layout(rows, k):
+    assert D.dbf_packed_bytes(rows, k) == 4 * O.default().packed_words(rows, k)
+
+
+def test_packed_bytes_edges():
+    assert D.dbf_packed_bytes(0, 5) == 0
+    assert D.dbf_packed_bytes(5, 0) == 0
+    # full tiles are whole 128-byte lines
+    assert D.dbf_packed_bytes(64, 128) == 1024
+
+
+def test_workspace_bytes():
+    assert D.dbf_workspace_bytes(512, 512, 256, 1, 0) == 0
+    assert D.dbf_workspace_bytes(512, 512, 256, 1, 1, D.DBF_PATH_DECODE) > 0
+    assert D.dbf_workspace_bytes(512, 512, 256, 1, 1, D.DBF_PATH_MFMA) > 0
+
+
+L = D.library()
+FAKE = 1 << 20            # a 16-byte aligned non-NULL address, never touched
+MIS = FAKE + 8            # misaligned
+
+
+def _terms(n=1, **over):
+    arr = (D._CTerm * max(n, 1))()
+    for i in range(n):
+        f = dict(b1=FAKE, b2=FAKE, alpha=FAKE, beta=FAKE, gamma=FAKE)
+        f.update(over)
+        arr[i] = D._CTerm(**f)
+    return arr
+
+
+def fwd(terms=None, n=1, N=8, M=8, R=8, x=FAKE, xdt=D.DBF_BF16, T=1, ldx=8,
+        y=FAKE, ydt=D.DBF_F32, ldy=8, acc=0, ws=FAKE, wsb=1 << 30, path=0):
+    if terms is None:
+        terms = _terms(n)
+    return L.dbf_linear_forward(terms, n, N, M, R, x, xdt, T, ldx, y, ydt, ldy,
+                                acc, ws, wsb, path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), D.DBF_EINVAL), (dict(n=9), D.DBF_EINVAL),
+    (dict(terms=_terms(1, b1=None)), D.DBF_EINVAL),
+    (dict(terms=_terms(1, gamma=None)), D.DBF_EINVAL),
+    (dict(terms=_terms(1, b2=MIS)), D.DBF_EALIGN),
+    (dict(terms=_terms(1, alpha=FAKE + 1)), D.DBF_EALIGN),
+    (dict(N=0), D.DBF_EINVAL), (dict(R=0), D.DBF_EINVAL), (dict(T=-1), D.DBF_EINVAL),
+    (dict(xdt=D.DBF_F32), D.DBF_EDTYPE), (dict(ydt=D.DBF_I8), D.DBF_EDTYPE),
+    (dict(acc=2), D.DBF_EINVAL), (dict(path=7), D.DBF_EINVAL),
+    (dict(ldx=7), D.DBF_EINVAL), (dict(ldy=7), D.DBF_EINVAL),
+    (dict(x=None), D.DBF_EINVAL), (dict(y=MIS), D.DBF_EALIGN),
+    (dict(ws=None), D.DBF_EWORKSPACE), (dict(wsb=16), D.DBF_EWORKSPACE),
+    (dict(ws=MIS), D.DBF_EALIGN),
+])
+def test_forward_validation(kw, code):
+    assert fwd(**kw) == code
+    assert D.dbf_last_error()
+
+
+def test_forward_zero_tokens_is_a_noop():
+    assert fwd(T=0, x=None, y=None, ws=None) == D.DBF_OK
+
+
+def i8(terms=None, n=1, N=8, M=8, R=8, x=FAKE, T=1, ldx=8, s1=None, s2=None,
+       y=None, ydt=D.DBF_F32, ldy=8, ws=FAKE, wsb=1 << 30):
+    if terms is None:
+        terms = _terms(n, gamma=None)
+    return L.dbf_linear_forward_i8(terms, n, N, M, R, x, T, ldx, s1, s2, y, ydt,
+                                   ldy, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(terms=_terms(1)), D.DBF_EINVAL),                       # gamma given
+    (dict(s2=FAKE), D.DBF_EINVAL),                               # s2 with beta
+    (dict(n=2, terms=(lambda a: (setattr(a[1], "beta", None), a)[1])(_terms(2, gamma=None))),
+     D.DBF_EINVAL),                                              # mixed beta
+    (dict(terms=_terms(1, gamma=None, beta=None), R=65536, M=65536),
+     D.DBF_EUNSUPPORTED),                                        # int32 overflow
+    (dict(y=FAKE, ydt=D.DBF_I32), D.DBF_EDTYPE),
+    (dict(s1=MIS), D.DBF_EALIGN),
+    (dict(wsb=4), D.DBF_EWORKSPACE),
+])
+def test_i8_validation(kw, code):
+    assert i8(**kw) == code
+
+
+def ad(w0=FAKE, ldw=8, terms=None, n=1, N=8, M=8, R=8, x=FAKE, T=1, ldx=8,
+       y=FAKE, ydt=D.DBF_F32, ldy=8, ws=FAKE, wsb=1 << 30):
+    if terms is None and n > 0:
+        terms = _terms(n)
+    return L.lordba_adapter_forward(w0, ldw, terms, n, N, M, R, x, T, ldx, y, ydt,
+                                    ldy, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), D.DBF_EINVAL), (dict(n=9), D.DBF_EINVAL),
+    (dict(ldw=4), D.DBF_EINVAL), (dict(w0=None), D.DBF_EINVAL),
+    (dict(w0=MIS), D.DBF_EALIGN), (dict(ydt=7), D.DBF_EDTYPE),
+    (dict(ws=None), D.DBF_EWORKSPACE), (dict(R=0), D.DBF_EINVAL),
+])
+def test_adapter_validation(kw, code):
+    assert ad(**kw) == code
+
+
+def test_pack_validation():
+    assert L.dbf_pack(FAKE, 9, 4, 4, 4, FAKE, None) == D.DBF_EDTYPE
+    assert L.dbf_pack(None, D.DBF_I8, 4, 4, 4, FAKE, None) == D.DBF_EINVAL
+    assert L.dbf_pack(FAKE, D.DBF_I8, 4, 4, 3, FAKE, None) == D.DBF_EINVAL
+    assert L.dbf_pack(FAKE, D.DBF_I8, 4, 4, 4, MIS, None) == D.DBF_EALIGN
+    assert L.dbf_pack(FAKE, D.DBF_I8, 0, 4, 4, FAKE, None) == D.DBF_OK
+    assert L.dbf_unpack(FAKE, 4, 4, FAKE, 3, None) == D.DBF_EINVAL
+    assert L.dbf_unpack(MIS, 4, 4, FAKE, 4, None) == D.DBF_EALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error")
+def test_valid_call_without_device_reports_edevice():
+    assert fwd() == D.DBF_EDEVICE
+    assert "device" in D.dbf_last_error()
