@@ -1,0 +1,286 @@
+"""Throughput of the double-binary factorized linear layer on one MI355X.
+
+Default workload: the Llama-7B-shaped projection as a one-term DBF layer
+(N = M = 4096, R = 2048, ~1 bit/weight), decode batch of 1 token, bf16 x and
+bf16 y.  A step is one forward, dbf_linear_forward, over one batch: both
+sign-accumulate stages, the three scale vectors and the output.
+
+Timing: the layer is replicated into enough distinct copies (>= 1 GiB in
+total) that each step reads its signs from HBM rather than from the 256 MiB
+last-level cache; W warm-up steps run eagerly, then K steps (one copy each,
+round robin) are captured in one HIP graph and replayed once between two HIP
+events on the capturing stream; ms_per_step = elapsed / K.  The graph's last
+output is checked against an eager call and against the fp64 oracle.
+
+Other workloads: --config 3 --rank {16,64} (LoRDBA adapter on a bf16 base),
+--config 4 (three-term layer), --config 5 (8192 x 8192, R = 6144, 4096
+tokens), with --tokens T.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bit_adapters_amd as D  # noqa: E402
+from bit_adapters_amd import synth as S  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+DEV = "cuda:0"
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_adapters_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dev_f16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(DEV)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def algorithmic(cfg, N, M, R, L, T, base):
+    """Bytes the method must move per forward (packed signs at one bit each,
+    fp16 scales, bf16 x and y, bf16 W0 if any) and its flops."""
+    signs = L * R * (N + M) / 8.0
+    scales = 2.0 * L * (N + R + M)
+    xy = 2.0 * T * (M + N)
+    w0 = 2.0 * N * M if base else 0.0
+    flops = 2.0 * T * R * (N + M) * L + (2.0 * T * N * M if base else 0.0)
+    return signs + scales + xy + w0, flops
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--tokens", type=int, default=None)
+    ap.add_argument("--rank", type=int, default=16)
+    ap.add_argument("--path", type=int, default=D.DBF_PATH_AUTO)
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the layer's multi-GPU sharding is "
+              "a design (DESIGN.md), not part of this build; use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    cfgd = S.CONFIGS[args.config]
+    T = args.tokens if args.tokens is not None else min(cfgd["T"])
+    base = bool(cfgd.get("base"))
+    layer = S.make_layer(args.config, R=args.rank if base else None)
+    N, M, R, L = layer["N"], layer["M"], layer["R"], len(layer["terms"])
+    x_np = S.make_x(args.config, T)
+    x = dev_bf16(x_np)
+
+    # one packed copy, then clones for rotation
+    terms0 = []
+    for t in layer["terms"]:
+        terms0.append(D.DbfTerm(
+            D.dbf_pack(torch.from_numpy(t["b1"]).to(DEV)),
+            D.dbf_pack(torch.from_numpy(t["b2"]).to(DEV)),
+            dev_f16(t["alpha"]), dev_f16(t["beta"]), dev_f16(t["gamma"])))
+    w0 = dev_bf16(layer["w0"]) if base else None
+    copy_bytes = sum(sum(v.numel() * v.element_size() for v in t) for t in terms0)
+    if base:
+        copy_bytes += w0.numel() * 2
+    ncopies = max(1, min(int(math.ceil(args.rotate_gib * 2 ** 30 / copy_bytes)), 4096))
+    copies = [(terms0, w0)]
+    for _ in range(ncopies - 1):
+        copies.append(([D.DbfTerm(*[v.clone() for v in t]) for t in terms0],
+                       w0.clone() if base else None))
+
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    if base:
+        nws = D.dbf_workspace_bytes(N, M, R, L, T, D.DBF_PATH_DECODE)
+    else:
+        nws = D.dbf_workspace_bytes(N, M, R, L, T, args.path)
+    ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device=DEV)
+
+    def step(i):
+        terms, w = copies[i % ncopies]
+        if base:
+            D.lordba_adapter_forward(w, terms, N, M, R, x, y=y, ws=ws)
+        else:
+            D.dbf_linear_forward(terms, N, M, R, x, y=y, ws=ws, path=args.path)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(args.steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    bytes_alg, flops = algorithmic(args.config, N, M, R, L, T, base)
+    tok_s = T / (ms * 1e-3)
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    large_t = T >= 256
+    if large_t:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2),
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic_for(args, T)
+
+    check = None
+    if not args.no_check:
+        check = verify(layer, x_np, x, y, copies[(args.steps - 1) % ncopies], base,
+                       N, M, R, T, args, step_index=args.steps - 1, ws=ws)
+
+    cpu = None if args.no_cpu else cpu_baseline(layer, args.config, T, base)
+
+    copy_probe = None
+    if args.copy_probe:
+        a = torch.empty(64 * 2 ** 20, dtype=torch.int32, device=DEV)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        copy_probe = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4}
+
+    name = cfgd["name"] + ("-r%d" % R if base else "")
+    out = {
+        "metric": "DBF linear tokens/s" + (" (adapter mode)" if base else ""),
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x / fp16 scales / 1-bit signs, fp32 accumulate",
+        "data": "synthetic (seeded i.i.d. signs and scales of the configuration)",
+        "config": {"workload": name, "N": N, "M": M, "R": R, "terms": L,
+                   "tokens": T, "path": ("adapter" if base else
+                                         {0: "auto", 1: "decode", 2: "mfma"}[args.path]),
+                   "rotated_copies": ncopies,
+                   "algorithmic_bytes": int(bytes_alg), "algorithmic_flops": int(flops),
+                   "effective_GBps": round(gbs, 1), "effective_TFLOPs": round(tflops, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    if copy_probe:
+        out["copy_probe"] = copy_probe
+    print(json.dumps(out), flush=True)
+
+
+def traffic_for(args, T):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        db = json.load(f)
+    key = "c%d-t%d%s-p%d" % (args.config, T, "-r%d" % args.rank if args.config == 3 else "",
+                             args.path)
+    ent = db.get(key)
+    if not ent or ent.get("sources") != kernel_sources_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def verify(layer, x_np, x, y, copy, base, N, M, R, T, args, step_index, ws):
+    """The graph's last output vs an eager call on the same copy (bitwise) and
+    vs the oracle on sampled rows."""
+    import oracle as O
+
+    yg = y.clone()
+    terms, w = copy
+    ye = torch.empty_like(y)
+    if base:
+        D.lordba_adapter_forward(w, terms, N, M, R, x, y=ye, ws=ws)
+    else:
+        D.dbf_linear_forward(terms, N, M, R, x, y=ye, ws=ws, path=args.path)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(yg, ye))
+    toks = list(range(min(T, 4)))
+    xs = O.widen_bf16(x_np[toks])
+    ref = O.default().forward(O.terms64(layer), xs)
+    if base:
+        ref = ref + O.default().dense(O.widen_bf16(layer["w0"]), xs)
+    from bit_adapters_amd.synth import f32_to_bf16_bits
+    ref_b = O.widen_bf16(f32_to_bf16_bits(ref.astype(np.float32)))
+    got = O.widen_bf16(yg[toks].view(torch.int16).cpu().numpy().view(np.uint16))
+    rel = float(np.linalg.norm(got - ref_b) / np.linalg.norm(ref_b))
+    mx = float(np.abs(got - ref_b).max() / np.abs(ref_b).max())
+    ok = same and rel <= 4e-3 and mx <= 1e-2
+    if not ok:
+        print("bench check failed: graph==eager %s rel_l2 %.3e max_abs %.3e"
+              % (same, rel, mx), file=sys.stderr)
+    return {"graph_equals_eager": same, "tokens_checked": len(toks),
+            "rel_l2_vs_oracle_bf16": round(rel, 7), "max_abs": round(mx, 7), "ok": ok}
+
+
+def cpu_baseline(layer, config, T, base, budget_s=12.0):
+    """The fp64 oracle on the host cores over a bounded sample of the same
+    workload: whole tokens of the same layer, until about budget_s seconds."""
+    import oracle as O
+
+    o = O.default()
+    terms = O.terms64(layer)
+    xs = O.widen_bf16(S.make_x(config, max(S.CONFIGS[config]["T"])))
+    w0 = O.widen_bf16(layer["w0"]) if base else None
+    done, t0 = 0, time.perf_counter()
+    while True:
+        tok = xs[done % xs.shape[0]][None, :]
+        o.forward(terms, tok)
+        if base:
+            o.dense(w0, tok)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 4096:
+            break
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": o.threads(),
+            "kind": "oracle",
+            "sample": "%d single-token forwards of the same layer (%.1f s), fp64" % (done, el)}
+
+
+if __name__ == "__main__":
+    main()

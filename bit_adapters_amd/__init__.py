@@ -172,10 +172,12 @@ def dbf_unpack(packed: torch.Tensor, rows: int, k: int,
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    """The caller's workspace, or a new zeroed one (its first 256 bytes are
+    the decode path's counters and must start at zero)."""
     if nbytes == 0:
         return ws, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 

@@ -253,19 +253,10 @@ int lordba_adapter_forward(const void* w0, int64_t ldw, const dbf_term* terms,
   }
   e = check_device();
   if (e != DBF_OK) return e;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  dbf::TermPtrs tp{};
-  int ks = 1;
-  if (n_terms > 0) {
-    tp = to_ptrs(terms, n_terms);
-    const hipError_t h = dbf::launch_decode_stage1(tp, M, R, x, DBF_BF16, T, ldx, ws, s);
-    if (h != hipSuccess) return launched(h);
-    ks = dbf::decode_stage1_splits(M, R, n_terms);
-  }
-  return launched(dbf::launch_adapter(static_cast<const uint16_t*>(w0), ldw, tp,
-                                      N, M, n_terms > 0 ? R : 1, x, T, ldx, y,
-                                      y_dtype, ldy, static_cast<const float*>(ws),
-                                      ks, s));
+  const dbf::TermPtrs tp = n_terms > 0 ? to_ptrs(terms, n_terms) : dbf::TermPtrs{};
+  return launched(dbf::launch_adapter(static_cast<const uint16_t*>(w0), ldw, tp, N, M,
+                                      n_terms > 0 ? R : 1, x, T, ldx, y, y_dtype, ldy, ws,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

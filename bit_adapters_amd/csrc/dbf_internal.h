@@ -89,8 +89,8 @@ struct TermPtrs {
   int n;
 };
 
-// Decode path (signed subset-sum tables).  ws holds fp32 w = beta * (B2 u)
-// as [n_terms][T][R_pad].
+// Decode path (signed subset-sum tables).  ws: 256 bytes of counters, then
+// fp32 partials of w = beta * (B2 u) as [n_terms][ks][T][R_pad].
 size_t decode_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T);
 hipError_t launch_decode(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                          const void* x, int x_dtype, int64_t T, int64_t ldx,
@@ -100,12 +100,6 @@ hipError_t launch_decode_i8(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                             const int8_t* x, int64_t T, int64_t ldx,
                             int32_t* s1, int32_t* s2, void* y, int y_dtype,
                             int64_t ldy, void* ws, hipStream_t s);
-// Only the first stage (w for every term, into ws); used by the adapter.
-hipError_t launch_decode_stage1(const TermPtrs& t, int64_t M, int64_t R,
-                                const void* x, int x_dtype, int64_t T,
-                                int64_t ldx, void* ws, hipStream_t s);
-// Number of K-split partials launch_decode_stage1 leaves per term.
-int decode_stage1_splits(int64_t M, int64_t R, int n_terms);
 
 // MFMA path.
 size_t mfma_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T);
@@ -114,12 +108,16 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                        void* y, int y_dtype, int64_t ldy, int accumulate,
                        void* ws, hipStream_t s);
 
-// Adapter: y = W0 x + sum_i alpha_i . B1_i w_i, with w from ws
-// (launch_decode_stage1 layout, ks partials per term).
+// Adapter: y = W0 x + sum_i Delta W_i x in one launch (stage 1 of the
+// decode path plus the base product; ws as for the decode path).
 hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
                           int64_t N, int64_t M, int64_t R, const void* x,
                           int64_t T, int64_t ldx, void* y, int y_dtype,
-                          int64_t ldy, const void* ws, int ks, hipStream_t s);
+                          int64_t ldy, void* ws, hipStream_t s);
+
+// The decode path keeps its stage-1 -> stage-2 counters in the first bytes
+// of the workspace (zero before first use, zero after every call).
+constexpr size_t kDecodeCounterBytes = 256;
 
 // Row stride (floats) of the rank-R intermediate in the workspace.
 inline int64_t ws_rstride(int64_t R) { return (R + 63) / 64 * 64; }

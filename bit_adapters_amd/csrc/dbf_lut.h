@@ -1,0 +1,312 @@
+// Device building blocks of the sign-accumulate over packed bits with
+// 16-entry signed subset-sum tables, shared by the decode kernel and the
+// fused adapter kernel.
+//
+// For each group of four consecutive activations a0..a3 and each 4-bit
+// pattern n the table holds
+//     E[n] = sum_j (bit j of n ? +a_j : -a_j) = 2 * sum_{bit j set} a_j - sum_j a_j,
+// the identity  sum_k s_k a_k = 2 sum_{s_k=+1} a_k - sum_k a_k  applied per
+// group with the -sum folded into every entry, so a row's product with the
+// activations is one LDS lookup and one add per nibble of its packed bits
+// (LoRDBA section 2, "Kernel de Inferencia": additions and subtractions in
+// place of multiplications in the inner products).
+//
+// A workgroup is 8 wavefronts over one 64-row tile; lane = row.  A pass
+// covers 8 * PW K-blocks; wave wv takes blocks kp + j * 8 + wv (j < PW), so
+// every wave reads whole contiguous tiles and all 64 lanes of a wave look up
+// the same group's 16 entries together (16 LDS banks, no conflicts).
+#pragma once
+
+#include "dbf_internal.h"
+
+namespace dbf {
+namespace lut {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxKS = 8;
+constexpr unsigned kSpinLimit = 1u << 26;
+
+enum { MODE_F = 0, MODE_I8_BETA = 1, MODE_I8 = 2 };
+
+// Token-block size and K-blocks per wave per pass for T tokens.
+__host__ __device__ constexpr int pw_of(int tb) { return tb == 1 ? 2 : 1; }
+inline int pick_tb(int64_t T) { return T <= 1 ? 1 : (T == 2 ? 2 : 4); }
+
+// LDS (elements of type A): tables [TB][groups][16], wave partials
+// [4][TB][64].
+template <int TB, int KW>
+__host__ __device__ constexpr int tbl_elems() { return TB * kWaves * pw_of(TB) * 8 * KW * 16; }
+template <int TB>
+__host__ __device__ constexpr int red_elems() { return kWaves * TB * 64; }
+template <typename A, int TB, int KW>
+__host__ __device__ constexpr size_t lds_bytes() {
+  return sizeof(A) * (tbl_elems<TB, KW>() + red_elems<TB>());
+}
+
+template <typename A>
+__device__ __forceinline__ void build_signed16(A a0, A a1, A a2, A a3, A* e) {
+  const A p0 = -a0 - a1, p1 = a0 - a1, p2 = a1 - a0, p3 = a0 + a1;
+  const A q0 = -a2 - a3, q1 = a2 - a3, q2 = a3 - a2, q3 = a2 + a3;
+  e[0] = p0 + q0;  e[1] = p1 + q0;  e[2] = p2 + q0;  e[3] = p3 + q0;
+  e[4] = p0 + q1;  e[5] = p1 + q1;  e[6] = p2 + q1;  e[7] = p3 + q1;
+  e[8] = p0 + q2;  e[9] = p1 + q2;  e[10] = p2 + q2; e[11] = p3 + q2;
+  e[12] = p0 + q3; e[13] = p1 + q3; e[14] = p2 + q3; e[15] = p3 + q3;
+}
+
+template <int KW>
+__device__ __forceinline__ void load_row_words(const uint32_t* p, uint32_t* wd) {
+  if constexpr (KW == 4) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    wd[0] = v[0]; wd[1] = v[1]; wd[2] = v[2]; wd[3] = v[3];
+  } else if constexpr (KW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    wd[0] = v.x; wd[1] = v.y;
+  } else {
+#pragma unroll
+    for (int w = 0; w < KW; ++w) wd[w] = p[w];
+  }
+}
+
+// This lane's words of the pass starting at K-block kp (zeros past kb_end).
+template <int TB, int KW>
+__device__ __forceinline__ void load_pass_bits(const uint32_t* __restrict__ bits,
+                                               int64_t rt, int64_t nkb, int64_t kp,
+                                               int64_t kb_end,
+                                               uint32_t (&wd)[pw_of(TB)][KW]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < pw_of(TB); ++j) {
+    const int64_t kb = kp + j * kWaves + wv;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) wd[j][w] = 0;
+    if (kb < kb_end) load_row_words<KW>(bits + ((rt * nkb + kb) * 64 + lane) * KW, wd[j]);
+  }
+}
+
+// Tables for the groups of the pass (ng groups of four activations per
+// token, act4(tok, g, a) writes group g's four values) built straight into
+// LDS, then this lane's lookups of the pass: acc[tok] += sum over the pass
+// of S[row, k] * act[tok][k].  Two accumulators per token keep the adds of
+// consecutive nibbles independent, so many LDS reads are in flight.  Ends
+// with a barrier, so the tables may be overwritten afterwards.
+template <typename A, int TB, int KW, typename Act4>
+__device__ __forceinline__ void tables_and_lookups(Act4 act4, A* tbl, int ng, int64_t kp,
+                                                   int64_t kb_end,
+                                                   const uint32_t (&wd)[pw_of(TB)][KW],
+                                                   A* acc) {
+  constexpr int PW = pw_of(TB);
+  constexpr int gpp = kWaves * PW * 8 * KW;
+  const int wv = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < TB * ng; e += kThreads) {
+    const int tok = e / ng, g = e - tok * ng;
+    A a[4];
+    act4(tok, g, a);
+    build_signed16<A>(a[0], a[1], a[2], a[3], tbl + (tok * gpp + g) * 16);
+  }
+  __syncthreads();
+  A acc2[TB];
+#pragma unroll
+  for (int tok = 0; tok < TB; ++tok) acc2[tok] = A(0);
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    if (kp + j * kWaves + wv >= kb_end) continue;  // wave-uniform
+    const A* tb = tbl + ((j * kWaves + wv) * 8 * KW) * 16;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+#pragma unroll
+      for (int c = 0; c < 8; c += 2) {
+        const int n0 = (wd[j][w] >> (4 * c)) & 15;
+        const int n1 = (wd[j][w] >> (4 * c + 4)) & 15;
+#pragma unroll
+        for (int tok = 0; tok < TB; ++tok) {
+          acc[tok] += tb[(tok * gpp + w * 8 + c) * 16 + n0];
+          acc2[tok] += tb[(tok * gpp + w * 8 + c + 1) * 16 + n1];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tok = 0; tok < TB; ++tok) acc[tok] += acc2[tok];
+  __syncthreads();
+}
+
+// Sum of the 4 wave partials of each lane's row, in wave order; the result
+// is valid in wave 0.
+template <typename A, int TB>
+__device__ __forceinline__ void reduce_waves(A* red, A* acc) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int tok = 0; tok < TB; ++tok) red[(wv * TB + tok) * 64 + lane] = acc[tok];
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int tok = 0; tok < TB; ++tok) {
+      A s = red[tok * 64 + lane];
+#pragma unroll
+      for (int v = 1; v < kWaves; ++v) s += red[(v * TB + tok) * 64 + lane];
+      acc[tok] = s;
+    }
+  }
+  __syncthreads();
+}
+
+// ---- stage 1: w = beta . (B2 (gamma . x)) over one row tile and K split ----
+struct Stage1 {
+  TermPtrs t;
+  const void* x;
+  int x_dtype;
+  int64_t ldx, T, M, R;
+  int64_t nkb, kb_per_split, nrt;
+  int ks;
+  void* ws;       // partials [L][ks][T][rs]
+  int64_t rs;
+  int vec4;       // x rows allow 8-byte loads of four activations
+};
+
+// Stage-1 workgroup `bid` in [0, nrt * ks * L): its row tile of B2_term,
+// K-blocks [kb0, kb1) of its split, one or more passes.
+template <typename A, int TB, int KW, int MODE>
+__device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
+  constexpr int PW = pw_of(TB);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per_term = static_cast<int>(p.nrt) * p.ks;
+  const int term = bid / per_term;
+  const int rem = bid - term * per_term;
+  const int64_t rt = rem / p.ks;
+  const int split = rem - static_cast<int>(rt) * p.ks;
+  const int64_t kb0 = static_cast<int64_t>(split) * p.kb_per_split;
+  const int64_t kb1 = min(p.nkb, kb0 + p.kb_per_split);
+  const uint16_t* gam = p.t.gamma[term];
+  const uint32_t* bits = p.t.b2[term];
+  const int64_t row = rt * 64 + lane;
+
+  uint32_t wd[PW][KW];
+  load_pass_bits<TB, KW>(bits, rt, p.nkb, kb0, kb1, wd);
+  bool have_bits = true;
+  for (int64_t tok0 = 0; tok0 < p.T; tok0 += TB) {
+    A acc[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) acc[i] = A(0);
+    for (int64_t kp = kb0; kp < kb1; kp += kWaves * PW) {
+      if (!have_bits) load_pass_bits<TB, KW>(bits, rt, p.nkb, kp, kb1, wd);
+      have_bits = false;
+      const int64_t kb_end = min(kb1, kp + kWaves * PW);
+      const int64_t k0 = kp * 32 * KW;
+      const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
+      auto act4 = [&](int tok, int g, A* a) {
+        const int64_t tt = tok0 + tok, k = k0 + 4 * g;
+        if constexpr (MODE == MODE_F) {
+          if (tt < p.T && k + 4 <= p.M && p.vec4) {
+            const uint2 xv = *reinterpret_cast<const uint2*>(
+                static_cast<const uint16_t*>(p.x) + tt * p.ldx + k);
+            const uint2 gv = *reinterpret_cast<const uint2*>(gam + k);
+            const uint16_t xs[4] = {uint16_t(xv.x), uint16_t(xv.x >> 16), uint16_t(xv.y),
+                                    uint16_t(xv.y >> 16)};
+            const uint16_t gs[4] = {uint16_t(gv.x), uint16_t(gv.x >> 16), uint16_t(gv.y),
+                                    uint16_t(gv.y >> 16)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              a[j] = f16_bits_to_f32(gs[j]) * (p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xs[j])
+                                                                      : f16_bits_to_f32(xs[j]));
+            return;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          A v = A(0);
+          if (tt < p.T && k + j < p.M) {
+            if constexpr (MODE == MODE_F)
+              v = f16_bits_to_f32(gam[k + j]) * load_act(p.x, p.x_dtype, tt * p.ldx + k + j);
+            else
+              v = static_cast<const int8_t*>(p.x)[tt * p.ldx + k + j];
+          }
+          a[j] = v;
+        }
+      };
+      tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc);
+    }
+    reduce_waves<A, TB>(red, acc);
+    if (wv == 0 && row < p.R) {
+#pragma unroll
+      for (int tok = 0; tok < TB; ++tok) {
+        const int64_t tt = tok0 + tok;
+        if (tt < p.T) {
+          const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
+          if constexpr (MODE == MODE_F)
+            static_cast<float*>(p.ws)[o] = f16_bits_to_f32(p.t.beta[term][row]) * acc[tok];
+          else
+            static_cast<int32_t*>(p.ws)[o] = acc[tok];
+        }
+      }
+    }
+  }
+}
+
+// ---- completion counters between the two roles of a launch --------------
+// ctr[0]: producer workgroups done; ctr[1]: consumers past the wait;
+// ctr[2]: set if a wait gave up.
+
+// Producer: after its results are stored, one release and one increment.
+__device__ __forceinline__ void publish(unsigned* ctr) {
+  __syncthreads();  // every wave's stores are issued and complete in L2
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Consumer: wait until n_prod producers have published, then acquire.
+__device__ __forceinline__ void wait_producers(unsigned* ctr, unsigned n_prod) {
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_prod) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_fetch_or(ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// Consumer, once its wait is over (called at its end, off the critical
+// path): the last of n_cons consumers resets the counters for the next call.
+__device__ __forceinline__ void consumer_done(unsigned* ctr, unsigned n_cons) {
+  if (threadIdx.x == 0) {
+    if (__hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        n_cons - 1u) {
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Splits of stage 1 along M (at most kMaxKS, whole K-block groups of 4)
+// so that stage 1 has about `want_wg` workgroups.
+inline int pick_ks(int64_t nrt, int n_terms, int64_t nkb, int64_t want_wg,
+                   int64_t* kb_per_split) {
+  const int64_t want = want_wg / std::max<int64_t>(1, nrt * n_terms);
+  const int64_t maxks = std::max<int64_t>(1, nkb / kWaves);
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(std::min(want, maxks), kMaxKS));
+  int64_t per = (nkb + ks - 1) / ks;
+  per = (per + kWaves - 1) / kWaves * kWaves;
+  ks = (nkb + per - 1) / per;
+  *kb_per_split = per;
+  return static_cast<int>(ks);
+}
+
+}  // namespace lut
+
+// Stage-1 parameters of the decode path for these sizes (K-split so that
+// stage 1 has enough workgroups when `split`, else as few splits as the
+// partial buffer allows); *n1 = its number of workgroups.  ws is the
+// caller's workspace (counters first).
+lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x,
+                        int x_dtype, int64_t T, int64_t ldx, void* ws, bool split,
+                        int* n1);
+
+}  // namespace dbf

@@ -102,3 +102,13 @@ def test_row_flip_on_gpu():
     np.testing.assert_allclose(y2[:, 5], -y[:, 5], rtol=1e-5, atol=1e-5)
     rest = [n for n in range(128) if n != 5]
     assert np.array_equal(y2[:, rest], y[:, rest])
+
+
+@pytest.mark.parametrize("N,M,R,L,T", [(256, 4096, 2048, 1, 1), (64, 4096, 64, 1, 1),
+                                       (128, 1536, 256, 2, 1), (128, 8192, 512, 1, 2)])
+def test_partial_passes(N, M, R, L, T):
+    # K-splits shorter than a pass (the last waves of a pass have no block)
+    layer, x = S.make_custom(N, M, R, L, T, seed=21)
+    y = to_np(run(layer, x))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref)
