@@ -1,18 +1,419 @@
-// MFMA path of the double-binary layer (T large): not built yet.
+// MFMA path of the double-binary layer (large token counts): the two
+// sign-accumulate products of LoRDBA section 2 ("Kernel de Inferencia") /
+// DBF section 2 ("Inferencia") as two tiled products on the matrix cores,
+// with the +-1 signs unpacked from the packed bits straight into MFMA
+// operand registers (exact in fp16).
+//
+//   prep:     u_i = fp16(gamma_i . x) for every term, and per token
+//             l_i[t] = sum_m |u_i[t, m]|; bmax_i = max_r |beta_i[r]|
+//   scale:    s_t = 2^e, the largest power of two with
+//             s_t * max_i(bmax_i * l_i[t]) * (1 + 2^-8) <= 2^14; since
+//             |w_i[t, r]| <= bmax_i * l_i[t], every s_t * w fits fp16
+//   stage 1:  v_i[t, r] = fp16(s_t * beta_i[r] * sum_m S2_i[r, m] u_i[t, m])
+//   stage 2:  y[t, n] = (1 / s_t) sum_i sum_r (+-alpha_i[n]) v_i[t, r]
+//
+// Rounding: u and v are each rounded to fp16 once (relative 2^-11), all
+// sums are fp32; alpha, beta and the +-1 signs are exact in fp16.
+//
+// Operand order.  The MFMA sums over k, so any k order works as long as A
+// and B agree.  u and v are stored with each 32 features reordered as pairs
+// (k, k + 16): position 2j holds k = j, position 2j + 1 holds k = j + 16.
+// A lane then builds its B fragment for pairs (k, k + 16) from one 32-bit
+// word of its packed sign row with one shift and one v_and_or_b32 per pair:
+// bits k and k + 16 land on the two fp16 sign bits.  Stage 2 folds alpha
+// into those values (+-|alpha_n|, exact), so all terms accumulate into the
+// same registers.
+//
+// Tiles: a workgroup computes BM tokens x BN columns with 4 wavefronts, each
+// owning BN / 4 columns of all BM tokens with v_mfma_f32_32x32x16_f16.  K
+// advances 64 features per step; the fp16 activation tile (A) is copied
+// global -> LDS, double-buffered, with 16 bytes of padding per row
+// (conflict-free ds_read_b128 fragments).  Workgroup indices are remapped so
+// that consecutive tiles of one XCD share token rows (L2 reuse).  The tile
+// shape is chosen per launch so that at least ~256 workgroups run.
 #include "dbf_internal.h"
 
 namespace dbf {
+namespace {
 
-size_t mfma_ws_bytes(int64_t /*N*/, int64_t /*M*/, int64_t R, int n_terms,
-                     int64_t T) {
-  return static_cast<size_t>(n_terms) * static_cast<size_t>(T) *
-         static_cast<size_t>(ws_rstride(R)) * 4u;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 64;       // features per K step
+constexpr int kThreads = 256;
+constexpr int ALD = BK + 8;  // halves per LDS row of the A tile
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t kpad(int64_t K) { return (K + BK - 1) / BK * BK; }
+
+// Power-of-two scale of the fp16 intermediate from the bound b = max_i
+// bmax_i * l_i[t]: s * b * (1 + 2^-8) <= 2^14.
+__device__ __forceinline__ float scale_from_bound(float b) {
+  if (!(b > 0.f)) return 1.f;
+  int e = 0;
+  frexpf(b * (1.f + 1.f / 256.f), &e);  // b' = f * 2^e, f in [0.5, 1)
+  return ldexpf(1.f, 14 - e);
 }
 
-hipError_t launch_mfma(const TermPtrs&, int64_t, int64_t, int64_t, const void*,
-                       int, int64_t, int64_t, void*, int, int64_t, int, void*,
-                       hipStream_t) {
-  return hipErrorNotSupported;
+// ---- prep: u = fp16(gamma . x) in pair order, l1 norms, max |beta| --------
+struct PrepArgs {
+  const void* x;
+  int x_dtype;
+  int64_t ldx, T, M, mpad, R;
+  int L;
+  const uint16_t* gamma[DBF_MAX_TERMS];
+  const uint16_t* beta[DBF_MAX_TERMS];
+  _Float16* u;  // [L][T][mpad]
+  float* l1;    // [L][T]
+  float* bmax;  // [L]
+};
+
+__global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int64_t blk = blockIdx.x;
+  const int64_t nrow = static_cast<int64_t>(p.L) * p.T;
+  float acc = 0.f;
+  if (blk < nrow) {
+    const int term = static_cast<int>(blk / p.T);
+    const int64_t tok = blk - static_cast<int64_t>(term) * p.T;
+    const uint16_t* g = p.gamma[term];
+    _Float16* out = p.u + blk * p.mpad;
+    // one 16-byte chunk (8 halves) per thread and iteration: positions
+    // [8 c, 8 c + 8) of the row = pairs j0..j0+3 of a 32-group
+    for (int64_t c = tid; c < p.mpad / 8; c += 256) {
+      const int64_t grp = c >> 2, q4 = c & 3;
+      const int64_t k0 = grp * 32 + 4 * q4;
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t klo = k0 + j, khi = klo + 16;
+        float lo = 0.f, hi = 0.f;
+        if (klo < p.M)
+          lo = f16_bits_to_f32(g[klo]) * load_act(p.x, p.x_dtype, tok * p.ldx + klo);
+        if (khi < p.M)
+          hi = f16_bits_to_f32(g[khi]) * load_act(p.x, p.x_dtype, tok * p.ldx + khi);
+        const _Float16 a = static_cast<_Float16>(lo), b = static_cast<_Float16>(hi);
+        acc += fabsf(static_cast<float>(a)) + fabsf(static_cast<float>(b));
+        o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+      }
+      *reinterpret_cast<uint4*>(out + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    const int term = static_cast<int>(blk - nrow);
+    for (int64_t r = tid; r < p.R; r += 256)
+      acc = fmaxf(acc, fabsf(f16_bits_to_f32(p.beta[term][r])));
+  }
+  red[tid] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = blk < nrow ? red[tid] + red[tid + s] : fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (blk < nrow) p.l1[blk] = red[0];
+    else p.bmax[blk - nrow] = red[0];
+  }
+}
+
+// ---- the two products -------------------------------------------------
+struct GemmArgs {
+  int stage;  // 1 or 2
+  int L;
+  int64_t T, K, kp, ncols;  // per-term contraction length (and padded), columns
+  int64_t nkb, nrt;         // bit layout of the sign matrix (rows = ncols)
+  int kw;
+  int ntt, ntc;             // token tiles, column tiles of this launch
+  const uint32_t* bits[DBF_MAX_TERMS];
+  const uint16_t* colscale[DBF_MAX_TERMS];  // beta (stage 1) / alpha (stage 2)
+  const _Float16* a;        // A operand [L][T][kp] in pair order
+  const float* l1;          // [L][T]
+  const float* bmax;        // [L]
+  _Float16* v;              // stage-1 output [L][T][vp] in pair order
+  int64_t vp;
+  void* y;
+  int y_dtype;
+  int64_t ldy;
+  int accumulate;
+};
+
+// The 2 packed words this lane needs for one K step of one 32-column block:
+// row `col` of the sign matrix, features [kstep * 64, kstep * 64 + 64).
+__device__ __forceinline__ uint2 load_bits(const GemmArgs& p, const uint32_t* bits,
+                                           int64_t col, int64_t kstep) {
+  if (col >= p.nrt * 64) return make_uint2(0, 0);
+  const int64_t rt = col >> 6, rr = col & 63;
+  if (p.kw == 4) {
+    const uint32_t* src = bits + ((rt * p.nkb + (kstep >> 1)) * 64 + rr) * 4 + 2 * (kstep & 1);
+    return *reinterpret_cast<const uint2*>(src);
+  }
+  // kw < 4: a single K-block of kw words per row
+  const uint32_t* src = bits + (rt * 64 + rr) * p.kw;
+  const int w0 = static_cast<int>(2 * kstep), w1 = w0 + 1;
+  return make_uint2(w0 < p.kw ? src[w0] : 0u, w1 < p.kw ? src[w1] : 0u);
+}
+
+// B fragment (8 fp16) for word `wd` (sign-folded: a set bit is a negative
+// value) and feature pairs j = 8 * sub + 4 * h + q (q < 4) with j + 16.
+__device__ __forceinline__ half8 unpack_frag(uint32_t wd, int h, int sub, uint32_t mag) {
+  const uint32_t v = wd >> (4 * h);
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = ((v << (15 - 8 * sub - q)) & 0x80008000u) | mag;
+  return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
+  constexpr int RB = BM / 32;        // 32-token row blocks per wave
+  constexpr int CB = BN / 128;       // 32-column blocks per wave
+  constexpr int CH = BM * 8 / kThreads;  // 16-byte A chunks per thread per step
+  __shared__ __align__(16) _Float16 As[2][BM * ALD];
+  __shared__ float tokscale[BM];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 31, h = lane >> 5;
+
+  const int ntiles = p.ntt * p.ntc;
+  int b = blockIdx.x;
+  if (ntiles % 8 == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
+  const int ttile = b / p.ntc, ctile = b - ttile * p.ntc;
+  const int64_t tok0 = static_cast<int64_t>(ttile) * BM;
+  const int64_t col0 = static_cast<int64_t>(ctile) * BN;
+  const int term1 = p.stage == 1 ? static_cast<int>(blockIdx.y) : 0;
+
+  if (tid < BM) {
+    const int64_t tok = tok0 + tid;
+    float bnd = 0.f;
+    if (tok < p.T)
+      for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
+    tokscale[tid] = scale_from_bound(bnd);
+  }
+
+  const int64_t spt = p.kp / BK;  // K steps per term
+  const int64_t nsteps = (p.stage == 1 ? 1 : p.L) * spt;
+
+  uint4 areg[CH];
+  auto load_a = [&](int64_t step) {
+    const int term = p.stage == 1 ? term1 : static_cast<int>(step / spt);
+    const int64_t kbase = (p.stage == 1 ? step : step - static_cast<int64_t>(term) * spt) * BK;
+    const _Float16* base = p.a + static_cast<int64_t>(term) * p.T * p.kp + kbase;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
+      const int64_t tok = tok0 + row;
+      areg[q] = tok < p.T ? *reinterpret_cast<const uint4*>(base + tok * p.kp + 8 * ch)
+                          : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
+      *reinterpret_cast<uint4*>(&As[buf][row * ALD + 8 * ch]) = areg[q];
+    }
+  };
+
+  int64_t bcol[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) bcol[cb] = col0 + (BN / 4) * wv + 32 * cb + li;
+  uint2 bw[CB];
+  auto load_b = [&](int64_t step) {
+    const int term = p.stage == 1 ? term1 : static_cast<int>(step / spt);
+    const int64_t ks = p.stage == 1 ? step : step - static_cast<int64_t>(term) * spt;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) bw[cb] = load_bits(p, p.bits[term], bcol[cb], ks);
+  };
+  uint32_t flip[CB], mag[CB];
+  int cur_term = -1;
+  auto set_term = [&](int term) {
+    if (term == cur_term) return;
+    cur_term = term;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      if (p.stage == 1) {
+        flip[cb] = 0xFFFFFFFFu;  // bit 1 (+1) -> sign bit 0
+        mag[cb] = 0x3C003C00u;   // 1.0, 1.0
+      } else {
+        const uint16_t a = bcol[cb] < p.ncols ? p.colscale[term][bcol[cb]] : uint16_t(0);
+        flip[cb] = (a & 0x8000u) ? 0u : 0xFFFFFFFFu;
+        const uint32_t m = a & 0x7FFFu;
+        mag[cb] = m | (m << 16);
+      }
+    }
+  };
+
+  floatx16 acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  for (int64_t step = 0; step < nsteps; ++step) {
+    const int buf = static_cast<int>(step & 1);
+    set_term(p.stage == 1 ? term1 : static_cast<int>(step / spt));
+    uint2 cw[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) cw[cb] = bw[cb];
+    __syncthreads();
+    if (step + 1 < nsteps) {
+      load_a(step + 1);
+      load_b(step + 1);
+    }
+    const _Float16* at = As[buf];
+#pragma unroll
+    for (int wi = 0; wi < 2; ++wi) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        half8 bf[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          bf[cb] = unpack_frag((wi == 0 ? cw[cb].x : cw[cb].y) ^ flip[cb], h, sub, mag[cb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const half8 af = *reinterpret_cast<const half8*>(
+              at + (32 * rb + li) * ALD + 32 * wi + 16 * sub + 8 * h);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+    if (step + 1 < nsteps) store_a(buf ^ 1);
+  }
+
+  // epilogue; D layout: lane l, register r -> column l % 32,
+  // row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the 32 x 32 block
+  if (p.stage == 1) {
+    // v = fp16(s_t * beta_r * acc) at the pair-order position of r
+    _Float16* vt = p.v + static_cast<int64_t>(term1) * p.T * p.vp;
+    float bsc[CB];
+    int64_t vpos[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      bsc[cb] = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term1][bcol[cb]]) : 0.f;
+      const int64_t r = bcol[cb], g = r >> 5, rr = r & 31;
+      vpos[cb] = g * 32 + (rr < 16 ? 2 * rr : 2 * (rr - 16) + 1);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t tok = tok0 + rl;
+        if (tok >= p.T) continue;
+        const float sc = tokscale[rl];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          if (bcol[cb] < p.vp)
+            vt[tok * p.vp + vpos[cb]] = static_cast<_Float16>(sc * bsc[cb] * acc[rb][cb][r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t tok = tok0 + rl;
+        if (tok >= p.T) continue;
+        const float inv = 1.0f / tokscale[rl];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          if (bcol[cb] < p.ncols)
+            store_out(p.y, p.y_dtype, tok * p.ldy + bcol[cb], acc[rb][cb][r] * inv,
+                      p.accumulate);
+      }
+    }
+  }
+}
+
+// Tile shape for T tokens and `cols` output columns: the largest of
+// 128 x 256, 128 x 128, 64 x 128 that still gives >= 256 workgroups.
+hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_t s) {
+  auto wgs = [&](int bm, int bn) { return cdiv(a.T, bm) * cdiv(cols, bn) * terms_in_grid; };
+  int bm = 128, bn = 256;
+  if (wgs(128, 256) < 256) { bn = 128; }
+  if (wgs(128, 128) < 256) { bm = 64; }
+  a.ntt = static_cast<int>(cdiv(a.T, bm));
+  a.ntc = static_cast<int>(cdiv(cols, bn));
+  const dim3 grid(static_cast<unsigned>(a.ntt * a.ntc), terms_in_grid);
+  if (bm == 128 && bn == 256) gemm_kernel<128, 256><<<grid, kThreads, 0, s>>>(a);
+  else if (bm == 128) gemm_kernel<128, 128><<<grid, kThreads, 0, s>>>(a);
+  else gemm_kernel<64, 128><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+struct WsLayout {
+  size_t u, v, l1, bmax, total;
+};
+
+WsLayout ws_layout(int64_t M, int64_t R, int L, int64_t T) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  WsLayout w{};
+  size_t off = kDecodeCounterBytes;
+  w.u = off; off += al(static_cast<size_t>(L) * T * kpad(M) * 2);
+  w.v = off; off += al(static_cast<size_t>(L) * T * kpad(R) * 2);
+  w.l1 = off; off += al(static_cast<size_t>(L) * T * 4);
+  w.bmax = off; off += al(static_cast<size_t>(L) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t mfma_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t T) {
+  return ws_layout(M, R, n_terms, T).total;
+}
+
+hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
+                       const void* x, int x_dtype, int64_t T, int64_t ldx,
+                       void* y, int y_dtype, int64_t ldy, int accumulate,
+                       void* ws, hipStream_t s) {
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  const WsLayout lay = ws_layout(M, R, t.n, T);
+  _Float16* u = reinterpret_cast<_Float16*>(base + lay.u);
+  _Float16* v = reinterpret_cast<_Float16*>(base + lay.v);
+  float* l1 = reinterpret_cast<float*>(base + lay.l1);
+  float* bmax = reinterpret_cast<float*>(base + lay.bmax);
+
+  PrepArgs pa{};
+  pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
+  pa.R = R; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
+  for (int i = 0; i < t.n; ++i) {
+    pa.gamma[i] = t.gamma[i];
+    pa.beta[i] = t.beta[i];
+  }
+  prep_kernel<<<dim3(static_cast<unsigned>(t.n * T + t.n)), 256, 0, s>>>(pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  GemmArgs a{};
+  a.stage = 1; a.L = t.n; a.T = T; a.K = M; a.kp = kpad(M); a.ncols = R;
+  a.nkb = layout_nkb(M); a.nrt = layout_nrt(R); a.kw = static_cast<int>(layout_kw(M));
+  for (int i = 0; i < t.n; ++i) {
+    a.bits[i] = t.b2[i];
+    a.colscale[i] = t.beta[i];
+  }
+  a.a = u; a.l1 = l1; a.bmax = bmax; a.v = v; a.vp = kpad(R);
+  e = launch_tiled(a, R, t.n, s);
+  if (e != hipSuccess) return e;
+
+  GemmArgs b = a;
+  b.stage = 2; b.K = R; b.kp = kpad(R); b.ncols = N;
+  b.nkb = layout_nkb(R); b.nrt = layout_nrt(N); b.kw = static_cast<int>(layout_kw(R));
+  for (int i = 0; i < t.n; ++i) {
+    b.bits[i] = t.b1[i];
+    b.colscale[i] = t.alpha[i];
+  }
+  b.a = v;
+  b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
+  return launch_tiled(b, N, 1, s);
 }
 
 }  // namespace dbf

@@ -1,0 +1,113 @@
+"""dbf_linear_forward on the MFMA path against the fp64 oracle.
+
+The MFMA path rounds gamma . x and the per-token-scaled rank-R intermediate
+to fp16 (relative ~2^-11 each), so it meets the same float tolerance as the
+decode path.  At 4096 tokens the oracle is evaluated on a sample of tokens
+(every token is independent)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_adapters_amd as D
+import oracle as O
+from bit_adapters_amd import synth as S
+from dbfutil import (DEV, assert_close, device_terms, round_bf16, to_np, x64,
+                     x_dev)
+
+pytestmark = pytest.mark.gpu
+
+MF = D.DBF_PATH_MFMA
+
+
+def run(layer, x, path=MF, **kw):
+    terms = device_terms(layer)
+    y = D.dbf_linear_forward(terms, layer["N"], layer["M"], layer["R"], x_dev(x),
+                             path=path, **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+ODD = [(1, 1, 1, 1, 1), (65, 33, 17, 2, 3), (130, 300, 70, 3, 5),
+       (300, 129, 257, 1, 130), (256, 256, 256, 1, 128), (77, 1000, 96, 2, 200),
+       (513, 64, 600, 1, 17), (40, 4100, 130, 1, 33)]
+
+
+@pytest.mark.parametrize("N,M,R,L,T", ODD)
+@pytest.mark.parametrize("xk", ["bf16", "f16"])
+def test_odd_shapes(N, M, R, L, T, xk):
+    print("mfma odd", N, M, R, L, T, xk, flush=True)
+    layer, x = S.make_custom(N, M, R, L, T, seed=N * 3 + M + R, x_kind=xk)
+    y = to_np(run(layer, x))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref)
+
+
+@pytest.mark.parametrize("T", [64, 256])
+def test_config4(T):
+    print("mfma config 4 T", T, flush=True)
+    layer = S.make_layer(4)
+    x = S.make_x(4, T)
+    y = to_np(run(layer, x, path=D.DBF_PATH_AUTO))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref)
+
+
+def test_config2_forced_mfma():
+    layer = S.make_layer(2)
+    x = S.make_x(2, 16)
+    y = to_np(run(layer, x))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref)
+
+
+def test_config5_sampled_tokens():
+    print("mfma config 5", flush=True)
+    layer = S.make_layer(5)
+    x = S.make_x(5, 4096)
+    y = run(layer, x, path=D.DBF_PATH_AUTO)
+    toks = np.array([0, 1, 127, 128, 1000, 2047, 2048, 3333, 4094, 4095])
+    got = to_np(y[torch.from_numpy(toks).to(DEV)])
+    ref = O.default().forward(O.terms64(layer), x64(x[toks]))
+    assert_close(got, ref)
+    # every output is finite and the rest of the output is not garbage:
+    # row norms of y track those of the sampled reference
+    yn = y.float().norm(dim=1).cpu().numpy()
+    assert np.all(np.isfinite(yn))
+    rn = np.linalg.norm(ref, axis=1)
+    assert np.all(yn > 0.5 * rn.min()) and np.all(yn < 2.0 * rn.max())
+
+
+def test_output_dtypes_accumulate_strides():
+    layer, x = S.make_custom(96, 200, 40, 2, 150, seed=3)
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    terms = device_terms(layer)
+    xd = torch.zeros((150, 208), dtype=torch.bfloat16, device=DEV)
+    xd[:, :200] = x_dev(x)
+    xs = xd[:, :200]
+    big = torch.full((150, 100), 7.0, dtype=torch.float32, device=DEV)
+    y = big[:, :96]
+    D.dbf_linear_forward(terms, 96, 200, 40, xs, y=y, path=MF)
+    torch.cuda.synchronize()
+    assert_close(to_np(y), ref)
+    assert torch.all(big[:, 96:] == 7.0)
+    base = torch.randn((150, 96), dtype=torch.float32, device=DEV)
+    y2 = base.clone()
+    D.dbf_linear_forward(terms, 96, 200, 40, xs, y=y2, accumulate=True, path=MF)
+    torch.cuda.synchronize()
+    assert_close(to_np(y2), ref + to_np(base))
+    yb = D.dbf_linear_forward(terms, 96, 200, 40, xs, y_dtype=torch.bfloat16, path=MF)
+    torch.cuda.synchronize()
+    assert_close(to_np(yb), round_bf16(ref), rel_l2=4e-3)
+
+
+def test_deterministic_and_scale_invariant():
+    layer, x = S.make_custom(300, 500, 200, 2, 140, seed=8)
+    a = run(layer, x).cpu()
+    b = run(layer, x).cpu()
+    assert torch.equal(a, b)
+    # a power-of-two scale of x scales y exactly (the per-token scale absorbs it)
+    xs = x_dev(x) * 64.0
+    terms = device_terms(layer)
+    c = D.dbf_linear_forward(terms, 300, 500, 200, xs, path=MF)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cpu(), a * 64.0)
