@@ -31,6 +31,8 @@
 // (conflict-free ds_read_b128 fragments).  Workgroup indices are remapped so
 // that consecutive tiles of one XCD share token rows (L2 reuse).  The tile
 // shape is chosen per launch so that at least ~256 workgroups run.
+#include <type_traits>
+
 #include "dbf_internal.h"
 
 namespace dbf {
@@ -66,6 +68,7 @@ struct PrepArgs {
   _Float16* u;  // [L][T][mpad]
   float* l1;    // [L][T]
   float* bmax;  // [L]
+  int vec;      // 8-byte loads of x and gamma allowed
 };
 
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
@@ -81,19 +84,39 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
     _Float16* out = p.u + blk * p.mpad;
     // one 16-byte chunk (8 halves) per thread and iteration: positions
     // [8 c, 8 c + 8) of the row = pairs j0..j0+3 of a 32-group
+    const uint16_t* xr = static_cast<const uint16_t*>(p.x) + tok * p.ldx;
     for (int64_t c = tid; c < p.mpad / 8; c += 256) {
       const int64_t grp = c >> 2, q4 = c & 3;
       const int64_t k0 = grp * 32 + 4 * q4;
+      float lo[4], hi[4];
+      if (p.vec && k0 + 20 <= p.M) {
+        const uint2 xl = *reinterpret_cast<const uint2*>(xr + k0);
+        const uint2 xh = *reinterpret_cast<const uint2*>(xr + k0 + 16);
+        const uint2 gl = *reinterpret_cast<const uint2*>(g + k0);
+        const uint2 gh = *reinterpret_cast<const uint2*>(g + k0 + 16);
+        const uint32_t xv[4] = {xl.x, xl.y, xh.x, xh.y}, gv[4] = {gl.x, gl.y, gh.x, gh.y};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int wi = j >> 1, sh = (j & 1) * 16;
+          const uint16_t xa = static_cast<uint16_t>(xv[wi] >> sh);
+          const uint16_t xb = static_cast<uint16_t>(xv[2 + wi] >> sh);
+          const float fa = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xa) : f16_bits_to_f32(xa);
+          const float fb = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
+          lo[j] = f16_bits_to_f32(static_cast<uint16_t>(gv[wi] >> sh)) * fa;
+          hi[j] = f16_bits_to_f32(static_cast<uint16_t>(gv[2 + wi] >> sh)) * fb;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t klo = k0 + j, khi = klo + 16;
+          lo[j] = klo < p.M ? f16_bits_to_f32(g[klo]) * load_act(p.x, p.x_dtype, tok * p.ldx + klo) : 0.f;
+          hi[j] = khi < p.M ? f16_bits_to_f32(g[khi]) * load_act(p.x, p.x_dtype, tok * p.ldx + khi) : 0.f;
+        }
+      }
       uint32_t o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t klo = k0 + j, khi = klo + 16;
-        float lo = 0.f, hi = 0.f;
-        if (klo < p.M)
-          lo = f16_bits_to_f32(g[klo]) * load_act(p.x, p.x_dtype, tok * p.ldx + klo);
-        if (khi < p.M)
-          hi = f16_bits_to_f32(g[khi]) * load_act(p.x, p.x_dtype, tok * p.ldx + khi);
-        const _Float16 a = static_cast<_Float16>(lo), b = static_cast<_Float16>(hi);
+        const _Float16 a = static_cast<_Float16>(lo[j]), b = static_cast<_Float16>(hi[j]);
         acc += fabsf(static_cast<float>(a)) + fabsf(static_cast<float>(b));
         o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
@@ -138,22 +161,6 @@ struct GemmArgs {
   int accumulate;
 };
 
-// The 2 packed words this lane needs for one K step of one 32-column block:
-// row `col` of the sign matrix, features [kstep * 64, kstep * 64 + 64).
-__device__ __forceinline__ uint2 load_bits(const GemmArgs& p, const uint32_t* bits,
-                                           int64_t col, int64_t kstep) {
-  if (col >= p.nrt * 64) return make_uint2(0, 0);
-  const int64_t rt = col >> 6, rr = col & 63;
-  if (p.kw == 4) {
-    const uint32_t* src = bits + ((rt * p.nkb + (kstep >> 1)) * 64 + rr) * 4 + 2 * (kstep & 1);
-    return *reinterpret_cast<const uint2*>(src);
-  }
-  // kw < 4: a single K-block of kw words per row
-  const uint32_t* src = bits + (rt * 64 + rr) * p.kw;
-  const int w0 = static_cast<int>(2 * kstep), w1 = w0 + 1;
-  return make_uint2(w0 < p.kw ? src[w0] : 0u, w1 < p.kw ? src[w1] : 0u);
-}
-
 // B fragment (8 fp16) for word `wd` (sign-folded: a set bit is a negative
 // value) and feature pairs j = 8 * sub + 4 * h + q (q < 4) with j + 16.
 __device__ __forceinline__ half8 unpack_frag(uint32_t wd, int h, int sub, uint32_t mag) {
@@ -164,10 +171,13 @@ __device__ __forceinline__ half8 unpack_frag(uint32_t wd, int h, int sub, uint32
   return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-template <int BM, int BN>
+// STAGE 1: one term per grid row (blockIdx.y); STAGE 2: all terms in turn.
+// KW4: the sign matrix has 4 words per row per tile (K >= 97); otherwise a
+// single K-block of kw words per row.
+template <int STAGE, bool KW4, int BM, int BN>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
-  constexpr int RB = BM / 32;        // 32-token row blocks per wave
-  constexpr int CB = BN / 128;       // 32-column blocks per wave
+  constexpr int RB = BM / 32;            // 32-token row blocks per wave
+  constexpr int CB = BN / 128;           // 32-column blocks per wave
   constexpr int CH = BM * 8 / kThreads;  // 16-byte A chunks per thread per step
   __shared__ __align__(16) _Float16 As[2][BM * ALD];
   __shared__ float tokscale[BM];
@@ -180,58 +190,84 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
   const int ttile = b / p.ntc, ctile = b - ttile * p.ntc;
   const int64_t tok0 = static_cast<int64_t>(ttile) * BM;
   const int64_t col0 = static_cast<int64_t>(ctile) * BN;
-  const int term1 = p.stage == 1 ? static_cast<int>(blockIdx.y) : 0;
+  const int term_first = STAGE == 1 ? static_cast<int>(blockIdx.y) : 0;
+  const int term_end = STAGE == 1 ? term_first + 1 : p.L;
 
   if (tid < BM) {
     const int64_t tok = tok0 + tid;
     float bnd = 0.f;
     if (tok < p.T)
-      for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
+      for (int i = 0; i < p.L; ++i)
+        bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
     tokscale[tid] = scale_from_bound(bnd);
   }
 
-  const int64_t spt = p.kp / BK;  // K steps per term
-  const int64_t nsteps = (p.stage == 1 ? 1 : p.L) * spt;
+  const int spt = static_cast<int>(p.kp / BK);  // K steps per term
 
-  uint4 areg[CH];
-  auto load_a = [&](int64_t step) {
-    const int term = p.stage == 1 ? term1 : static_cast<int>(step / spt);
-    const int64_t kbase = (p.stage == 1 ? step : step - static_cast<int64_t>(term) * spt) * BK;
-    const _Float16* base = p.a + static_cast<int64_t>(term) * p.T * p.kp + kbase;
+  // per-thread A chunk offsets (row, 16-byte column) and validity
+  int64_t aoff[CH];
+  bool aok[CH];
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
-      const int64_t tok = tok0 + row;
-      areg[q] = tok < p.T ? *reinterpret_cast<const uint4*>(base + tok * p.kp + 8 * ch)
-                          : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(&As[buf][row * ALD + 8 * ch]) = areg[q];
-    }
-  };
-
+  for (int q = 0; q < CH; ++q) {
+    const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
+    aok[q] = tok0 + row < p.T;
+    aoff[q] = (tok0 + row) * p.kp + 8 * ch;
+  }
+  // per-lane packed row offsets (in words) of this wave's columns
+  int64_t boff[CB];
+  bool bok[CB];
   int64_t bcol[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) bcol[cb] = col0 + (BN / 4) * wv + 32 * cb + li;
-  uint2 bw[CB];
-  auto load_b = [&](int64_t step) {
-    const int term = p.stage == 1 ? term1 : static_cast<int>(step / spt);
-    const int64_t ks = p.stage == 1 ? step : step - static_cast<int64_t>(term) * spt;
+  for (int cb = 0; cb < CB; ++cb) {
+    bcol[cb] = col0 + (BN / 4) * wv + 32 * cb + li;
+    bok[cb] = bcol[cb] < p.nrt * 64;
+    const int64_t rt = bcol[cb] >> 6, rr = bcol[cb] & 63;
+    boff[cb] = KW4 ? (rt * p.nkb * 64 + rr) * 4 : (rt * 64 + rr) * p.kw;
+  }
+
+  // load cursor: (term, step within the term), advanced one step at a time
+  int lterm = term_first, lks = 0;
+  uint4 areg[2][CH];
+  uint2 bw[2][CB];
+  auto issue = [&](auto slot) {
+    constexpr int S = decltype(slot)::value;
+    const _Float16* base = p.a + static_cast<int64_t>(lterm) * p.T * p.kp + lks * BK;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) bw[cb] = load_bits(p, p.bits[term], bcol[cb], ks);
-  };
-  uint32_t flip[CB], mag[CB];
-  int cur_term = -1;
-  auto set_term = [&](int term) {
-    if (term == cur_term) return;
-    cur_term = term;
+    for (int q = 0; q < CH; ++q)
+      areg[S][q] = aok[q] ? *reinterpret_cast<const uint4*>(base + aoff[q]) : make_uint4(0, 0, 0, 0);
+    const uint32_t* bits = p.bits[lterm];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      if (p.stage == 1) {
+      if (!bok[cb]) {
+        bw[S][cb] = make_uint2(0, 0);
+      } else if constexpr (KW4) {
+        bw[S][cb] = *reinterpret_cast<const uint2*>(bits + boff[cb] + (lks >> 1) * 256 + 2 * (lks & 1));
+      } else {
+        const int w0 = 2 * lks, w1 = w0 + 1;
+        const uint32_t* src = bits + boff[cb];
+        bw[S][cb] = make_uint2(w0 < p.kw ? src[w0] : 0u, w1 < p.kw ? src[w1] : 0u);
+      }
+    }
+    if (++lks == spt) {
+      lks = 0;
+      ++lterm;
+    }
+  };
+  auto store_a = [&](auto buf) {
+    constexpr int S = decltype(buf)::value;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
+      *reinterpret_cast<uint4*>(&As[S][row * ALD + 8 * ch]) = areg[S][q];
+    }
+  };
+
+  // sign fold and magnitude per column block (stage 2: +-|alpha|, stage 1: +-1)
+  uint32_t flip[CB], mag[CB];
+  auto set_term = [&](int term) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      if constexpr (STAGE == 1) {
         flip[cb] = 0xFFFFFFFFu;  // bit 1 (+1) -> sign bit 0
         mag[cb] = 0x3C003C00u;   // 1.0, 1.0
       } else {
@@ -251,21 +287,25 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  for (int64_t step = 0; step < nsteps; ++step) {
-    const int buf = static_cast<int>(step & 1);
-    set_term(p.stage == 1 ? term1 : static_cast<int>(step / spt));
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  const int nsteps = (term_end - term_first) * spt;
+  // pipeline: LDS holds step s (buffer s & 1); registers hold steps s + 1
+  // (slot (s + 1) & 1) and s + 2 (slot s & 1, issued during step s)
+  issue(I0{});
+  if (nsteps > 1) issue(I1{});
+  store_a(I0{});
+  int cterm = term_first, cks = 0;  // compute cursor
+  set_term(cterm);
+  auto kstep = [&](int step, auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    using Other = std::integral_constant<int, B ^ 1>;
     uint2 cw[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) cw[cb] = bw[cb];
+    for (int cb = 0; cb < CB; ++cb) cw[cb] = bw[B][cb];
     __syncthreads();
-    if (step + 1 < nsteps) {
-      load_a(step + 1);
-      load_b(step + 1);
-    }
-    const _Float16* at = As[buf];
+    if (step + 2 < nsteps) issue(bufc);
+    const _Float16* at = As[B];
 #pragma unroll
     for (int wi = 0; wi < 2; ++wi) {
 #pragma unroll
@@ -284,19 +324,27 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
         }
       }
     }
-    if (step + 1 < nsteps) store_a(buf ^ 1);
+    if (step + 1 < nsteps) store_a(Other{});
+    if (STAGE == 2 && ++cks == spt) {
+      cks = 0;
+      if (++cterm < term_end) set_term(cterm);
+    }
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    kstep(step, I0{});
+    if (step + 1 < nsteps) kstep(step + 1, I1{});
   }
 
   // epilogue; D layout: lane l, register r -> column l % 32,
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the 32 x 32 block
-  if (p.stage == 1) {
+  if constexpr (STAGE == 1) {
     // v = fp16(s_t * beta_r * acc) at the pair-order position of r
-    _Float16* vt = p.v + static_cast<int64_t>(term1) * p.T * p.vp;
+    _Float16* vt = p.v + static_cast<int64_t>(term_first) * p.T * p.vp;
     float bsc[CB];
     int64_t vpos[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      bsc[cb] = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term1][bcol[cb]]) : 0.f;
+      bsc[cb] = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term_first][bcol[cb]]) : 0.f;
       const int64_t r = bcol[cb], g = r >> 5, rr = r & 31;
       vpos[cb] = g * 32 + (rr < 16 ? 2 * rr : 2 * (rr - 16) + 1);
     }
@@ -335,6 +383,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 
 // Tile shape for T tokens and `cols` output columns: the largest of
 // 128 x 256, 128 x 128, 64 x 128 that still gives >= 256 workgroups.
+template <int STAGE, bool KW4>
 hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_t s) {
   auto wgs = [&](int bm, int bn) { return cdiv(a.T, bm) * cdiv(cols, bn) * terms_in_grid; };
   int bm = 128, bn = 256;
@@ -343,10 +392,16 @@ hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_
   a.ntt = static_cast<int>(cdiv(a.T, bm));
   a.ntc = static_cast<int>(cdiv(cols, bn));
   const dim3 grid(static_cast<unsigned>(a.ntt * a.ntc), terms_in_grid);
-  if (bm == 128 && bn == 256) gemm_kernel<128, 256><<<grid, kThreads, 0, s>>>(a);
-  else if (bm == 128) gemm_kernel<128, 128><<<grid, kThreads, 0, s>>>(a);
-  else gemm_kernel<64, 128><<<grid, kThreads, 0, s>>>(a);
+  if (bm == 128 && bn == 256) gemm_kernel<STAGE, KW4, 128, 256><<<grid, kThreads, 0, s>>>(a);
+  else if (bm == 128) gemm_kernel<STAGE, KW4, 128, 128><<<grid, kThreads, 0, s>>>(a);
+  else gemm_kernel<STAGE, KW4, 64, 128><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int STAGE>
+hipError_t launch_stage(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_t s) {
+  return a.kw == 4 ? launch_tiled<STAGE, true>(a, cols, terms_in_grid, s)
+                   : launch_tiled<STAGE, false>(a, cols, terms_in_grid, s);
 }
 
 struct WsLayout {
@@ -385,6 +440,9 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   PrepArgs pa{};
   pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
   pa.R = R; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
+  pa.vec = (ldx % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 8 == 0);
+  for (int i = 0; i < t.n; ++i)
+    if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) pa.vec = 0;
   for (int i = 0; i < t.n; ++i) {
     pa.gamma[i] = t.gamma[i];
     pa.beta[i] = t.beta[i];
@@ -401,7 +459,7 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
     a.colscale[i] = t.beta[i];
   }
   a.a = u; a.l1 = l1; a.bmax = bmax; a.v = v; a.vp = kpad(R);
-  e = launch_tiled(a, R, t.n, s);
+  e = launch_stage<1>(a, R, t.n, s);
   if (e != hipSuccess) return e;
 
   GemmArgs b = a;
@@ -413,7 +471,7 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   }
   b.a = v;
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
-  return launch_tiled(b, N, 1, s);
+  return launch_stage<2>(b, N, 1, s);
 }
 
 }  // namespace dbf
