@@ -26,7 +26,8 @@
 //
 // Tiles: a workgroup computes BM tokens x BN columns with 4 wavefronts, each
 // owning BN / 4 columns of all BM tokens with v_mfma_f32_32x32x16_f16.  K
-// advances 64 features per step; the fp16 activation tile (A) is copied
+// advances 128 features (one K-block of the bit layout) per step; the fp16
+// activation tile (A) is copied
 // global -> LDS, double-buffered, with 16 bytes of padding per row
 // (conflict-free ds_read_b128 fragments).  Workgroup indices are remapped so
 // that consecutive tiles of one XCD share token rows (L2 reuse).  The tile
@@ -41,7 +42,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;       // features per K step
+constexpr int BK = 128;      // features per K step (one K-block of the bit layout)
 constexpr int kThreads = 256;
 constexpr int ALD = BK + 8;  // halves per LDS row of the A tile
 
@@ -162,24 +163,37 @@ struct GemmArgs {
 };
 
 // B fragment (8 fp16) for word `wd` (sign-folded: a set bit is a negative
-// value) and feature pairs j = 8 * sub + 4 * h + q (q < 4) with j + 16.
+// value) and feature pairs j = 8 * sub + 4 * h + q (q < 4) with j + 16:
+// per pair one shift puts bits j and j + 16 on the two fp16 sign bits and
+// one v_bfi_b32 merges in the magnitude pair `mag`.  `mag` must come from
+// opaque() so that the compiler cannot see its clear sign bits and turn the
+// bit insert back into an AND and an OR.
 __device__ __forceinline__ half8 unpack_frag(uint32_t wd, int h, int sub, uint32_t mag) {
   const uint32_t v = wd >> (4 * h);
   uint32_t o[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = ((v << (15 - 8 * sub - q)) & 0x80008000u) | mag;
+  for (int q = 0; q < 4; ++q)
+    o[q] = ((v << (15 - 8 * sub - q)) & 0x80008000u) | (mag & 0x7FFF7FFFu);
   return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// The value unchanged, but unknown to the optimizer (emits no instruction).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
 }
 
 // STAGE 1: one term per grid row (blockIdx.y); STAGE 2: all terms in turn.
 // KW4: the sign matrix has 4 words per row per tile (K >= 97); otherwise a
 // single K-block of kw words per row.
-template <int STAGE, bool KW4, int BM, int BN>
+// NS: K steps of A and sign words prefetched into registers (1 or 2).
+template <int STAGE, bool KW4, int BM, int BN, int NS>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
   constexpr int RB = BM / 32;            // 32-token row blocks per wave
   constexpr int CB = BN / 128;           // 32-column blocks per wave
-  constexpr int CH = BM * 8 / kThreads;  // 16-byte A chunks per thread per step
-  __shared__ __align__(16) _Float16 As[2][BM * ALD];
+  constexpr int CH = BM * (BK / 8) / kThreads;  // 16-byte A chunks per thread per step
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  _Float16 (*As)[BM * ALD] = reinterpret_cast<_Float16 (*)[BM * ALD]>(smem_raw);
   __shared__ float tokscale[BM];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 31, h = lane >> 5;
@@ -209,7 +223,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
   bool aok[CH];
 #pragma unroll
   for (int q = 0; q < CH; ++q) {
-    const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
+    const int c = tid + q * kThreads, row = c / (BK / 8), ch = c % (BK / 8);
     aok[q] = tok0 + row < p.T;
     aoff[q] = (tok0 + row) * p.kp + 8 * ch;
   }
@@ -227,8 +241,8 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 
   // load cursor: (term, step within the term), advanced one step at a time
   int lterm = term_first, lks = 0;
-  uint4 areg[2][CH];
-  uint2 bw[2][CB];
+  uint4 areg[NS][CH];
+  uint4 bw[NS][CB];
   auto issue = [&](auto slot) {
     constexpr int S = decltype(slot)::value;
     const _Float16* base = p.a + static_cast<int64_t>(lterm) * p.T * p.kp + lks * BK;
@@ -239,13 +253,16 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       if (!bok[cb]) {
-        bw[S][cb] = make_uint2(0, 0);
+        bw[S][cb] = make_uint4(0, 0, 0, 0);
       } else if constexpr (KW4) {
-        bw[S][cb] = *reinterpret_cast<const uint2*>(bits + boff[cb] + (lks >> 1) * 256 + 2 * (lks & 1));
+        bw[S][cb] = *reinterpret_cast<const uint4*>(bits + boff[cb] + static_cast<int64_t>(lks) * 256);
       } else {
-        const int w0 = 2 * lks, w1 = w0 + 1;
+        // a single K-block of kw < 4 words per row
         const uint32_t* src = bits + boff[cb];
-        bw[S][cb] = make_uint2(w0 < p.kw ? src[w0] : 0u, w1 < p.kw ? src[w1] : 0u);
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = j < p.kw ? src[j] : 0u;
+        bw[S][cb] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
     if (++lks == spt) {
@@ -253,12 +270,12 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
       ++lterm;
     }
   };
-  auto store_a = [&](auto buf) {
-    constexpr int S = decltype(buf)::value;
+  auto store_a = [&](auto buf, auto slot) {
+    constexpr int Bf = decltype(buf)::value, S = decltype(slot)::value;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      const int c = tid + q * kThreads, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(&As[S][row * ALD + 8 * ch]) = areg[S][q];
+      const int c = tid + q * kThreads, row = c / (BK / 8), ch = c % (BK / 8);
+      *reinterpret_cast<uint4*>(&As[Bf][row * ALD + 8 * ch]) = areg[S][q];
     }
   };
 
@@ -268,13 +285,13 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       if constexpr (STAGE == 1) {
-        flip[cb] = 0xFFFFFFFFu;  // bit 1 (+1) -> sign bit 0
-        mag[cb] = 0x3C003C00u;   // 1.0, 1.0
+        flip[cb] = 0xFFFFFFFFu;           // bit 1 (+1) -> sign bit 0
+        mag[cb] = opaque(0x3C003C00u);    // 1.0, 1.0
       } else {
         const uint16_t a = bcol[cb] < p.ncols ? p.colscale[term][bcol[cb]] : uint16_t(0);
         flip[cb] = (a & 0x8000u) ? 0u : 0xFFFFFFFFu;
         const uint32_t m = a & 0x7FFFu;
-        mag[cb] = m | (m << 16);
+        mag[cb] = opaque(m | (m << 16));
       }
     }
   };
@@ -290,30 +307,43 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   const int nsteps = (term_end - term_first) * spt;
-  // pipeline: LDS holds step s (buffer s & 1); registers hold steps s + 1
-  // (slot (s + 1) & 1) and s + 2 (slot s & 1, issued during step s)
+  // pipeline: LDS holds step s (buffer s & 1).  NS = 2: registers hold
+  // steps s + 1 (slot (s + 1) & 1) and s + 2 (slot s & 1, issued during step
+  // s).  NS = 1: the single slot holds step s + 1, issued during step s.
   issue(I0{});
-  if (nsteps > 1) issue(I1{});
-  store_a(I0{});
+  if constexpr (NS == 2) {
+    if (nsteps > 1) issue(I1{});
+  }
+  store_a(I0{}, I0{});
   int cterm = term_first, cks = 0;  // compute cursor
   set_term(cterm);
+  uint4 bcur[CB];  // NS = 1: sign words of the step being computed
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) bcur[cb] = bw[0][cb];
   auto kstep = [&](int step, auto bufc) {
     constexpr int B = decltype(bufc)::value;
     using Other = std::integral_constant<int, B ^ 1>;
-    uint2 cw[CB];
+    uint32_t cw[CB][4];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) cw[cb] = bw[B][cb];
+    for (int cb = 0; cb < CB; ++cb) {
+      const uint4 wv4 = NS == 2 ? bw[B % NS][cb] : bcur[cb];
+      cw[cb][0] = wv4.x; cw[cb][1] = wv4.y; cw[cb][2] = wv4.z; cw[cb][3] = wv4.w;
+    }
     __syncthreads();
-    if (step + 2 < nsteps) issue(bufc);
+    if constexpr (NS == 2) {
+      if (step + 2 < nsteps) issue(bufc);
+    } else {
+      if (step + 1 < nsteps) issue(I0{});
+    }
     const _Float16* at = As[B];
 #pragma unroll
-    for (int wi = 0; wi < 2; ++wi) {
+    for (int wi = 0; wi < 4; ++wi) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         half8 bf[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          bf[cb] = unpack_frag((wi == 0 ? cw[cb].x : cw[cb].y) ^ flip[cb], h, sub, mag[cb]);
+          bf[cb] = unpack_frag(cw[cb][wi] ^ flip[cb], h, sub, mag[cb]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const half8 af = *reinterpret_cast<const half8*>(
@@ -324,7 +354,15 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
         }
       }
     }
-    if (step + 1 < nsteps) store_a(Other{});
+    if (step + 1 < nsteps) {
+      if constexpr (NS == 2) {
+        store_a(Other{}, Other{});
+      } else {
+        store_a(Other{}, I0{});
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) bcur[cb] = bw[0][cb];
+      }
+    }
     if (STAGE == 2 && ++cks == spt) {
       cks = 0;
       if (++cterm < term_end) set_term(cterm);
@@ -392,10 +430,22 @@ hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_
   a.ntt = static_cast<int>(cdiv(a.T, bm));
   a.ntc = static_cast<int>(cdiv(cols, bn));
   const dim3 grid(static_cast<unsigned>(a.ntt * a.ntc), terms_in_grid);
-  if (bm == 128 && bn == 256) gemm_kernel<STAGE, KW4, 128, 256><<<grid, kThreads, 0, s>>>(a);
-  else if (bm == 128) gemm_kernel<STAGE, KW4, 128, 128><<<grid, kThreads, 0, s>>>(a);
-  else gemm_kernel<STAGE, KW4, 64, 128><<<grid, kThreads, 0, s>>>(a);
-  return hipGetLastError();
+  auto go = [&](auto kern, int bm_) -> hipError_t {
+    const size_t lds = 2u * static_cast<size_t>(bm_) * ALD * sizeof(_Float16);
+    static bool attr_set = false;  // per instantiation; idempotent if raced
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    kern<<<grid, kThreads, lds, s>>>(a);
+    return hipGetLastError();
+  };
+  if (bm == 128 && bn == 256) return go(gemm_kernel<STAGE, KW4, 128, 256, 1>, 128);
+  if (bm == 128) return go(gemm_kernel<STAGE, KW4, 128, 128, 2>, 128);
+  return go(gemm_kernel<STAGE, KW4, 64, 128, 2>, 64);
 }
 
 template <int STAGE>

@@ -111,3 +111,15 @@ def test_deterministic_and_scale_invariant():
     c = D.dbf_linear_forward(terms, 300, 500, 200, xs, path=MF)
     torch.cuda.synchronize()
     assert torch.equal(c.cpu(), a * 64.0)
+
+
+@pytest.mark.parametrize("R", [80, 88, 95, 96])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_first_row_block_small_rank(R, seed):
+    # sign rows of 3 words (rank <= 96) with a single K step: every row block
+    # of the tile must come out right (regression for an operand hazard that
+    # corrupted the first 32 rows)
+    layer, x = S.make_custom(40, 300, R, 1, 40, seed=seed)
+    y = to_np(run(layer, x))
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(y, ref)
