@@ -2,8 +2,17 @@
 // w_i = beta_i . B2_i (gamma_i . x), the adapter kept unmerged beside the
 // frozen base (LoRDBA sections 1 and 5).
 //
-// Workgroups [0, n1) run the decode path's stage 1 (dbf_lut.h) for the
-// adapter's B2 and publish w.  Workgroups [n1, n1 + ceil(N / 16)) own 16
+// Small ranks (R <= 64, the adapter sizes LoRDBA works with): every
+// workgroup computes the whole rank-R intermediate w itself on the matrix
+// cores (v_mfma_f32_16x16x32_f16: B2 rows as +-1 fp16 fragments unpacked
+// from the packed words, against fp16 gamma . x for up to 16 tokens) and
+// keeps it in LDS; that is at most 4 MFMAs per 32 input features and
+// workgroup, a small fraction of its W0 stream, and it needs no other
+// workgroup, no workspace and no wait.
+//
+// Larger ranks: workgroups [0, n1) run the decode path's stage 1
+// (dbf_lut.h) for the adapter's B2 and publish w.  Workgroups
+// [n1, n1 + ceil(N / 16)) own 16
 // output rows each: their 8 wavefronts split the input features in eight and
 // stream their share of the 16 bf16 W0 rows straight into
 // v_mfma_f32_16x16x32_bf16 (A = W0 rows as stored, B = up to 16 tokens of
@@ -179,6 +188,242 @@ __global__ void __launch_bounds__(kMainThreads) adapter_fused(lut::Stage1 s1, Ma
   main_role(m, static_cast<int64_t>(blockIdx.x) - n1, reinterpret_cast<float*>(smem));
 }
 
+// ---- small ranks: every workgroup derives w itself ------------------------
+
+constexpr int kSmallTiles = 4;  // 16-rank MFMA tiles, summed over the terms
+constexpr int kGroup = kUnroll * 32;  // features per unrolled group
+
+struct Small {
+  const uint16_t* w0;
+  int64_t ldw;
+  TermPtrs t;
+  int64_t N, M, R, T, ldx;
+  const uint16_t* x;
+  void* y;
+  int y_dtype;
+  int64_t ldy;
+  int64_t kq;  // features per wave, a multiple of kGroup
+  int fast;    // 16-byte W0 / x / B2 and 8-byte gamma loads allowed
+};
+
+// fp16 g as the exact sum hi + lo of two bf16 values: hi keeps the top eight
+// significant bits, lo the last three (so both products with a bf16
+// activation are exact in the fp32 accumulator).
+__device__ __forceinline__ uint32_t split_f16(uint16_t g) {
+  const float f = f16_bits_to_f32(g);
+  const uint32_t h = __float_as_uint(f) & 0xFFFF0000u;
+  const uint32_t l = __float_as_uint(f - __uint_as_float(h));
+  return (h >> 16) | (l & 0xFFFF0000u);  // hi | lo << 16
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// 16 ranks x 16 tokens of (+-gamma) . x for the step whose B operand is bx:
+// the lane's eight B2 bits pick sign masks from the table, which flip the
+// split gamma of its eight features.
+__device__ __forceinline__ floatx4 rank_step(floatx4 acc, uint32_t byte, const uint4& hi,
+                                             const uint4& lo, const uint4& bx,
+                                             const uint32_t* lut) {
+  const uint4 m = *reinterpret_cast<const uint4*>(lut + 4 * byte);
+  const uint4 ah = make_uint4(hi.x ^ m.x, hi.y ^ m.y, hi.z ^ m.z, hi.w ^ m.w);
+  const uint4 alo = make_uint4(lo.x ^ m.x, lo.y ^ m.y, lo.z ^ m.z, lo.w ^ m.w);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah),
+                                                __builtin_bit_cast(bf16x8, bx), acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo),
+                                                 __builtin_bit_cast(bf16x8, bx), acc, 0, 0, 0);
+}
+
+template <int L, int QR>
+constexpr size_t small_lds_bytes() {
+  constexpr size_t gam = size_t(kMainWaves) * L * 2 * kGroup * 2;
+  constexpr size_t red = size_t(kMainWaves) * (L * QR + 1) * 256 * 4;
+  return 4096 + (gam > red ? gam : red) + size_t(L * QR) * 256 * 4;
+}
+
+// Workgroup = 16 output rows.  Each wave streams its share of the features
+// once per 16 tokens and feeds every x fragment to the base MFMA and to the
+// L * QR rank tiles.  LDS: sign-mask table [256][4] | per-wave split gamma
+// [waves][L][hi, lo][kGroup] during the stream, reused afterwards for the
+// per-wave partials [waves][1 + L * QR][16][16] | w [L * QR * 16][16].
+template <int L, int QR>
+__global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
+  constexpr int NQ = L * QR;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
+  uint16_t* gam = reinterpret_cast<uint16_t*>(smem + 4096);
+  float* red = reinterpret_cast<float*>(smem + 4096);
+  float* wfin = reinterpret_cast<float*>(smem + small_lds_bytes<L, QR>() - NQ * 256 * 4);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 15, lq = lane >> 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t arow = n0 + li;
+  const bool arow_ok = arow < p.N;
+  const uint16_t* wrow = p.w0 + (arow_ok ? arow : 0) * p.ldw;
+  const int64_t kbeg = wv * p.kq;
+  const int64_t kend = min(p.M, kbeg + p.kq);
+  const bool vec = p.fast != 0;
+  const int64_t kwM = layout_kw(p.M), kwR = layout_kw(p.R);
+  uint16_t* mygam = gam + wv * L * 2 * kGroup;
+
+  // dword d of entry b flips the low half where bit 2d of b is clear (-1)
+  // and the high half where bit 2d + 1 is clear
+  for (int e = tid; e < 1024; e += kMainThreads) {
+    const uint32_t nb = ~static_cast<uint32_t>(e >> 2);
+    const int d = e & 3;
+    lut[e] = (((nb >> (2 * d)) & 1u) << 15) | (((nb >> (2 * d + 1)) & 1u) << 31);
+  }
+  // owner threads (row oi, token oj) fetch their B1 row and alpha now
+  const bool owner = tid < 256;
+  const int oi = (tid >> 4) & 15, oj = tid & 15;
+  const int64_t on = n0 + oi;
+  uint32_t b1w[L][2];
+  float al[L];
+#pragma unroll
+  for (int term = 0; term < L; ++term) {
+    b1w[term][0] = b1w[term][1] = 0u;
+    al[term] = 0.f;
+    if (owner && on < p.N) {
+      const uint32_t* b1 = p.t.b1[term] + ((on >> 6) * 64 + (on & 63)) * kwR;
+      b1w[term][0] = b1[0];
+      if (kwR > 1) b1w[term][1] = b1[1];
+      al[term] = f16_bits_to_f32(p.t.alpha[term][on]);
+    }
+  }
+  __syncthreads();
+
+  for (int64_t tb0 = 0; tb0 < p.T; tb0 += 16) {
+    const int64_t tok = tb0 + li;
+    const bool tok_ok = tok < p.T;
+    const uint16_t* xrow = p.x + (tok_ok ? tok : 0) * p.ldx;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    floatx4 wacc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) wacc[q] = acc;
+    int64_t k0 = kbeg;
+    if (vec) {
+      for (; k0 + kGroup <= kend; k0 += kGroup) {
+        uint4 a[kUnroll], b[kUnroll], bw[NQ][2];
+        uint2 g4[L];
+#pragma unroll
+        for (int term = 0; term < L; ++term)
+          g4[term] = *reinterpret_cast<const uint2*>(p.t.gamma[term] + k0 + 4 * lane);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          // rank 16 (q % QR) + li, K-blocks k0 / 128 and the next (4 words each)
+          const uint32_t* b2 = p.t.b2[q / QR] + ((k0 >> 7) * 64 + 16 * (q % QR) + li) * 4;
+          bw[q][0] = *reinterpret_cast<const uint4*>(b2);
+          bw[q][1] = *reinterpret_cast<const uint4*>(b2 + 256);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t k = k0 + u * 32 + lq * 8;
+          a[u] = load8(wrow, k, p.M, arow_ok, true);
+          b[u] = load8(xrow, k, p.M, tok_ok, true);
+        }
+        // this group's gamma, split, into the wave's own LDS slice (read
+        // back by other lanes of the same wave only)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int term = 0; term < L; ++term) {
+          const uint32_t s0 = split_f16(g4[term].x & 0xFFFFu), s1 = split_f16(g4[term].x >> 16);
+          const uint32_t s2 = split_f16(g4[term].y & 0xFFFFu), s3 = split_f16(g4[term].y >> 16);
+          *reinterpret_cast<uint2*>(mygam + (term * 2) * kGroup + 4 * lane) =
+              make_uint2((s0 & 0xFFFFu) | (s1 << 16), (s2 & 0xFFFFu) | (s3 << 16));
+          *reinterpret_cast<uint2*>(mygam + (term * 2 + 1) * kGroup + 4 * lane) =
+              make_uint2((s0 >> 16) | (s1 & 0xFFFF0000u), (s2 >> 16) | (s3 & 0xFFFF0000u));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+#pragma unroll
+          for (int term = 0; term < L; ++term) {
+            const uint4 hi = *reinterpret_cast<const uint4*>(mygam + (term * 2) * kGroup + u * 32 + lq * 8);
+            const uint4 lo = *reinterpret_cast<const uint4*>(mygam + (term * 2 + 1) * kGroup + u * 32 + lq * 8);
+#pragma unroll
+            for (int qr = 0; qr < QR; ++qr) {
+              const int q = term * QR + qr;
+              const uint32_t byte = (pick(bw[q][u >> 2], u & 3) >> (8 * lq)) & 0xFFu;
+              wacc[q] = rank_step(wacc[q], byte, hi, lo, b[u], lut);
+            }
+          }
+        }
+      }
+    }
+    for (; k0 < kend; k0 += 32) {
+      const int64_t k = k0 + lq * 8;
+      const bool in = k < kend;
+      const uint4 a = load8(wrow, k, kend, arow_ok && in, vec);
+      const uint4 b = load8(xrow, k, kend, tok_ok && in, vec);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+      const int64_t kb = k0 / (32 * kwM), w = (k0 % (32 * kwM)) / 32;
+#pragma unroll
+      for (int term = 0; term < L; ++term) {
+        uint32_t s[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          s[j] = (in && k + j < kend) ? split_f16(p.t.gamma[term][k + j]) : 0u;
+        const uint4 hi = make_uint4((s[0] & 0xFFFFu) | (s[1] << 16), (s[2] & 0xFFFFu) | (s[3] << 16),
+                                    (s[4] & 0xFFFFu) | (s[5] << 16), (s[6] & 0xFFFFu) | (s[7] << 16));
+        const uint4 lo = make_uint4((s[0] >> 16) | (s[1] & 0xFFFF0000u), (s[2] >> 16) | (s[3] & 0xFFFF0000u),
+                                    (s[4] >> 16) | (s[5] & 0xFFFF0000u), (s[6] >> 16) | (s[7] & 0xFFFF0000u));
+#pragma unroll
+        for (int qr = 0; qr < QR; ++qr) {
+          const int64_t r = 16 * qr + li;
+          const uint32_t word = p.t.b2[term][(kb * 64 + r) * kwM + w];
+          const int q = term * QR + qr;
+          wacc[q] = rank_step(wacc[q], (word >> (8 * lq)) & 0xFFu, hi, lo, b, lut);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with its gamma slice
+    // D[i][j]: row (rank) i = 4 * (lane / 16) + r, token j = lane % 16
+    float* myred = red + wv * (NQ + 1) * 256;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      myred[(4 * lq + r) * 16 + li] = acc[r];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) myred[(1 + q) * 256 + (4 * lq + r) * 16 + li] = wacc[q][r];
+    }
+    __syncthreads();
+    // w = beta . (sum over the waves), as [tile * 16 + rank][token]
+    for (int e = tid; e < NQ * 256; e += kMainThreads) {
+      const int q = e >> 8, i = (e >> 4) & 15;
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < kMainWaves; ++v) s += red[(v * (NQ + 1) + 1 + q) * 256 + (e & 255)];
+      const int64_t r = 16 * (q % QR) + i;
+      wfin[e] = r < p.R ? f16_bits_to_f32(p.t.beta[q / QR][r]) * s : 0.f;
+    }
+    float v = 0.f;
+    if (owner) {
+#pragma unroll
+      for (int q = 0; q < kMainWaves; ++q) v += red[q * (NQ + 1) * 256 + tid];
+    }
+    __syncthreads();
+    const int64_t tt = tb0 + oj;
+    if (owner && on < p.N && tt < p.T) {
+#pragma unroll
+      for (int term = 0; term < L; ++term) {
+        const float* wt = wfin + term * QR * 256 + oj;
+        float z[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < p.R; ++r) {
+          const float wr = wt[r * 16];
+          const uint32_t word = r < 32 ? b1w[term][0] : b1w[term][1];
+          z[r & 3] += ((word >> (r & 31)) & 1u) ? wr : -wr;
+        }
+        v += al[term] * ((z[0] + z[1]) + (z[2] + z[3]));
+      }
+      store_out(p.y, p.y_dtype, tt * p.ldy + on, v, 0);
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
@@ -197,6 +442,32 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
   const size_t main_lds = sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk);
   if (t.n == 0) {
     adapter_base_only<<<dim3(m.nmain), kMainThreads, main_lds, s>>>(m);
+    return hipGetLastError();
+  }
+  const int64_t qr = (R + 15) / 16;
+  if (t.n * qr <= kSmallTiles) {
+    Small sp{};
+    sp.w0 = w0; sp.ldw = ldw; sp.t = t; sp.N = N; sp.M = M; sp.R = R; sp.T = T;
+    sp.ldx = ldx; sp.x = m.x; sp.y = y; sp.y_dtype = y_dtype; sp.ldy = ldy;
+    sp.kq = ((M + kMainWaves - 1) / kMainWaves + kGroup - 1) / kGroup * kGroup;
+    sp.fast = m.vec;
+    for (int i = 0; i < t.n; ++i)
+      if (reinterpret_cast<uintptr_t>(t.b2[i]) % 16 != 0 ||
+          reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0)
+        sp.fast = 0;
+#define DBF_SM(L_, QR_)                                                              \
+  adapter_small<L_, QR_><<<dim3(m.nmain), kMainThreads, small_lds_bytes<L_, QR_>(), s>>>(sp)
+    switch (t.n * 4 + static_cast<int>(qr)) {
+      case 5: DBF_SM(1, 1); break;
+      case 6: DBF_SM(1, 2); break;
+      case 7: DBF_SM(1, 3); break;
+      case 8: DBF_SM(1, 4); break;
+      case 9: DBF_SM(2, 1); break;
+      case 10: DBF_SM(2, 2); break;
+      case 13: DBF_SM(3, 1); break;
+      default: DBF_SM(4, 1); break;
+    }
+#undef DBF_SM
     return hipGetLastError();
   }
   int n1 = 0;

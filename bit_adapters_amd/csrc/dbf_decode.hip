@@ -33,21 +33,25 @@ struct Stage2 {
   int64_t ldy;
   int accumulate;
   int32_t* s2_out;
-  int32_t* s1_out;  // int8 variant: exact S1, written by stage-2 workgroup 0
+  int32_t* s1_out;  // int8 variant: exact S1, written by stage-2 workgroups of row tile 0
   unsigned* ctr;
   unsigned n1, n2;
+  int64_t nrt;      // row tiles of N; workgroup = (token block, row tile)
 };
 
 template <typename A, int TB, int KW, int MODE>
-__device__ __forceinline__ void stage2_role(const Stage2& p, int64_t rt, A* tbl, A* red) {
+__device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tbl, A* red) {
   constexpr int PW = pw_of(TB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t tblk = bid2 / p.nrt;
+  const int64_t rt = bid2 - tblk * p.nrt;
   const int64_t row = rt * 64 + lane;
   uint32_t wd[PW][KW];
   load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
   wait_producers(p.ctr, p.n1);
   bool have_bits = true;
-  for (int64_t tok0 = 0; tok0 < p.T; tok0 += TB) {
+  {
+    const int64_t tok0 = tblk * TB;
     float yacc[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) yacc[i] = 0.f;
@@ -180,7 +184,8 @@ Stage2 make_stage2(const TermPtrs& t, const Stage1& s1, int64_t N, int64_t R, in
   b.ws = s1.ws; b.rs = s1.rs;
   b.ctr = static_cast<unsigned*>(ws);
   b.n1 = static_cast<unsigned>(n1);
-  b.n2 = static_cast<unsigned>(layout_nrt(N));
+  b.nrt = layout_nrt(N);
+  b.n2 = static_cast<unsigned>(b.nrt * s1.ntb);
   return b;
 }
 
@@ -193,21 +198,23 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
   a.nkb = layout_nkb(M);
   a.nrt = layout_nrt(R);
   int64_t per = 0;
-  a.ks = lut::pick_ks(a.nrt, t.n, a.nkb, split ? kStage1Wg : 1, &per);
+  a.ntb = static_cast<int>((T + lut::pick_tb(T) - 1) / lut::pick_tb(T));
+  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Wg : 1, &per);
   a.kb_per_split = per;
   a.ws = static_cast<unsigned char*>(ws) + kDecodeCounterBytes;
   a.rs = ws_rstride(R);
   a.vec4 = (ldx % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 8 == 0) && (M % 4 == 0);
   for (int i = 0; i < t.n; ++i)
     if (t.gamma[i] && reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) a.vec4 = 0;
-  *n1 = static_cast<int>(a.nrt * a.ks * t.n);
+  *n1 = static_cast<int>(a.nrt * a.ks * t.n * a.ntb);
   return a;
 }
 
 size_t decode_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t T) {
   int64_t per = 0;
-  const int ks = std::max(lut::pick_ks(layout_nrt(R), n_terms, layout_nkb(M), kStage1Wg, &per),
-                          lut::pick_ks(layout_nrt(R), n_terms, layout_nkb(M), 1, &per));
+  const int64_t ntb = (T + lut::pick_tb(T) - 1) / lut::pick_tb(T);
+  const int ks = std::max(lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
+                          lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per));
   return kDecodeCounterBytes + static_cast<size_t>(n_terms) * ks * static_cast<size_t>(T) *
                                    static_cast<size_t>(ws_rstride(R)) * 4u;
 }

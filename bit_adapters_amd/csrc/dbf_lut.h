@@ -160,17 +160,21 @@ struct Stage1 {
   int64_t ldx, T, M, R;
   int64_t nkb, kb_per_split, nrt;
   int ks;
+  int ntb;        // token blocks (of TB tokens), one per workgroup
   void* ws;       // partials [L][ks][T][rs]
   int64_t rs;
   int vec4;       // x rows allow 8-byte loads of four activations
 };
 
-// Stage-1 workgroup `bid` in [0, nrt * ks * L): its row tile of B2_term,
-// K-blocks [kb0, kb1) of its split, one or more passes.
+// Stage-1 workgroup `bid` in [0, ntb * L * nrt * ks): its token block, row
+// tile of B2_term and K-blocks [kb0, kb1) of its split (one or more passes).
 template <typename A, int TB, int KW, int MODE>
 __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
   constexpr int PW = pw_of(TB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per_tb = p.t.n * static_cast<int>(p.nrt) * p.ks;
+  const int tblk = bid / per_tb;
+  bid -= tblk * per_tb;
   const int per_term = static_cast<int>(p.nrt) * p.ks;
   const int term = bid / per_term;
   const int rem = bid - term * per_term;
@@ -185,7 +189,8 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
   uint32_t wd[PW][KW];
   load_pass_bits<TB, KW>(bits, rt, p.nkb, kb0, kb1, wd);
   bool have_bits = true;
-  for (int64_t tok0 = 0; tok0 < p.T; tok0 += TB) {
+  {
+    const int64_t tok0 = static_cast<int64_t>(tblk) * TB;
     A acc[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) acc[i] = A(0);

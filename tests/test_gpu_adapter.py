@@ -44,10 +44,18 @@ def test_lordba_config(R, T):
     assert_close(_run(layer, x, n_terms=0), base_ref, what="base only")
 
 
+# Ranks with L * ceil(R / 16) <= 4 take the in-workgroup rank path (every
+# term count and rank-tile count it is built for appears here); larger ones
+# take the published-intermediate path.
 @pytest.mark.parametrize("N,M,R,L,T", [(65, 33, 17, 2, 3), (130, 300, 70, 3, 5),
                                        (1, 1, 1, 1, 1), (200, 1000, 64, 1, 20),
-                                       (50, 520, 16, 1, 16)])
+                                       (50, 520, 16, 1, 16), (96, 1280, 48, 1, 2),
+                                       (300, 777, 32, 1, 5), (64, 2304, 10, 3, 1),
+                                       (128, 4096, 16, 4, 4), (80, 1536, 16, 2, 33),
+                                       (70, 600, 31, 2, 7), (256, 2048, 128, 1, 2),
+                                       (40, 4096, 96, 1, 1)])
 def test_odd_shapes(N, M, R, L, T):
+    print("adapter odd", N, M, R, L, T, flush=True)
     layer, x = S.make_custom(N, M, R, L, T, seed=9, base=True, scale_lo=0.01,
                              scale_hi=0.05)
     o = O.default()
@@ -69,3 +77,25 @@ def test_strided_x_and_bf16_output():
                                  xd[:, :200], y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_close(to_np(y), ref, rel_l2=4e-3)
+
+
+def test_unaligned_activation_rows():
+    # ldx = 605: no 16-byte loads, every feature takes the bounded step
+    layer, x = S.make_custom(48, 600, 40, 1, 3, seed=4, base=True, scale_lo=0.01,
+                             scale_hi=0.05)
+    o = O.default()
+    ref = o.adapter(O.widen_bf16(layer["w0"]), O.terms64(layer), x64(x))
+    xd = torch.zeros((3, 605), dtype=torch.bfloat16, device=DEV)
+    xd[:, :600] = x_dev(x)
+    y = D.lordba_adapter_forward(bf16_dev(layer["w0"]), device_terms(layer), 48, 600, 40,
+                                 xd[:, :600])
+    torch.cuda.synchronize()
+    assert_close(to_np(y), ref)
+
+
+def test_adapter_deterministic():
+    layer = S.make_layer(3, R=64)
+    x = S.make_x(3, 4)
+    a = _run(layer, x)
+    b = _run(layer, x)
+    assert np.array_equal(a, b)
