@@ -2,25 +2,26 @@
 // w_i = beta_i . B2_i (gamma_i . x), the adapter kept unmerged beside the
 // frozen base (LoRDBA sections 1 and 5).
 //
-// Small ranks (R <= 64, the adapter sizes LoRDBA works with): every
-// workgroup computes the whole rank-R intermediate w itself on the matrix
-// cores (v_mfma_f32_16x16x32_f16: B2 rows as +-1 fp16 fragments unpacked
-// from the packed words, against fp16 gamma . x for up to 16 tokens) and
-// keeps it in LDS; that is at most 4 MFMAs per 32 input features and
-// workgroup, a small fraction of its W0 stream, and it needs no other
-// workgroup, no workspace and no wait.
+// A row workgroup owns 16 output rows; its 8 wavefronts split the input
+// features in eight and stream their share of the 16 bf16 W0 rows straight
+// into v_mfma_f32_16x16x32_bf16 (A = W0 rows as stored, B = up to 16 tokens
+// of x), so the base product costs no VALU work.  Token counts above 16 are
+// handled 16 at a time (the base is re-streamed per 16 tokens: this kernel
+// serves decode batches).
 //
-// Larger ranks: workgroups [0, n1) run the decode path's stage 1
-// (dbf_lut.h) for the adapter's B2 and publish w.  Workgroups
-// [n1, n1 + ceil(N / 16)) own 16
-// output rows each: their 8 wavefronts split the input features in eight and
-// stream their share of the 16 bf16 W0 rows straight into
-// v_mfma_f32_16x16x32_bf16 (A = W0 rows as stored, B = up to 16 tokens of
-// x), 8 loads deep, so the base costs no VALU work and keeps HBM busy; only
-// then do they wait for stage 1, which has long finished, stage w in LDS,
-// and add alpha . (B1 w) for their rows before writing y once.  Token counts
-// above 16 are handled 16 at a time (the base is re-streamed per 16 tokens;
-// this kernel is for decode batches).
+// Small adapters (at most 2 terms and L * ceil(R / 16) <= 4; LoRDBA uses one
+// term of rank 16 to 64): each row workgroup also derives the whole
+// intermediate w itself, on the matrix cores, from the x fragments it already
+// holds.  The A operand is +-gamma over 16 ranks: gamma split exactly into two
+// bf16 values, the signs flipped by the packed B2 bits, so every product is
+// exact and the sums are fp32.  That adds at most 8 MFMAs per 32 features to
+// the base's one, needs no other workgroup, no workspace and no wait, and the
+// wavefronts load one group of features ahead of their MFMAs.
+//
+// Larger adapters: workgroups [0, n1) run the decode path's stage 1
+// (dbf_lut.h) for B2 and publish w; the row workgroups stream the base, then
+// wait for stage 1 (long finished by then), stage w in LDS and add
+// alpha . (B1 w) before writing y once.
 #include "dbf_lut.h"
 
 namespace dbf {
@@ -61,6 +62,14 @@ __device__ __forceinline__ uint4 load8(const uint16_t* p, int64_t k, int64_t K,
                     v[4] | (uint32_t(v[5]) << 16), v[6] | (uint32_t(v[7]) << 16));
 }
 
+// 16 bytes at p + k (k + 8 within the row).  Rows past N or T are read as
+// row 0 and not zeroed: an MFMA output element depends on one A row and one
+// B column only, and the outputs of those rows and tokens are never stored.
+// Without a branch the loads stay in flight across the MFMAs.
+__device__ __forceinline__ uint4 load16(const uint16_t* p, int64_t k) {
+  return *reinterpret_cast<const uint4*>(p + k);
+}
+
 constexpr int kMainWaves = lut::kWaves;
 constexpr int kMainThreads = lut::kThreads;
 
@@ -90,8 +99,8 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t k = k0 + u * 32 + lq * 8;
-        a[u] = load8(wrow, k, p.M, arow_ok, vec);
-        b[u] = load8(xrow, k, p.M, tok_ok, vec);
+        a[u] = vec ? load16(wrow, k) : load8(wrow, k, p.M, arow_ok, false);
+        b[u] = vec ? load16(xrow, k) : load8(xrow, k, p.M, tok_ok, false);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
@@ -170,11 +179,6 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
   if (waited) lut::consumer_done(p.ctr, p.nmain);
 }
 
-__global__ void __launch_bounds__(kMainThreads) adapter_base_only(Main m) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  main_role(m, blockIdx.x, reinterpret_cast<float*>(smem));
-}
-
 template <int TB, int KW>
 __global__ void __launch_bounds__(kMainThreads) adapter_fused(lut::Stage1 s1, Main m, int n1) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -191,7 +195,9 @@ __global__ void __launch_bounds__(kMainThreads) adapter_fused(lut::Stage1 s1, Ma
 // ---- small ranks: every workgroup derives w itself ------------------------
 
 constexpr int kSmallTiles = 4;  // 16-rank MFMA tiles, summed over the terms
-constexpr int kGroup = kUnroll * 32;  // features per unrolled group
+constexpr int kSmallTerms = 2;  // more terms run out of registers
+constexpr int kSteps = 4;       // 32-feature MFMA steps per group
+constexpr int kGroup = kSteps * 32;  // one K-block of packed bits (kw = 4)
 
 struct Small {
   const uint16_t* w0;
@@ -203,21 +209,17 @@ struct Small {
   int y_dtype;
   int64_t ldy;
   int64_t kq;  // features per wave, a multiple of kGroup
-  int fast;    // 16-byte W0 / x / B2 and 8-byte gamma loads allowed
+  int fast;    // 16-byte W0 / x / B2 and 4-byte gamma loads allowed
 };
 
 // fp16 g as the exact sum hi + lo of two bf16 values: hi keeps the top eight
 // significant bits, lo the last three (so both products with a bf16
-// activation are exact in the fp32 accumulator).
+// activation are exact in the fp32 accumulator).  Returns hi | lo << 16.
 __device__ __forceinline__ uint32_t split_f16(uint16_t g) {
   const float f = f16_bits_to_f32(g);
   const uint32_t h = __float_as_uint(f) & 0xFFFF0000u;
   const uint32_t l = __float_as_uint(f - __uint_as_float(h));
-  return (h >> 16) | (l & 0xFFFF0000u);  // hi | lo << 16
-}
-
-__device__ __forceinline__ uint32_t pick(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+  return (h >> 16) | (l & 0xFFFF0000u);
 }
 
 // 16 ranks x 16 tokens of (+-gamma) . x for the step whose B operand is bx:
@@ -242,11 +244,80 @@ constexpr size_t small_lds_bytes() {
   return 4096 + (gam > red ? gam : red) + size_t(L * QR) * 256 * 4;
 }
 
+// Operands of one group (kSteps steps) of one wave, loaded one group ahead.
+// Within a group, lane quarter lq takes features [32 lq, 32 lq + 32): step u
+// gives it features 32 lq + 8 u .. + 8 (the MFMA sums over whichever features
+// each lane holds, as long as A and B agree), so its B2 bits for the whole
+// group are one word: byte u of word lq of the rank's 128-feature K-block.
+template <int L, int QR>
+struct Group {
+  static constexpr int NQ = L * QR > 0 ? L * QR : 1;
+  static constexpr int NL = L > 0 ? L : 1;
+  uint4 a[kSteps], b[kSteps];  // W0 rows / x tokens, 8 features per lane
+  uint32_t bw[NQ];             // B2 word lq of the lane's rank
+  uint32_t g[NL];              // gamma of features 2 * lane, 2 * lane + 1
+};
+
+template <int L, int QR>
+__device__ __forceinline__ void load_group(Group<L, QR>& G, const Small& p, int64_t k0,
+                                           const uint16_t* wrow, const uint16_t* xrow,
+                                           int lane, int li, int lq) {
+#pragma unroll
+  for (int term = 0; term < L; ++term)
+    G.g[term] = *reinterpret_cast<const uint32_t*>(p.t.gamma[term] + k0 + 2 * lane);
+#pragma unroll
+  for (int q = 0; q < L * QR; ++q)
+    G.bw[q] = p.t.b2[q / QR][((k0 >> 7) * 64 + 16 * (q % QR) + li) * 4 + lq];
+#pragma unroll
+  for (int u = 0; u < kSteps; ++u) {
+    const int64_t k = k0 + lq * 32 + u * 8;
+    G.a[u] = load16(wrow, k);
+    G.b[u] = load16(xrow, k);
+  }
+}
+
+template <int L, int QR>
+__device__ __forceinline__ void compute_group(const Group<L, QR>& G, floatx4& acc,
+                                              floatx4* wacc, uint16_t* mygam,
+                                              const uint32_t* lut, int lane, int lq) {
+  // the group's gamma, split, into the wave's own LDS slice (read back by
+  // other lanes of the same wave only; the fences keep the order)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int term = 0; term < L; ++term) {
+    const uint32_t s0 = split_f16(G.g[term] & 0xFFFFu), s1 = split_f16(G.g[term] >> 16);
+    reinterpret_cast<uint32_t*>(mygam + (term * 2) * kGroup)[lane] = (s0 & 0xFFFFu) | (s1 << 16);
+    reinterpret_cast<uint32_t*>(mygam + (term * 2 + 1) * kGroup)[lane] =
+        (s0 >> 16) | (s1 & 0xFFFF0000u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int u = 0; u < kSteps; ++u) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8, G.a[u]), __builtin_bit_cast(bf16x8, G.b[u]), acc, 0, 0, 0);
+#pragma unroll
+    for (int term = 0; term < L; ++term) {
+      const uint4 hi = *reinterpret_cast<const uint4*>(mygam + (term * 2) * kGroup + lq * 32 + u * 8);
+      const uint4 lo =
+          *reinterpret_cast<const uint4*>(mygam + (term * 2 + 1) * kGroup + lq * 32 + u * 8);
+#pragma unroll
+      for (int qr = 0; qr < QR; ++qr) {
+        const int q = term * QR + qr;
+        wacc[q] = rank_step(wacc[q], (G.bw[q] >> (8 * u)) & 0xFFu, hi, lo, G.b[u], lut);
+      }
+    }
+    // keep the scheduler from hoisting every step's LDS reads (registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Workgroup = 16 output rows.  Each wave streams its share of the features
-// once per 16 tokens and feeds every x fragment to the base MFMA and to the
-// L * QR rank tiles.  LDS: sign-mask table [256][4] | per-wave split gamma
-// [waves][L][hi, lo][kGroup] during the stream, reused afterwards for the
-// per-wave partials [waves][1 + L * QR][16][16] | w [L * QR * 16][16].
+// once per 16 tokens, one group ahead of its MFMAs, and feeds every x
+// fragment to the base product and to the L * QR rank tiles.  LDS:
+// sign-mask table [256][4] | per-wave split gamma [waves][L][hi, lo][kGroup]
+// during the stream, reused afterwards for the per-wave partials
+// [waves][1 + L * QR][16][16] | w [L * QR * 16][16].  L = 0 is the bare
+// base product.
 template <int L, int QR>
 __global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
   constexpr int NQ = L * QR;
@@ -266,20 +337,24 @@ __global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
   const bool vec = p.fast != 0;
   const int64_t kwM = layout_kw(p.M), kwR = layout_kw(p.R);
   uint16_t* mygam = gam + wv * L * 2 * kGroup;
+  // whole groups of this wave (the bounded steps take the rest)
+  const int64_t ngroups = (vec && kend > kbeg) ? (kend - kbeg) / kGroup : 0;
 
-  // dword d of entry b flips the low half where bit 2d of b is clear (-1)
-  // and the high half where bit 2d + 1 is clear
-  for (int e = tid; e < 1024; e += kMainThreads) {
-    const uint32_t nb = ~static_cast<uint32_t>(e >> 2);
-    const int d = e & 3;
-    lut[e] = (((nb >> (2 * d)) & 1u) << 15) | (((nb >> (2 * d + 1)) & 1u) << 31);
+  if (L > 0) {
+    // dword d of entry b flips the low half where bit 2d of b is clear (-1)
+    // and the high half where bit 2d + 1 is clear
+    for (int e = tid; e < 1024; e += kMainThreads) {
+      const uint32_t nb = ~static_cast<uint32_t>(e >> 2);
+      const int d = e & 3;
+      lut[e] = (((nb >> (2 * d)) & 1u) << 15) | (((nb >> (2 * d + 1)) & 1u) << 31);
+    }
   }
   // owner threads (row oi, token oj) fetch their B1 row and alpha now
   const bool owner = tid < 256;
   const int oi = (tid >> 4) & 15, oj = tid & 15;
   const int64_t on = n0 + oi;
-  uint32_t b1w[L][2];
-  float al[L];
+  uint32_t b1w[Group<L, QR>::NL][2];
+  float al[Group<L, QR>::NL];
 #pragma unroll
   for (int term = 0; term < L; ++term) {
     b1w[term][0] = b1w[term][1] = 0u;
@@ -298,62 +373,23 @@ __global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
     const bool tok_ok = tok < p.T;
     const uint16_t* xrow = p.x + (tok_ok ? tok : 0) * p.ldx;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    floatx4 wacc[NQ];
+    floatx4 wacc[Group<L, QR>::NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) wacc[q] = acc;
-    int64_t k0 = kbeg;
-    if (vec) {
-      for (; k0 + kGroup <= kend; k0 += kGroup) {
-        uint4 a[kUnroll], b[kUnroll], bw[NQ][2];
-        uint2 g4[L];
-#pragma unroll
-        for (int term = 0; term < L; ++term)
-          g4[term] = *reinterpret_cast<const uint2*>(p.t.gamma[term] + k0 + 4 * lane);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          // rank 16 (q % QR) + li, K-blocks k0 / 128 and the next (4 words each)
-          const uint32_t* b2 = p.t.b2[q / QR] + ((k0 >> 7) * 64 + 16 * (q % QR) + li) * 4;
-          bw[q][0] = *reinterpret_cast<const uint4*>(b2);
-          bw[q][1] = *reinterpret_cast<const uint4*>(b2 + 256);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int64_t k = k0 + u * 32 + lq * 8;
-          a[u] = load8(wrow, k, p.M, arow_ok, true);
-          b[u] = load8(xrow, k, p.M, tok_ok, true);
-        }
-        // this group's gamma, split, into the wave's own LDS slice (read
-        // back by other lanes of the same wave only)
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-        for (int term = 0; term < L; ++term) {
-          const uint32_t s0 = split_f16(g4[term].x & 0xFFFFu), s1 = split_f16(g4[term].x >> 16);
-          const uint32_t s2 = split_f16(g4[term].y & 0xFFFFu), s3 = split_f16(g4[term].y >> 16);
-          *reinterpret_cast<uint2*>(mygam + (term * 2) * kGroup + 4 * lane) =
-              make_uint2((s0 & 0xFFFFu) | (s1 << 16), (s2 & 0xFFFFu) | (s3 << 16));
-          *reinterpret_cast<uint2*>(mygam + (term * 2 + 1) * kGroup + 4 * lane) =
-              make_uint2((s0 >> 16) | (s1 & 0xFFFF0000u), (s2 >> 16) | (s3 & 0xFFFF0000u));
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
-#pragma unroll
-          for (int term = 0; term < L; ++term) {
-            const uint4 hi = *reinterpret_cast<const uint4*>(mygam + (term * 2) * kGroup + u * 32 + lq * 8);
-            const uint4 lo = *reinterpret_cast<const uint4*>(mygam + (term * 2 + 1) * kGroup + u * 32 + lq * 8);
-#pragma unroll
-            for (int qr = 0; qr < QR; ++qr) {
-              const int q = term * QR + qr;
-              const uint32_t byte = (pick(bw[q][u >> 2], u & 3) >> (8 * lq)) & 0xFFu;
-              wacc[q] = rank_step(wacc[q], byte, hi, lo, b[u], lut);
-            }
-          }
-        }
+    for (int q = 0; q < Group<L, QR>::NQ; ++q) wacc[q] = acc;
+    {
+      Group<L, QR> G0, G1;
+      if (ngroups > 0) load_group(G0, p, kbeg, wrow, xrow, lane, li, lq);
+      for (int64_t g = 0; g < ngroups; g += 2) {
+        if (g + 1 < ngroups)
+          load_group(G1, p, kbeg + (g + 1) * kGroup, wrow, xrow, lane, li, lq);
+        compute_group(G0, acc, wacc, mygam, lut, lane, lq);
+        if (g + 1 >= ngroups) break;
+        if (g + 2 < ngroups)
+          load_group(G0, p, kbeg + (g + 2) * kGroup, wrow, xrow, lane, li, lq);
+        compute_group(G1, acc, wacc, mygam, lut, lane, lq);
       }
     }
-    for (; k0 < kend; k0 += 32) {
+    for (int64_t k0 = kbeg + ngroups * kGroup; k0 < kend; k0 += 32) {
       const int64_t k = k0 + lq * 8;
       const bool in = k < kend;
       const uint4 a = load8(wrow, k, kend, arow_ok && in, vec);
@@ -439,13 +475,8 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
           (reinterpret_cast<uintptr_t>(w0) % 16 == 0) &&
           (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   m.nmain = static_cast<unsigned>((N + 15) / 16);
-  const size_t main_lds = sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk);
-  if (t.n == 0) {
-    adapter_base_only<<<dim3(m.nmain), kMainThreads, main_lds, s>>>(m);
-    return hipGetLastError();
-  }
-  const int64_t qr = (R + 15) / 16;
-  if (t.n * qr <= kSmallTiles) {
+  const int64_t qr = t.n > 0 ? (R + 15) / 16 : 0;
+  if (t.n <= kSmallTerms && t.n * qr <= kSmallTiles) {
     Small sp{};
     sp.w0 = w0; sp.ldw = ldw; sp.t = t; sp.N = N; sp.M = M; sp.R = R; sp.T = T;
     sp.ldx = ldx; sp.x = m.x; sp.y = y; sp.y_dtype = y_dtype; sp.ldy = ldy;
@@ -453,23 +484,23 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
     sp.fast = m.vec;
     for (int i = 0; i < t.n; ++i)
       if (reinterpret_cast<uintptr_t>(t.b2[i]) % 16 != 0 ||
-          reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0)
+          reinterpret_cast<uintptr_t>(t.gamma[i]) % 4 != 0)
         sp.fast = 0;
 #define DBF_SM(L_, QR_)                                                              \
   adapter_small<L_, QR_><<<dim3(m.nmain), kMainThreads, small_lds_bytes<L_, QR_>(), s>>>(sp)
     switch (t.n * 4 + static_cast<int>(qr)) {
+      case 0: DBF_SM(0, 1); break;
       case 5: DBF_SM(1, 1); break;
       case 6: DBF_SM(1, 2); break;
       case 7: DBF_SM(1, 3); break;
       case 8: DBF_SM(1, 4); break;
       case 9: DBF_SM(2, 1); break;
-      case 10: DBF_SM(2, 2); break;
-      case 13: DBF_SM(3, 1); break;
-      default: DBF_SM(4, 1); break;
+      default: DBF_SM(2, 2); break;
     }
 #undef DBF_SM
     return hipGetLastError();
   }
+  const size_t main_lds = sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk);
   int n1 = 0;
   const lut::Stage1 a = make_stage1(t, M, R, x, DBF_BF16, T, ldx, ws, true, &n1);
   m.ws = static_cast<const float*>(a.ws);
