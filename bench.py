@@ -58,6 +58,19 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
+def dev_x(x_np):
+    """Activations on the device: bf16 (stored as uint16 bits) or fp16."""
+    if x_np.dtype == np.float16:
+        return dev_f16(x_np)
+    return dev_bf16(x_np)
+
+
+def widen_x(x_np):
+    """Activations as the oracle sees them (fp64, exact widening)."""
+    import oracle as O
+    return x_np.astype(np.float64) if x_np.dtype == np.float16 else O.widen_bf16(x_np)
+
+
 def algorithmic(cfg, N, M, R, L, T, base):
     """Bytes the method must move per forward (packed signs at one bit each,
     fp16 scales, bf16 x and y, bf16 W0 if any) and its flops."""
@@ -97,7 +110,7 @@ def main():
     layer = S.make_layer(args.config, R=args.rank if base else None)
     N, M, R, L = layer["N"], layer["M"], layer["R"], len(layer["terms"])
     x_np = S.make_x(args.config, T)
-    x = dev_bf16(x_np)
+    x = dev_x(x_np)
 
     # one packed copy, then clones for rotation
     terms0 = []
@@ -241,7 +254,7 @@ def verify(layer, x_np, x, y, copy, base, N, M, R, T, args, step_index, ws):
     torch.cuda.synchronize()
     same = bool(torch.equal(yg, ye))
     toks = list(range(min(T, 4)))
-    xs = O.widen_bf16(x_np[toks])
+    xs = widen_x(x_np[toks])
     ref = O.default().forward(O.terms64(layer), xs)
     if base:
         ref = ref + O.default().dense(O.widen_bf16(layer["w0"]), xs)
@@ -265,7 +278,7 @@ def cpu_baseline(layer, config, T, base, budget_s=12.0):
 
     o = O.default()
     terms = O.terms64(layer)
-    xs = O.widen_bf16(S.make_x(config, max(S.CONFIGS[config]["T"])))
+    xs = widen_x(S.make_x(config, max(S.CONFIGS[config]["T"])))
     w0 = O.widen_bf16(layer["w0"]) if base else None
     done, t0 = 0, time.perf_counter()
     while True:

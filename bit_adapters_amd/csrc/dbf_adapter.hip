@@ -47,8 +47,8 @@ struct Main {
   int64_t rs;
   int64_t kq;  // features per wave (multiple of 32)
   int vec;     // 16-byte loads allowed
-  unsigned* ctr;
-  unsigned n1, nmain;
+  lut::Sync sync;  // n_prod = stage-1 workgroups, n_cons = row workgroups
+  unsigned nmain;
 };
 
 __device__ __forceinline__ uint4 load8(const uint16_t* p, int64_t k, int64_t K,
@@ -87,6 +87,7 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
   const int64_t kend = min(p.M, kbeg + p.kq);
   const bool vec = p.vec != 0;
   bool waited = false;
+  unsigned ticket = 0;
 
   for (int64_t tb0 = 0; tb0 < p.T; tb0 += 16) {
     const int64_t tok = tb0 + li;
@@ -129,7 +130,7 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
 
     if (p.t.n > 0) {
       if (!waited) {
-        lut::wait_producers(p.ctr, p.n1);
+        ticket = lut::wait_producers(p.sync);
         waited = true;
       }
       const int64_t kw = layout_kw(p.R), nkb = layout_nkb(p.R);
@@ -176,7 +177,7 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
     if (owner && n < p.N && tt < p.T) store_out(p.y, p.y_dtype, tt * p.ldy + n, v, 0);
     __syncthreads();
   }
-  if (waited) lut::consumer_done(p.ctr, p.nmain);
+  if (waited) lut::consumer_done(p.sync, ticket);
 }
 
 template <int TB, int KW>
@@ -186,7 +187,7 @@ __global__ void __launch_bounds__(kMainThreads) adapter_fused(lut::Stage1 s1, Ma
     float* tbl = reinterpret_cast<float*>(smem);
     float* red = tbl + lut::tbl_elems<TB, KW>();
     lut::stage1_role<float, TB, KW, lut::MODE_F>(s1, blockIdx.x, tbl, red);
-    lut::publish(m.ctr);
+    lut::publish(m.sync, blockIdx.x);
     return;
   }
   main_role(m, static_cast<int64_t>(blockIdx.x) - n1, reinterpret_cast<float*>(smem));
@@ -506,8 +507,7 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
   m.ws = static_cast<const float*>(a.ws);
   m.ks = a.ks;
   m.rs = a.rs;
-  m.ctr = static_cast<unsigned*>(ws);
-  m.n1 = static_cast<unsigned>(n1);
+  m.sync = lut::make_sync(ws, n1, m.nmain);
   const int tb = lut::pick_tb(T), kw = static_cast<int>(layout_kw(M));
   const dim3 grid(static_cast<unsigned>(n1) + m.nmain);
 #define DBF_AD(TB_, KW_)                                                                 \

@@ -34,8 +34,8 @@ struct Stage2 {
   int accumulate;
   int32_t* s2_out;
   int32_t* s1_out;  // int8 variant: exact S1, written by stage-2 workgroups of row tile 0
-  unsigned* ctr;
-  unsigned n1, n2;
+  Sync sync;        // n_prod = stage-1 workgroups, n_cons = stage-2 workgroups
+  unsigned n2;
   int64_t nrt;      // row tiles of N; workgroup = (token block, row tile)
 };
 
@@ -48,7 +48,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   const int64_t row = rt * 64 + lane;
   uint32_t wd[PW][KW];
   load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
-  wait_producers(p.ctr, p.n1);
+  const unsigned ticket = wait_producers(p.sync);
   bool have_bits = true;
   {
     const int64_t tok0 = tblk * TB;
@@ -123,7 +123,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
       }
     }
   }
-  consumer_done(p.ctr, p.n2);
+  consumer_done(p.sync, ticket);
 }
 
 template <typename A, int TB, int KW1, int KW2, int MODE>
@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, 
   const int bid = blockIdx.x;
   if (bid < n1) {
     stage1_role<A, TB, KW1, MODE>(s1, bid, tbl, red);
-    if (run_stage2) publish(s2.ctr);
+    if (run_stage2) publish(s2.sync, static_cast<unsigned>(bid));
     return;
   }
   stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
@@ -182,10 +182,9 @@ Stage2 make_stage2(const TermPtrs& t, const Stage1& s1, int64_t N, int64_t R, in
   Stage2 b{};
   b.t = t; b.T = T; b.N = N; b.R = R; b.nkb = layout_nkb(R); b.ks = s1.ks;
   b.ws = s1.ws; b.rs = s1.rs;
-  b.ctr = static_cast<unsigned*>(ws);
-  b.n1 = static_cast<unsigned>(n1);
   b.nrt = layout_nrt(N);
   b.n2 = static_cast<unsigned>(b.nrt * s1.ntb);
+  b.sync = make_sync(ws, n1, b.n2);
   return b;
 }
 
@@ -201,12 +200,12 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
   a.ntb = static_cast<int>((T + lut::pick_tb(T) - 1) / lut::pick_tb(T));
   a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Wg : 1, &per);
   a.kb_per_split = per;
-  a.ws = static_cast<unsigned char*>(ws) + kDecodeCounterBytes;
   a.rs = ws_rstride(R);
   a.vec4 = (ldx % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 8 == 0) && (M % 4 == 0);
   for (int i = 0; i < t.n; ++i)
     if (t.gamma[i] && reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) a.vec4 = 0;
   *n1 = static_cast<int>(a.nrt * a.ks * t.n * a.ntb);
+  a.ws = static_cast<unsigned char*>(ws) + kWsHeadBytes;
   return a;
 }
 
@@ -215,7 +214,7 @@ size_t decode_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t
   const int64_t ntb = (T + lut::pick_tb(T) - 1) / lut::pick_tb(T);
   const int ks = std::max(lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
                           lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per));
-  return kDecodeCounterBytes + static_cast<size_t>(n_terms) * ks * static_cast<size_t>(T) *
+  return kWsHeadBytes + static_cast<size_t>(n_terms) * ks * static_cast<size_t>(T) *
                                    static_cast<size_t>(ws_rstride(R)) * 4u;
 }
 

@@ -115,9 +115,13 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
                           int64_t T, int64_t ldx, void* y, int y_dtype,
                           int64_t ldy, void* ws, hipStream_t s);
 
-// The decode path keeps its stage-1 -> stage-2 counters in the first bytes
-// of the workspace (zero before first use, zero after every call).
-constexpr size_t kDecodeCounterBytes = 256;
+// The head of every workspace carries the decode path's stage-1 -> stage-2
+// handoff: 256 bytes of counters, then kSyncWords 4-byte producer words.
+// It is zero before first use and every call leaves it zero; no path keeps
+// scratch there.
+constexpr size_t kSyncWords = 4096;
+constexpr size_t kWsHeadBytes = 256 + 4 * kSyncWords;
+static_assert(kWsHeadBytes == DBF_WS_HEAD_BYTES, "workspace head size");
 
 // Row stride (floats) of the rank-R intermediate in the workspace.
 inline int64_t ws_rstride(int64_t R) { return (R + 63) / 64 * 64; }

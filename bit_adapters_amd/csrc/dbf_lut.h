@@ -44,6 +44,13 @@ __host__ __device__ constexpr size_t lds_bytes() {
   return sizeof(A) * (tbl_elems<TB, KW>() + red_elems<TB>());
 }
 
+// A result another workgroup of the launch will read: written through to
+// memory (system-scope store), so the producer needs no L2 writeback.
+template <typename V>
+__device__ __forceinline__ void store_shared(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 template <typename A>
 __device__ __forceinline__ void build_signed16(A a0, A a1, A a2, A a3, A* e) {
   const A p0 = -a0 - a1, p1 = a0 - a1, p2 = a1 - a0, p3 = a0 + a1;
@@ -240,53 +247,96 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
         if (tt < p.T) {
           const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
           if constexpr (MODE == MODE_F)
-            static_cast<float*>(p.ws)[o] = f16_bits_to_f32(p.t.beta[term][row]) * acc[tok];
+            store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(p.t.beta[term][row]) * acc[tok]);
           else
-            static_cast<int32_t*>(p.ws)[o] = acc[tok];
+            store_shared(static_cast<int32_t*>(p.ws) + o, static_cast<int32_t>(acc[tok]));
         }
       }
     }
   }
 }
 
-// ---- completion counters between the two roles of a launch --------------
-// ctr[0]: producer workgroups done; ctr[1]: consumers past the wait;
-// ctr[2]: set if a wait gave up.
+// ---- handoff between the two roles of a launch ---------------------------
+// Producer p owns word p % kSyncWords of the workspace head (one producer
+// per word up to kSyncWords producers).  Its results are written through to
+// memory (system-scope stores, see store_shared) and, once they are
+// complete, it adds one to its word, also at system scope: no L2 writeback
+// of the whole cache is needed on the producer's side.  Consumers poll the
+// words with loads that bypass the caches, then invalidate their caches
+// (agent-scope acquire) before reading the results.  Counters: ctr[0]
+// consumers past their wait, ctr[2] set if a wait gave up.
+struct Sync {
+  unsigned* ctr;
+  unsigned* words;
+  unsigned n_prod, n_cons;
+};
 
-// Producer: after its results are stored, one release and one increment.
-__device__ __forceinline__ void publish(unsigned* ctr) {
-  __syncthreads();  // every wave's stores are issued and complete in L2
+inline Sync make_sync(void* ws, int64_t n_prod, int64_t n_cons) {
+  Sync s;
+  s.ctr = static_cast<unsigned*>(ws);
+  s.words = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + 256);
+  s.n_prod = static_cast<unsigned>(n_prod);
+  s.n_cons = static_cast<unsigned>(n_cons);
+  return s;
+}
+
+// Producer `pid`, called by all threads after its store_shared results:
+// the storing wave (wave 0) waits for their completion, then adds its word.
+__device__ __forceinline__ void publish(const Sync& s, unsigned pid) {
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+    __hip_atomic_fetch_add(s.words + pid % kSyncWords, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
-// Consumer: wait until n_prod producers have published, then acquire.
-__device__ __forceinline__ void wait_producers(unsigned* ctr, unsigned n_prod) {
-  if (threadIdx.x == 0) {
+// Consumer: the lanes of wave 0 poll the producer words until each holds
+// its count, then acquire; the workgroup barrier orders the other waves
+// after it.  Thread 0 then takes a ticket (the consumers' arrival order) at
+// once; its value is only needed by consumer_done at the end.
+__device__ __forceinline__ unsigned wait_producers(const Sync& s) {
+  unsigned ticket = 0;
+  if (threadIdx.x < 64) {
+    const unsigned lane = threadIdx.x;
+    const unsigned nw = s.n_prod < kSyncWords ? s.n_prod : static_cast<unsigned>(kSyncWords);
+    const unsigned base = s.n_prod / static_cast<unsigned>(kSyncWords);
+    const unsigned extra = s.n_prod % static_cast<unsigned>(kSyncWords);
     unsigned spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_prod) {
+    while (true) {
+      bool ok = true;
+      for (unsigned w = lane; w < nw; w += 64) {
+        const unsigned want = base + (w < extra ? 1u : 0u);
+        ok &= __hip_atomic_load(s.words + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= want;
+      }
+      if (__all(ok)) break;
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
-        __hip_atomic_fetch_or(ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0)
+          __hip_atomic_fetch_or(s.ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         break;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (lane == 0)
+      ticket = __hip_atomic_fetch_add(s.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   __syncthreads();
+  return ticket;
 }
 
-// Consumer, once its wait is over (called at its end, off the critical
-// path): the last of n_cons consumers resets the counters for the next call.
-__device__ __forceinline__ void consumer_done(unsigned* ctr, unsigned n_cons) {
-  if (threadIdx.x == 0) {
-    if (__hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        n_cons - 1u) {
-      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+// Consumer, at its end, with the ticket of its wait: the last consumer to
+// pass its wait (every producer has published and every consumer has
+// waited by then) clears the producer words and the counter for the next
+// call.
+__device__ __forceinline__ void consumer_done(const Sync& s, unsigned ticket) {
+  __shared__ unsigned last;
+  if (threadIdx.x == 0) last = ticket == s.n_cons - 1u;
+  __syncthreads();
+  if (last) {
+    const unsigned nw = s.n_prod < kSyncWords ? s.n_prod : static_cast<unsigned>(kSyncWords);
+    for (unsigned w = threadIdx.x; w < nw; w += blockDim.x)
+      __hip_atomic_store(s.words + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (threadIdx.x == 0) __hip_atomic_store(s.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 

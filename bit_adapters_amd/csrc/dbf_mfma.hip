@@ -461,7 +461,7 @@ struct WsLayout {
 WsLayout ws_layout(int64_t M, int64_t R, int L, int64_t T) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   WsLayout w{};
-  size_t off = kDecodeCounterBytes;
+  size_t off = kWsHeadBytes;
   w.u = off; off += al(static_cast<size_t>(L) * T * kpad(M) * 2);
   w.v = off; off += al(static_cast<size_t>(L) * T * kpad(R) * 2);
   w.l1 = off; off += al(static_cast<size_t>(L) * T * 4);

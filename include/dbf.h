@@ -130,12 +130,15 @@ typedef struct dbf_term {
 /* Bytes of device workspace dbf_linear_forward / dbf_linear_forward_i8 /
  * lordba_adapter_forward need for these sizes and path (the rank-R
  * intermediate of every term, and per-token scale slots for the MFMA
- * path).  The caller allocates it, 16-byte aligned.  Its first 256 bytes
- * hold the decode path's completion counters: they must be zero before the
- * first call that uses the buffer (e.g. allocate it zeroed), and every call
- * leaves them zero again.  The rest is scratch, clobbered by every call.
+ * path).  The caller allocates it, 16-byte aligned.  Its first
+ * DBF_WS_HEAD_BYTES bytes hold the decode path's handoff counters between
+ * the workgroups of one launch: they must be zero before the first call
+ * that uses the buffer (e.g. allocate it zeroed), every call leaves them
+ * zero again, and no path keeps scratch there, so one buffer may serve calls
+ * of every path in turn.  The rest is scratch, clobbered by every call.
  * Calls that run at the same time (on different streams) need separate
  * workspaces. */
+#define DBF_WS_HEAD_BYTES 16640
 size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
                            int64_t T, int path);
 
