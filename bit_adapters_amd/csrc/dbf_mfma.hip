@@ -44,7 +44,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 128;      // features per K step (one K-block of the bit layout)
 constexpr int kThreads = 256;
-constexpr int ALD = BK + 8;  // halves per LDS row of the A tile
+constexpr int kStages = 2;   // LDS stages of the K-step pipeline
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t kpad(int64_t K) { return (K + BK - 1) / BK * BK; }
@@ -69,7 +69,7 @@ struct PrepArgs {
   _Float16* u;  // [L][T][mpad]
   float* l1;    // [L][T]
   float* bmax;  // [L]
-  int vec;      // 8-byte loads of x and gamma allowed
+  int vec;      // 16-byte loads of x and gamma allowed
 };
 
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
@@ -83,46 +83,46 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
     const int64_t tok = blk - static_cast<int64_t>(term) * p.T;
     const uint16_t* g = p.gamma[term];
     _Float16* out = p.u + blk * p.mpad;
-    // one 16-byte chunk (8 halves) per thread and iteration: positions
-    // [8 c, 8 c + 8) of the row = pairs j0..j0+3 of a 32-group
     const uint16_t* xr = static_cast<const uint16_t*>(p.x) + tok * p.ldx;
-    for (int64_t c = tid; c < p.mpad / 8; c += 256) {
-      const int64_t grp = c >> 2, q4 = c & 3;
-      const int64_t k0 = grp * 32 + 4 * q4;
-      float lo[4], hi[4];
-      if (p.vec && k0 + 20 <= p.M) {
-        const uint2 xl = *reinterpret_cast<const uint2*>(xr + k0);
-        const uint2 xh = *reinterpret_cast<const uint2*>(xr + k0 + 16);
-        const uint2 gl = *reinterpret_cast<const uint2*>(g + k0);
-        const uint2 gh = *reinterpret_cast<const uint2*>(g + k0 + 16);
-        const uint32_t xv[4] = {xl.x, xl.y, xh.x, xh.y}, gv[4] = {gl.x, gl.y, gh.x, gh.y};
+    // one 32-feature group per thread and iteration: features k0 .. k0 + 31
+    // in, positions 2 j (feature k0 + j) and 2 j + 1 (k0 + 16 + j) out
+    for (int64_t grp = tid; grp < p.mpad / 32; grp += 256) {
+      const int64_t k0 = grp * 32;
+      float a[32];
+      if (p.vec && k0 + 32 <= p.M) {
+        uint32_t xw[16], gw[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int wi = j >> 1, sh = (j & 1) * 16;
-          const uint16_t xa = static_cast<uint16_t>(xv[wi] >> sh);
-          const uint16_t xb = static_cast<uint16_t>(xv[2 + wi] >> sh);
-          const float fa = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xa) : f16_bits_to_f32(xa);
-          const float fb = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
-          lo[j] = f16_bits_to_f32(static_cast<uint16_t>(gv[wi] >> sh)) * fa;
-          hi[j] = f16_bits_to_f32(static_cast<uint16_t>(gv[2 + wi] >> sh)) * fb;
+        for (int q = 0; q < 4; ++q) {
+          const uint4 xv = reinterpret_cast<const uint4*>(xr + k0)[q];
+          const uint4 gv = reinterpret_cast<const uint4*>(g + k0)[q];
+          xw[4 * q] = xv.x; xw[4 * q + 1] = xv.y; xw[4 * q + 2] = xv.z; xw[4 * q + 3] = xv.w;
+          gw[4 * q] = gv.x; gw[4 * q + 1] = gv.y; gw[4 * q + 2] = gv.z; gw[4 * q + 3] = gv.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
+          const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
+          const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
+          a[i] = f16_bits_to_f32(gb) * xf;
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t klo = k0 + j, khi = klo + 16;
-          lo[j] = klo < p.M ? f16_bits_to_f32(g[klo]) * load_act(p.x, p.x_dtype, tok * p.ldx + klo) : 0.f;
-          hi[j] = khi < p.M ? f16_bits_to_f32(g[khi]) * load_act(p.x, p.x_dtype, tok * p.ldx + khi) : 0.f;
+        for (int i = 0; i < 32; ++i) {
+          const int64_t k = k0 + i;
+          a[i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
         }
       }
-      uint32_t o[4];
+      uint32_t o[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const _Float16 a = static_cast<_Float16>(lo[j]), b = static_cast<_Float16>(hi[j]);
-        acc += fabsf(static_cast<float>(a)) + fabsf(static_cast<float>(b));
-        o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+      for (int j = 0; j < 16; ++j) {
+        const _Float16 lo = static_cast<_Float16>(a[j]), hi = static_cast<_Float16>(a[j + 16]);
+        acc += fabsf(static_cast<float>(lo)) + fabsf(static_cast<float>(hi));
+        o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
       }
-      *reinterpret_cast<uint4*>(out + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+      uint4* dst = reinterpret_cast<uint4*>(out + 32 * grp);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     }
   } else {
     const int term = static_cast<int>(blk - nrow);
@@ -183,17 +183,57 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return v;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane l's
+// bytes land at LDS byte address lds + 16 l (global_load_lds_dwordx4, M0 =
+// lds).  Written as inline asm so that the compiler does not guard every
+// later LDS read with a wait for all such copies; the kernel waits for them
+// itself (wait_then_barrier) before reading a stage.  The instruction has no
+// register result, and its address registers are read when it issues.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; it is still clobbered
+__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait for this wave's vector-memory operations down to n outstanding, then
+// a workgroup barrier; the signal fences keep the compiler from moving
+// memory operations across either.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // STAGE 1: one term per grid row (blockIdx.y); STAGE 2: all terms in turn.
 // KW4: the sign matrix has 4 words per row per tile (K >= 97); otherwise a
 // single K-block of kw words per row.
-// NS: K steps of A and sign words prefetched into registers (1 or 2).
-template <int STAGE, bool KW4, int BM, int BN, int NS>
+// NB: LDS stages.  Each K step's operands (the BM x 128 fp16 A tile and, with
+// KW4, the 16 bytes of sign words of each of the BN columns) are copied
+// global -> LDS directly (global_load_lds_dwordx4, no register staging),
+// NB - 1 steps ahead of the MFMAs.  A rows are stored unpadded, 16-byte chunk
+// c of row r at chunk c ^ (r & 15), so the ds_read_b128 fragment reads of 16
+// consecutive rows hit 16 different chunk slots (all 64 banks, no conflict).
+template <int STAGE, bool KW4, int BM, int BN, int NB>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
   constexpr int RB = BM / 32;            // 32-token row blocks per wave
   constexpr int CB = BN / 128;           // 32-column blocks per wave
-  constexpr int CH = BM * (BK / 8) / kThreads;  // 16-byte A chunks per thread per step
+  constexpr int ACH = BM * (BK / 8) / kThreads;  // A chunks (16 B) per thread per step
+  constexpr int LPS = ACH + (KW4 ? 1 : 0);       // loads per thread per step
+  constexpr int ABYTES = BM * BK * 2;
+  constexpr int SBYTES = ABYTES + (KW4 ? BN * 16 : 0);
+  static_assert(LPS * (NB - 2) < 64, "vmcnt range");
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  _Float16 (*As)[BM * ALD] = reinterpret_cast<_Float16 (*)[BM * ALD]>(smem_raw);
   __shared__ float tokscale[BM];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 31, h = lane >> 5;
@@ -218,64 +258,50 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 
   const int spt = static_cast<int>(p.kp / BK);  // K steps per term
 
-  // per-thread A chunk offsets (row, 16-byte column) and validity
-  int64_t aoff[CH];
-  bool aok[CH];
+  // this thread's A chunks: LDS chunk q * 256 + tid of a stage is row
+  // (q * 256 + tid) / 16, slot tid % 16, and holds logical chunk
+  // slot ^ (row & 15).  Rows past T read row T - 1 (never stored).
+  int64_t aoff[ACH];
 #pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    const int c = tid + q * kThreads, row = c / (BK / 8), ch = c % (BK / 8);
-    aok[q] = tok0 + row < p.T;
-    aoff[q] = (tok0 + row) * p.kp + 8 * ch;
+  for (int q = 0; q < ACH; ++q) {
+    const int row = (q * kThreads + tid) >> 4;
+    const int c = (tid & 15) ^ (row & 15);
+    const int64_t tok = min(tok0 + row, p.T - 1);
+    aoff[q] = tok * p.kp + 8 * c;
   }
-  // per-lane packed row offsets (in words) of this wave's columns
-  int64_t boff[CB];
-  bool bok[CB];
+  // sign words: column col0 + j (j < BN) of a stage at byte ABYTES + 16 j;
+  // wave wv copies columns [wv * BN / 4, (wv + 1) * BN / 4)
+  int64_t boff = 0;
+  bool blane = true;
+  if constexpr (KW4) {
+    blane = lane < BN / 4;
+    const int64_t col = col0 + (BN / 4) * wv + lane;
+    const int64_t c = col < p.nrt * 64 ? col : 0;
+    boff = ((c >> 6) * p.nkb * 64 + (c & 63)) * 4;
+  }
+  // this lane's MFMA columns
   int64_t bcol[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    bcol[cb] = col0 + (BN / 4) * wv + 32 * cb + li;
-    bok[cb] = bcol[cb] < p.nrt * 64;
-    const int64_t rt = bcol[cb] >> 6, rr = bcol[cb] & 63;
-    boff[cb] = KW4 ? (rt * p.nkb * 64 + rr) * 4 : (rt * 64 + rr) * p.kw;
-  }
+  for (int cb = 0; cb < CB; ++cb) bcol[cb] = col0 + (BN / 4) * wv + 32 * cb + li;
 
   // load cursor: (term, step within the term), advanced one step at a time
   int lterm = term_first, lks = 0;
-  uint4 areg[NS][CH];
-  uint4 bw[NS][CB];
-  auto issue = [&](auto slot) {
-    constexpr int S = decltype(slot)::value;
+  // LDS byte address of the stages (the low 32 bits of the shared-aperture
+  // address are the LDS offset)
+  const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem_raw));
+  auto issue = [&](int stage_slot) {
+    const unsigned st = lds0 + stage_slot * SBYTES;
     const _Float16* base = p.a + static_cast<int64_t>(lterm) * p.T * p.kp + lks * BK;
 #pragma unroll
-    for (int q = 0; q < CH; ++q)
-      areg[S][q] = aok[q] ? *reinterpret_cast<const uint4*>(base + aoff[q]) : make_uint4(0, 0, 0, 0);
-    const uint32_t* bits = p.bits[lterm];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      if (!bok[cb]) {
-        bw[S][cb] = make_uint4(0, 0, 0, 0);
-      } else if constexpr (KW4) {
-        bw[S][cb] = *reinterpret_cast<const uint4*>(bits + boff[cb] + static_cast<int64_t>(lks) * 256);
-      } else {
-        // a single K-block of kw < 4 words per row
-        const uint32_t* src = bits + boff[cb];
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = j < p.kw ? src[j] : 0u;
-        bw[S][cb] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+    for (int q = 0; q < ACH; ++q) copy16_to_lds(base + aoff[q], st + q * 4096 + wv * 1024);
+    if constexpr (KW4) {
+      if (blane)
+        copy16_to_lds(p.bits[lterm] + boff + static_cast<int64_t>(lks) * 256,
+                      st + ABYTES + wv * (BN / 4) * 16);
     }
     if (++lks == spt) {
       lks = 0;
       ++lterm;
-    }
-  };
-  auto store_a = [&](auto buf, auto slot) {
-    constexpr int Bf = decltype(buf)::value, S = decltype(slot)::value;
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int c = tid + q * kThreads, row = c / (BK / 8), ch = c % (BK / 8);
-      *reinterpret_cast<uint4*>(&As[Bf][row * ALD + 8 * ch]) = areg[S][q];
     }
   };
 
@@ -304,74 +330,73 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   const int nsteps = (term_end - term_first) * spt;
-  // pipeline: LDS holds step s (buffer s & 1).  NS = 2: registers hold
-  // steps s + 1 (slot (s + 1) & 1) and s + 2 (slot s & 1, issued during step
-  // s).  NS = 1: the single slot holds step s + 1, issued during step s.
-  issue(I0{});
-  if constexpr (NS == 2) {
-    if (nsteps > 1) issue(I1{});
-  }
-  store_a(I0{}, I0{});
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (j < nsteps) issue(j);
   int cterm = term_first, cks = 0;  // compute cursor
   set_term(cterm);
-  uint4 bcur[CB];  // NS = 1: sign words of the step being computed
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) bcur[cb] = bw[0][cb];
-  auto kstep = [&](int step, auto bufc) {
-    constexpr int B = decltype(bufc)::value;
-    using Other = std::integral_constant<int, B ^ 1>;
+  for (int step = 0; step < nsteps; ++step) {
+    // this step's copies are done once at most (later steps issued) * LPS
+    // of this wave's loads are still in flight; then all waves' are
+    const int later = min(NB - 2, nsteps - 1 - step);
+    if constexpr (NB == 2) {
+      wait_then_barrier<0>();
+    } else {
+      if (later >= NB - 2) wait_then_barrier<LPS * (NB - 2)>();
+      else if (NB >= 4 && later == 1) wait_then_barrier<LPS>();
+      else wait_then_barrier<0>();
+    }
+    // the stage read one step ago is free again
+    if (step + NB - 1 < nsteps) issue((step + NB - 1) % NB);
+    const unsigned char* st = smem_raw + (step % NB) * SBYTES;
     uint32_t cw[CB][4];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const uint4 wv4 = NS == 2 ? bw[B % NS][cb] : bcur[cb];
-      cw[cb][0] = wv4.x; cw[cb][1] = wv4.y; cw[cb][2] = wv4.z; cw[cb][3] = wv4.w;
-    }
-    __syncthreads();
-    if constexpr (NS == 2) {
-      if (step + 2 < nsteps) issue(bufc);
-    } else {
-      if (step + 1 < nsteps) issue(I0{});
-    }
-    const _Float16* at = As[B];
+      if constexpr (KW4) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(st + ABYTES + ((BN / 4) * wv + 32 * cb + li) * 16);
+        cw[cb][0] = w4.x; cw[cb][1] = w4.y; cw[cb][2] = w4.z; cw[cb][3] = w4.w;
+      } else {
+        // a single K-block of kw < 4 words per row (one step per term)
+        const int64_t col = bcol[cb];
+        const uint32_t* src = p.bits[cterm] + ((col >> 6) * 64 + (col & 63)) * p.kw;
 #pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
+        for (int j = 0; j < 4; ++j) cw[cb][j] = (j < p.kw && col < p.nrt * 64) ? src[j] : 0u;
+      }
+    }
+    // 8 sub-steps of 16 features (wi, sub); the A fragments and sign values
+    // of sub-step kk + 1 are fetched before the MFMAs of kk (the compiler
+    // schedules them)
+    half8 af[2][RB], bf[2][CB];
+    auto fetch = [&](int kk, int slot) {
+      const int wi = kk >> 1, sub = kk & 1;
+      const int c = 4 * wi + 2 * sub + h;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        half8 bf[CB];
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 32 * rb + li;
+        af[slot][rb] = *reinterpret_cast<const half8*>(st + row * (BK * 2) + ((c ^ (row & 15)) << 4));
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        bf[slot][cb] = unpack_frag(cw[cb][wi] ^ flip[cb], h, sub, mag[cb]);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk + 1 < 8) fetch(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          bf[cb] = unpack_frag(cw[cb][wi] ^ flip[cb], h, sub, mag[cb]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const half8 af = *reinterpret_cast<const half8*>(
-              at + (32 * rb + li) * ALD + 32 * wi + 16 * sub + 8 * h);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[rb][cb], 0, 0, 0);
-        }
-      }
-    }
-    if (step + 1 < nsteps) {
-      if constexpr (NS == 2) {
-        store_a(Other{}, Other{});
-      } else {
-        store_a(Other{}, I0{});
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) bcur[cb] = bw[0][cb];
-      }
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][rb], bf[kk & 1][cb],
+                                                               acc[rb][cb], 0, 0, 0);
     }
     if (STAGE == 2 && ++cks == spt) {
       cks = 0;
       if (++cterm < term_end) set_term(cterm);
     }
-  };
-  for (int step = 0; step < nsteps; step += 2) {
-    kstep(step, I0{});
-    if (step + 1 < nsteps) kstep(step + 1, I1{});
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue; D layout: lane l, register r -> column l % 32,
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the 32 x 32 block
@@ -430,8 +455,7 @@ hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_
   a.ntt = static_cast<int>(cdiv(a.T, bm));
   a.ntc = static_cast<int>(cdiv(cols, bn));
   const dim3 grid(static_cast<unsigned>(a.ntt * a.ntc), terms_in_grid);
-  auto go = [&](auto kern, int bm_) -> hipError_t {
-    const size_t lds = 2u * static_cast<size_t>(bm_) * ALD * sizeof(_Float16);
+  auto go = [&](auto kern, size_t lds) -> hipError_t {
     static bool attr_set = false;  // per instantiation; idempotent if raced
     if (!attr_set) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -443,9 +467,13 @@ hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_
     kern<<<grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
   };
-  if (bm == 128 && bn == 256) return go(gemm_kernel<STAGE, KW4, 128, 256, 1>, 128);
-  if (bm == 128) return go(gemm_kernel<STAGE, KW4, 128, 128, 2>, 128);
-  return go(gemm_kernel<STAGE, KW4, 64, 128, 2>, 64);
+  // LDS per stage: the fp16 A tile plus (KW4) 16 bytes of sign words per column
+  auto lds_of = [](int bm_, int bn_, int nb_) {
+    return static_cast<size_t>(nb_) * (static_cast<size_t>(bm_) * BK * 2 + (KW4 ? bn_ * 16 : 0));
+  };
+  if (bm == 128 && bn == 256) return go(gemm_kernel<STAGE, KW4, 128, 256, kStages>, lds_of(128, 256, kStages));
+  if (bm == 128) return go(gemm_kernel<STAGE, KW4, 128, 128, kStages>, lds_of(128, 128, kStages));
+  return go(gemm_kernel<STAGE, KW4, 64, 128, kStages>, lds_of(64, 128, kStages));
 }
 
 template <int STAGE>
@@ -490,9 +518,9 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   PrepArgs pa{};
   pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
   pa.R = R; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
-  pa.vec = (ldx % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 8 == 0);
+  pa.vec = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   for (int i = 0; i < t.n; ++i)
-    if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) pa.vec = 0;
+    if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) pa.vec = 0;
   for (int i = 0; i < t.n; ++i) {
     pa.gamma[i] = t.gamma[i];
     pa.beta[i] = t.beta[i];
