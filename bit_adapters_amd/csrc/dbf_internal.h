@@ -116,11 +116,13 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
                           int64_t ldy, void* ws, hipStream_t s);
 
 // The head of every workspace carries the decode path's stage-1 -> stage-2
-// handoff: 256 bytes of counters, then kSyncWords 4-byte producer words.
-// It is zero before first use and every call leaves it zero; no path keeps
-// scratch there.
-constexpr size_t kSyncWords = 4096;
-constexpr size_t kWsHeadBytes = 256 + 4 * kSyncWords;
+// handoff: 256 bytes of counters, then kSyncSlots producer counters, each in
+// its own 256-byte slot (counters packed into a few cache lines made every
+// handoff 2-3 us slower).  It is zero before first use and every call leaves
+// it zero; no path keeps scratch there.
+constexpr size_t kSyncSlots = 64;
+constexpr size_t kSyncStride = 64;  // 4-byte words between slots (256 B)
+constexpr size_t kWsHeadBytes = 256 + 4 * kSyncSlots * kSyncStride;
 static_assert(kWsHeadBytes == DBF_WS_HEAD_BYTES, "workspace head size");
 
 // Row stride (floats) of the rank-R intermediate in the workspace.

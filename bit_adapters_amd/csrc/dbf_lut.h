@@ -257,58 +257,57 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
 }
 
 // ---- handoff between the two roles of a launch ---------------------------
-// Producer p owns word p % kSyncWords of the workspace head (one producer
-// per word up to kSyncWords producers).  Its results are written through to
-// memory (system-scope stores, see store_shared) and, once they are
-// complete, it adds one to its word, also at system scope: no L2 writeback
-// of the whole cache is needed on the producer's side.  Consumers poll the
-// words with loads that bypass the caches, then invalidate their caches
-// (agent-scope acquire) before reading the results.  Counters: ctr[0]
-// consumers past their wait, ctr[2] set if a wait gave up.
+// Producer p adds one to counter p % kSyncSlots in the workspace head, each
+// counter in its own 256-byte slot.  Its results are written through to
+// memory first (system-scope stores, store_shared), so no L2 writeback of the
+// whole cache is needed; it waits for them, then adds, also at system scope.
+// Consumers poll the counters with loads that bypass the caches (lane l of
+// wave 0 reads counter l), then invalidate their caches (agent-scope
+// acquire) before reading the results.  ctr[0] counts consumers past their
+// wait, ctr[2] is set if a wait gave up.
 struct Sync {
   unsigned* ctr;
-  unsigned* words;
+  unsigned* slots;
   unsigned n_prod, n_cons;
 };
 
 inline Sync make_sync(void* ws, int64_t n_prod, int64_t n_cons) {
   Sync s;
   s.ctr = static_cast<unsigned*>(ws);
-  s.words = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + 256);
+  s.slots = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + 256);
   s.n_prod = static_cast<unsigned>(n_prod);
   s.n_cons = static_cast<unsigned>(n_cons);
   return s;
 }
 
 // Producer `pid`, called by all threads after its store_shared results:
-// the storing wave (wave 0) waits for their completion, then adds its word.
+// the storing wave (wave 0) waits for their completion, then adds.
 __device__ __forceinline__ void publish(const Sync& s, unsigned pid) {
   if (threadIdx.x == 0) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
-    __hip_atomic_fetch_add(s.words + pid % kSyncWords, 1u, __ATOMIC_RELAXED,
+    __hip_atomic_fetch_add(s.slots + (pid % kSyncSlots) * kSyncStride, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
-// Consumer: the lanes of wave 0 poll the producer words until each holds
-// its count, then acquire; the workgroup barrier orders the other waves
-// after it.  Thread 0 then takes a ticket (the consumers' arrival order) at
-// once; its value is only needed by consumer_done at the end.
+// Consumer: lane l of wave 0 polls counter l until every counter holds its
+// count, then acquires; the workgroup barrier orders the other waves after
+// it.  Thread 0 then takes a ticket (the consumers' arrival order) at once;
+// its value is only needed by consumer_done at the end.
 __device__ __forceinline__ unsigned wait_producers(const Sync& s) {
+  static_assert(kSyncSlots <= 64, "one counter per lane");
   unsigned ticket = 0;
   if (threadIdx.x < 64) {
     const unsigned lane = threadIdx.x;
-    const unsigned nw = s.n_prod < kSyncWords ? s.n_prod : static_cast<unsigned>(kSyncWords);
-    const unsigned base = s.n_prod / static_cast<unsigned>(kSyncWords);
-    const unsigned extra = s.n_prod % static_cast<unsigned>(kSyncWords);
+    const unsigned ns = static_cast<unsigned>(kSyncSlots);
+    const unsigned want = lane < ns ? s.n_prod / ns + (lane < s.n_prod % ns ? 1u : 0u) : 0u;
     unsigned spins = 0;
     while (true) {
-      bool ok = true;
-      for (unsigned w = lane; w < nw; w += 64) {
-        const unsigned want = base + (w < extra ? 1u : 0u);
-        ok &= __hip_atomic_load(s.words + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= want;
-      }
-      if (__all(ok)) break;
+      const unsigned have =
+          want > 0u ? __hip_atomic_load(s.slots + lane * kSyncStride, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_SYSTEM)
+                    : 0u;
+      if (__all(have >= want)) break;
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
         if (lane == 0)
@@ -326,17 +325,12 @@ __device__ __forceinline__ unsigned wait_producers(const Sync& s) {
 
 // Consumer, at its end, with the ticket of its wait: the last consumer to
 // pass its wait (every producer has published and every consumer has
-// waited by then) clears the producer words and the counter for the next
-// call.
+// waited by then) clears the counters for the next call.
 __device__ __forceinline__ void consumer_done(const Sync& s, unsigned ticket) {
-  __shared__ unsigned last;
-  if (threadIdx.x == 0) last = ticket == s.n_cons - 1u;
-  __syncthreads();
-  if (last) {
-    const unsigned nw = s.n_prod < kSyncWords ? s.n_prod : static_cast<unsigned>(kSyncWords);
-    for (unsigned w = threadIdx.x; w < nw; w += blockDim.x)
-      __hip_atomic_store(s.words + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    if (threadIdx.x == 0) __hip_atomic_store(s.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (threadIdx.x == 0 && ticket == s.n_cons - 1u) {
+    for (unsigned i = 0; i < kSyncSlots; ++i)
+      __hip_atomic_store(s.slots + i * kSyncStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(s.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
