@@ -48,7 +48,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   const int64_t row = rt * 64 + lane;
   uint32_t wd[PW][KW];
   load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
-  const unsigned ticket = wait_producers(p.sync);
+  const unsigned ticket = wait_producers(p.sync, false);  // partials via load_shared4
   bool have_bits = true;
   {
     const int64_t tok0 = tblk * TB;
@@ -79,7 +79,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
           PT4 q[kMaxKS];
 #pragma unroll
           for (int s = 0; s < kMaxKS; ++s)
-            if (s < p.ks) q[s] = *reinterpret_cast<const PT4*>(wsp + base + s * p.T * p.rs);
+            if (s < p.ks) q[s] = load_shared4<PT4>(wsp + base + s * p.T * p.rs);
           PT4 sum = q[0];
 #pragma unroll
           for (int s = 1; s < kMaxKS; ++s)

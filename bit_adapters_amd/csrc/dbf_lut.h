@@ -51,6 +51,23 @@ __device__ __forceinline__ void store_shared(V* p, V v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Four results of other workgroups of the launch (16-byte aligned), read at
+// system scope: the loads bypass the caches, so they see what store_shared
+// wrote through once the producer's counter was seen, without an
+// invalidation of the whole L2.
+template <typename V4, typename E>
+__device__ __forceinline__ V4 load_shared4(const E* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  V4 v;
+  v.x = __builtin_bit_cast(E, static_cast<uint32_t>(lo));
+  v.y = __builtin_bit_cast(E, static_cast<uint32_t>(lo >> 32));
+  v.z = __builtin_bit_cast(E, static_cast<uint32_t>(hi));
+  v.w = __builtin_bit_cast(E, static_cast<uint32_t>(hi >> 32));
+  return v;
+}
+
 template <typename A>
 __device__ __forceinline__ void build_signed16(A a0, A a1, A a2, A a3, A* e) {
   const A p0 = -a0 - a1, p1 = a0 - a1, p2 = a1 - a0, p3 = a0 + a1;
@@ -291,10 +308,12 @@ __device__ __forceinline__ void publish(const Sync& s, unsigned pid) {
 }
 
 // Consumer: lane l of wave 0 polls counter l until every counter holds its
-// count, then acquires; the workgroup barrier orders the other waves after
-// it.  Thread 0 then takes a ticket (the consumers' arrival order) at once;
+// count, then acquires (an agent-scope invalidation of L1 and L2, about a
+// microsecond; a consumer that reads the results only with load_shared4
+// passes acquire = false); the workgroup barrier orders the other waves
+// after it.  Thread 0 then takes a ticket (the consumers' arrival order);
 // its value is only needed by consumer_done at the end.
-__device__ __forceinline__ unsigned wait_producers(const Sync& s) {
+__device__ __forceinline__ unsigned wait_producers(const Sync& s, bool acquire = true) {
   static_assert(kSyncSlots <= 64, "one counter per lane");
   unsigned ticket = 0;
   if (threadIdx.x < 64) {
@@ -315,11 +334,13 @@ __device__ __forceinline__ unsigned wait_producers(const Sync& s) {
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (lane == 0)
-      ticket = __hip_atomic_fetch_add(s.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+  // after the barrier, which would otherwise wait for the ticket's return;
+  // the loads that follow overlap with it
+  if (threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(s.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   return ticket;
 }
 
@@ -327,10 +348,14 @@ __device__ __forceinline__ unsigned wait_producers(const Sync& s) {
 // pass its wait (every producer has published and every consumer has
 // waited by then) clears the counters for the next call.
 __device__ __forceinline__ void consumer_done(const Sync& s, unsigned ticket) {
-  if (threadIdx.x == 0 && ticket == s.n_cons - 1u) {
-    for (unsigned i = 0; i < kSyncSlots; ++i)
-      __hip_atomic_store(s.slots + i * kSyncStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(s.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (threadIdx.x < 64) {
+    // thread 0 holds the ticket; the lanes of wave 0 clear one counter each
+    if (__builtin_amdgcn_readfirstlane(ticket) == s.n_cons - 1u) {
+      if (threadIdx.x < kSyncSlots)
+        __hip_atomic_store(s.slots + threadIdx.x * kSyncStride, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+      if (threadIdx.x == 0) __hip_atomic_store(s.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
