@@ -72,8 +72,11 @@ struct PrepArgs {
   int vec;      // 16-byte loads of x and gamma allowed
 };
 
+constexpr int kPrepSeg = 8192;  // features of a row staged in LDS at a time
+
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
-  __shared__ float red[256];
+  __shared__ float red[4];
+  __shared__ __align__(16) _Float16 useg[kPrepSeg];
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x;
   const int64_t nrow = static_cast<int64_t>(p.L) * p.T;
@@ -84,60 +87,79 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
     const uint16_t* g = p.gamma[term];
     _Float16* out = p.u + blk * p.mpad;
     const uint16_t* xr = static_cast<const uint16_t*>(p.x) + tok * p.ldx;
-    // one 32-feature group per thread and iteration: features k0 .. k0 + 31
-    // in, positions 2 j (feature k0 + j) and 2 j + 1 (k0 + 16 + j) out
-    for (int64_t grp = tid; grp < p.mpad / 32; grp += 256) {
-      const int64_t k0 = grp * 32;
-      float a[32];
-      if (p.vec && k0 + 32 <= p.M) {
-        uint32_t xw[16], gw[16];
+    // the row in segments of kPrepSeg features: u in natural order into LDS
+    // (coalesced 16-byte loads, 8 features per thread and chunk), then each
+    // thread writes one 16-byte chunk of the pair order (positions 2 j and
+    // 2 j + 1 hold features j and j + 16 of a 32-feature group)
+    for (int64_t seg = 0; seg < p.mpad; seg += kPrepSeg) {
+      const int64_t segn = min<int64_t>(kPrepSeg, p.mpad - seg);
+      for (int64_t c = tid; c < segn / 8; c += 256) {
+        const int64_t k0 = seg + 8 * c;
+        float a[8];
+        if (p.vec && k0 + 8 <= p.M) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xr + k0);
+          const uint4 gv = *reinterpret_cast<const uint4*>(g + k0);
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 xv = reinterpret_cast<const uint4*>(xr + k0)[q];
-          const uint4 gv = reinterpret_cast<const uint4*>(g + k0)[q];
-          xw[4 * q] = xv.x; xw[4 * q + 1] = xv.y; xw[4 * q + 2] = xv.z; xw[4 * q + 3] = xv.w;
-          gw[4 * q] = gv.x; gw[4 * q + 1] = gv.y; gw[4 * q + 2] = gv.z; gw[4 * q + 3] = gv.w;
-        }
+          for (int i = 0; i < 8; ++i) {
+            const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
+            const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
+            const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
+            a[i] = f16_bits_to_f32(gb) * xf;
+          }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
-          const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
-          const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
-          a[i] = f16_bits_to_f32(gb) * xf;
+          for (int i = 0; i < 8; ++i) {
+            const int64_t k = k0 + i;
+            a[i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
+          }
         }
-      } else {
+        uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int64_t k = k0 + i;
-          a[i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const _Float16 lo = static_cast<_Float16>(a[2 * j]), hi = static_cast<_Float16>(a[2 * j + 1]);
+          acc += fabsf(static_cast<float>(lo)) + fabsf(static_cast<float>(hi));
+          o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
+        reinterpret_cast<uint4*>(useg)[c] = make_uint4(o[0], o[1], o[2], o[3]);
       }
-      uint32_t o[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const _Float16 lo = static_cast<_Float16>(a[j]), hi = static_cast<_Float16>(a[j + 16]);
-        acc += fabsf(static_cast<float>(lo)) + fabsf(static_cast<float>(hi));
-        o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      __syncthreads();
+      // output chunk c: group c / 4, pairs 4 (c % 4) .. + 3 = features
+      // 4 (c % 4) .. + 3 (low halves) and 16 + 4 (c % 4) .. + 3 (high halves)
+      for (int64_t c = tid; c < segn / 8; c += 256) {
+        const int64_t grp = c >> 2, q4 = c & 3;
+        const uint2 lo = reinterpret_cast<const uint2*>(useg)[grp * 8 + q4];      // features 4 q4 ..
+        const uint2 hi = reinterpret_cast<const uint2*>(useg)[grp * 8 + 4 + q4];  // 16 + 4 q4 ..
+        uint4 w;
+        w.x = (lo.x & 0xFFFFu) | (hi.x << 16);
+        w.y = (lo.x >> 16) | (hi.x & 0xFFFF0000u);
+        w.z = (lo.y & 0xFFFFu) | (hi.y << 16);
+        w.w = (lo.y >> 16) | (hi.y & 0xFFFF0000u);
+        reinterpret_cast<uint4*>(out + seg)[c] = w;
       }
-      uint4* dst = reinterpret_cast<uint4*>(out + 32 * grp);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+      __syncthreads();
     }
   } else {
     const int term = static_cast<int>(blk - nrow);
     for (int64_t r = tid; r < p.R; r += 256)
       acc = fmaxf(acc, fabsf(f16_bits_to_f32(p.beta[term][r])));
   }
-  red[tid] = acc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = blk < nrow ? red[tid] + red[tid + s] : fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
+  // sum (or max) over the workgroup: within each wave, then over the 4 waves
+  const bool sum = blk < nrow;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(acc, off);
+    acc = sum ? acc + o : fmaxf(acc, o);
   }
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
   if (tid == 0) {
-    if (blk < nrow) p.l1[blk] = red[0];
-    else p.bmax[blk - nrow] = red[0];
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) r = sum ? r + red[w] : fmaxf(r, red[w]);
+    if (sum) p.l1[blk] = r;
+    else p.bmax[blk - nrow] = r;
   }
 }
 
