@@ -247,7 +247,8 @@ __device__ __forceinline__ void wait_then_barrier() {
 // c of row r at chunk c ^ (r & 15), so the ds_read_b128 fragment reads of 16
 // consecutive rows hit 16 different chunk slots (all 64 banks, no conflict).
 template <int STAGE, bool KW4, int BM, int BN, int NB>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_kernel(GemmArgs p) {
   constexpr int RB = BM / 32;            // 32-token row blocks per wave
   constexpr int CB = BN / 128;           // 32-column blocks per wave
   constexpr int ACH = BM * (BK / 8) / kThreads;  // A chunks (16 B) per thread per step
@@ -421,48 +422,78 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue; D layout: lane l, register r -> column l % 32,
-  // row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the 32 x 32 block
-  if constexpr (STAGE == 1) {
-    // v = fp16(s_t * beta_r * acc) at the pair-order position of r
-    _Float16* vt = p.v + static_cast<int64_t>(term_first) * p.T * p.vp;
-    float bsc[CB];
-    int64_t vpos[CB];
+  // row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the 32 x 32 block.  Each wave
+  // stages one 32-column block at a time in its own LDS slice (the stage
+  // buffers are free now) and writes it out as 16-byte row chunks.
+  __syncthreads();  // every wave is done with the stage buffers
+  unsigned char* wbuf = smem_raw + wv * (BM * 32 * 4);
+  // staged element: fp16 v; y as stored, or fp32 when adding to y (one
+  // rounding of old + new)
+  const int esize = STAGE == 1 ? 2 : ((p.y_dtype == DBF_F32 || p.accumulate) ? 4 : 2);
+  const int cpr = 32 * esize / 16;  // 16-byte chunks per staged row
+  const bool vec_y = STAGE == 2 && !p.accumulate && (p.ldy * esize) % 16 == 0;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      bsc[cb] = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term_first][bcol[cb]]) : 0.f;
-      const int64_t r = bcol[cb], g = r >> 5, rr = r & 31;
-      vpos[cb] = g * 32 + (rr < 16 ? 2 * rr : 2 * (rr - 16) + 1);
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t c0 = col0 + (BN / 4) * wv + 32 * cb;  // first column of the block
+    if constexpr (STAGE == 1) {
+      // v = fp16(s_t * beta_r * acc) at the pair-order position of r
+      const float bsc = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term_first][bcol[cb]]) : 0.f;
+      const int pos = li < 16 ? 2 * li : 2 * (li - 16) + 1;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+          reinterpret_cast<_Float16*>(wbuf)[rl * 32 + pos] =
+              static_cast<_Float16>(tokscale[rl] * bsc * acc[rb][cb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float o = acc[rb][cb][r] / tokscale[rl];
+          if (esize == 4)
+            reinterpret_cast<float*>(wbuf)[rl * 32 + li] = o;
+          else
+            reinterpret_cast<uint16_t*>(wbuf)[rl * 32 + li] =
+                p.y_dtype == DBF_BF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
+        }
     }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int64_t tok = tok0 + rl;
-        if (tok >= p.T) continue;
-        const float sc = tokscale[rl];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          if (bcol[cb] < p.vp)
-            vt[tok * p.vp + vpos[cb]] = static_cast<_Float16>(sc * bsc[cb] * acc[rb][cb][r]);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // slice written by the whole wave
+    for (int c = lane; c < BM * cpr; c += 64) {
+      const int row = c / cpr, ch = c - row * cpr;
+      const int64_t tok = tok0 + row;
+      if (tok >= p.T) continue;
+      const uint4 d = reinterpret_cast<const uint4*>(wbuf)[c];
+      if constexpr (STAGE == 1) {
+        // 8 positions of the 32-position group of this block
+        const int64_t pos = c0 + 8 * ch;
+        if (pos < p.vp)
+          *reinterpret_cast<uint4*>(p.v + (static_cast<int64_t>(term_first) * p.T + tok) * p.vp + pos) = d;
+      } else {
+        const int per = 16 / esize;
+        const int64_t col = c0 + per * ch;
+        if (vec_y && col + per <= p.ncols) {
+          *reinterpret_cast<uint4*>(static_cast<unsigned char*>(p.y) + (tok * p.ldy + col) * esize) = d;
+        } else {
+          const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+          for (int e = 0; e < per; ++e) {
+            if (col + e >= p.ncols) break;
+            float v;
+            if (esize == 4)
+              v = __uint_as_float(w[e]);
+            else {
+              const uint16_t b = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+              v = p.y_dtype == DBF_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+            }
+            store_out(p.y, p.y_dtype, tok * p.ldy + col + e, v, p.accumulate);
+          }
+        }
       }
     }
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int64_t tok = tok0 + rl;
-        if (tok >= p.T) continue;
-        const float inv = 1.0f / tokscale[rl];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          if (bcol[cb] < p.ncols)
-            store_out(p.y, p.y_dtype, tok * p.ldy + bcol[cb], acc[rb][cb][r] * inv,
-                      p.accumulate);
-      }
-    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // slice read before reuse
   }
 }
 
