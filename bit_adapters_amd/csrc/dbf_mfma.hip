@@ -11,6 +11,8 @@
 //             |w_i[t, r]| <= bmax_i * l_i[t], every s_t * w fits fp16
 //   stage 1:  v_i[t, r] = fp16(s_t * beta_i[r] * sum_m S2_i[r, m] u_i[t, m])
 //   stage 2:  y[t, n] = (1 / s_t) sum_i sum_r (+-alpha_i[n]) v_i[t, r]
+//             (one term: alpha_1[n] / s_t * sum_r (+-1) v_1[t, r], alpha
+//             applied in the epilogue)
 //
 // Rounding: u and v are each rounded to fp16 once (relative 2^-11), all
 // sums are fp32; alpha, beta and the +-1 signs are exact in fp16.
@@ -20,9 +22,9 @@
 // (k, k + 16): position 2j holds k = j, position 2j + 1 holds k = j + 16.
 // A lane then builds its B fragment for pairs (k, k + 16) from one 32-bit
 // word of its packed sign row with one shift and one v_and_or_b32 per pair:
-// bits k and k + 16 land on the two fp16 sign bits.  Stage 2 folds alpha
-// into those values (+-|alpha_n|, exact), so all terms accumulate into the
-// same registers.
+// bits k and k + 16 land on the two fp16 sign bits.  With several terms,
+// stage 2 folds alpha into those values (+-|alpha_n|, exact), so all terms
+// accumulate into the same registers.
 //
 // Tiles: a workgroup computes BM tokens x BN columns with 4 wavefronts, each
 // owning BN / 4 columns of all BM tokens with v_mfma_f32_32x32x16_f16.  K
@@ -330,10 +332,14 @@ gemm_kernel(GemmArgs p) {
 
   // sign fold and magnitude per column block (stage 2: +-|alpha|, stage 1: +-1)
   uint32_t flip[CB], mag[CB];
+  // With one term, stage 2 applies alpha in the epilogue instead, so its
+  // sign operand is +-1 as in stage 1 (fewer toggling operand bits: the
+  // matrix cores run measurably faster on them).
+  const bool fold_alpha = STAGE == 2 && p.L > 1;
   auto set_term = [&](int term) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      if constexpr (STAGE == 1) {
+      if (!fold_alpha) {
         flip[cb] = 0xFFFFFFFFu;           // bit 1 (+1) -> sign bit 0
         mag[cb] = opaque(0x3C003C00u);    // 1.0, 1.0
       } else {
@@ -448,12 +454,13 @@ gemm_kernel(GemmArgs p) {
               static_cast<_Float16>(tokscale[rl] * bsc * acc[rb][cb][r]);
         }
     } else {
+      const float asc = (!fold_alpha && bcol[cb] < p.ncols) ? f16_bits_to_f32(p.colscale[0][bcol[cb]]) : 1.f;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float o = acc[rb][cb][r] / tokscale[rl];
+          const float o = asc * acc[rb][cb][r] / tokscale[rl];
           if (esize == 4)
             reinterpret_cast<float*>(wbuf)[rl * 32 + li] = o;
           else
