@@ -29,9 +29,9 @@
 // Tiles: a workgroup computes BM tokens x BN columns with 4 wavefronts, each
 // owning BN / 4 columns of all BM tokens with v_mfma_f32_32x32x16_f16.  K
 // advances 128 features (one K-block of the bit layout) per step; the fp16
-// activation tile (A) is copied
-// global -> LDS, double-buffered, with 16 bytes of padding per row
-// (conflict-free ds_read_b128 fragments).  Workgroup indices are remapped so
+// activation tile (A) and the columns' sign words are copied global -> LDS
+// directly (two stages, one step ahead), the A rows XOR-swizzled for
+// conflict-free ds_read_b128 fragments.  Workgroup indices are remapped so
 // that consecutive tiles of one XCD share token rows (L2 reuse).  The tile
 // shape is chosen per launch so that at least ~256 workgroups run.
 #include <type_traits>
