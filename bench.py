@@ -169,9 +169,9 @@ def main():
     tok_s = T / (ms * 1e-3)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    # the library's automatic choice: decode kernel up to 16 tokens, MFMA above
+    # the library's automatic choice: decode kernel while T * terms <= 32
     path = "adapter" if base else (
-        {1: "decode", 2: "mfma"}.get(args.path) or ("decode" if T <= 16 else "mfma"))
+        {1: "decode", 2: "mfma"}.get(args.path) or ("decode" if T * L <= 32 else "mfma"))
     # achieved = algorithmic bytes (flops) per step / HIP-event time per step;
     # decode and adapter steps are one kernel launch each, the MFMA step is
     # three (prep, stage-1 GEMM, stage-2 GEMM) and is rated as a whole

@@ -23,11 +23,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
 
 // Decode path up to this many tokens when the caller lets the library pick.
-constexpr int64_t kAutoDecodeMaxT = 16;
+// DBF_PATH_AUTO: the decode kernel while T * n_terms <= 32 (measured on the
+// 4096 x 4096 R 2048 layer and the three-term 11008 x 4096 layer: below it
+// the decode launch is faster, above it the MFMA products are).
+constexpr int64_t kAutoDecodeMaxWork = 32;
 
-int resolve_path(int path, int64_t T) {
+int resolve_path(int path, int64_t T, int n_terms) {
   if (path != DBF_PATH_AUTO) return path;
-  return T <= kAutoDecodeMaxT ? DBF_PATH_DECODE : DBF_PATH_MFMA;
+  return T * n_terms <= kAutoDecodeMaxWork ? DBF_PATH_DECODE : DBF_PATH_MFMA;
 }
 
 constexpr int kMaxDevices = 64;
@@ -147,7 +150,7 @@ int dbf_unpack(const uint32_t* packed, int64_t rows, int64_t k, int8_t* dst,
 size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
                            int64_t T, int path) {
   if (N <= 0 || M <= 0 || R <= 0 || n_terms <= 0 || T <= 0) return 0;
-  if (resolve_path(path, T) == DBF_PATH_MFMA)
+  if (resolve_path(path, T, n_terms) == DBF_PATH_MFMA)
     return dbf::mfma_ws_bytes(N, M, R, n_terms, T);
   return dbf::decode_ws_bytes(N, M, R, n_terms, T);
 }
@@ -172,7 +175,7 @@ int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
   if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
   if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
   if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
-  const int p = resolve_path(path, T);
+  const int p = resolve_path(path, T, n_terms);
   e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, n_terms, T, p));
   if (e != DBF_OK) return e;
   e = check_device();

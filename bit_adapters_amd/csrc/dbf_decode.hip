@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, 
   stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
 }
 
-constexpr int64_t kStage1Wg = 192;
+constexpr int64_t kStage1Wg = 512;
 
 template <typename A, int MODE>
 hipError_t run(const Stage1& s1, const Stage2& s2, int n1, int n2, int run_stage2,

@@ -31,7 +31,7 @@ enum { MODE_F = 0, MODE_I8_BETA = 1, MODE_I8 = 2 };
 
 // Token-block size and K-blocks per wave per pass for T tokens.
 __host__ __device__ constexpr int pw_of(int tb) { return tb == 1 ? 2 : 1; }
-inline int pick_tb(int64_t T) { return T <= 1 ? 1 : (T == 2 ? 2 : 4); }
+inline int pick_tb(int64_t T) { return T <= 1 ? 1 : (T <= 4 ? 2 : 4); }
 
 // LDS (elements of type A): tables [TB][groups][16], wave partials
 // [4][TB][64].

@@ -154,9 +154,9 @@ size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
  *   y                [T x N], y_dtype DBF_F32, DBF_BF16 or DBF_F16, ldy.
  *   accumulate       0: y = result; 1: y = y + result (in fp32).
  *   ws, ws_bytes     workspace of dbf_workspace_bytes(..., path) bytes.
- *   path             DBF_PATH_AUTO picks the decode path for T <= 16 and the
- *                    MFMA path above; the others force one (both are
- *                    correct for every T >= 1).
+ *   path             DBF_PATH_AUTO picks the decode path while
+ *                    T * n_terms <= 32 and the MFMA path above; the others
+ *                    force one (both are correct for every T >= 1).
  * Accumulation is fp32; the decode path keeps every intermediate in fp32,
  * the MFMA path rounds gamma*x and the scaled rank-R intermediate to fp16
  * (with an exact power-of-two scale per token).

@@ -55,6 +55,17 @@ def test_workspace_bytes():
     assert D.dbf_workspace_bytes(512, 512, 256, 1, 1, D.DBF_PATH_MFMA) > 0
 
 
+@pytest.mark.parametrize("T,L,path", [(1, 1, "decode"), (32, 1, "decode"), (33, 1, "mfma"),
+                                      (10, 3, "decode"), (11, 3, "mfma"), (4096, 1, "mfma")])
+def test_auto_path_rule(T, L, path):
+    # automatic choice: the decode kernel while T * n_terms <= 32
+    want = D.DBF_PATH_DECODE if path == "decode" else D.DBF_PATH_MFMA
+    auto = D.dbf_workspace_bytes(4096, 4096, 2048, L, T, D.DBF_PATH_AUTO)
+    assert auto == D.dbf_workspace_bytes(4096, 4096, 2048, L, T, want)
+    other = D.DBF_PATH_MFMA if want == D.DBF_PATH_DECODE else D.DBF_PATH_DECODE
+    assert auto != D.dbf_workspace_bytes(4096, 4096, 2048, L, T, other)
+
+
 L = D.library()
 FAKE = 1 << 20            # a 16-byte aligned non-NULL address, never touched
 MIS = FAKE + 8            # misaligned
