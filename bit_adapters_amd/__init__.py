@@ -24,14 +24,16 @@ _i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_s
 
 DBF_OK, DBF_EINVAL, DBF_EDTYPE, DBF_EALIGN = 0, -1, -2, -3
 DBF_EWORKSPACE, DBF_EDEVICE, DBF_EUNSUPPORTED, DBF_ELAUNCH = -4, -5, -6, -7
+DBF_ESTALLED = -8
 DBF_F16, DBF_BF16, DBF_F32, DBF_I8, DBF_I32 = 1, 2, 3, 4, 5
 DBF_PATH_AUTO, DBF_PATH_DECODE, DBF_PATH_MFMA = 0, 1, 2
 DBF_MAX_TERMS = 8
+DBF_WS_HEAD_BYTES = 16640
 
 EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
            "dbf_packed_bytes", "dbf_pack", "dbf_unpack", "dbf_workspace_bytes",
            "dbf_linear_forward", "dbf_linear_forward_i8",
-           "lordba_adapter_forward")
+           "lordba_adapter_forward", "dbf_workspace_check")
 
 
 class _CTerm(ctypes.Structure):
@@ -75,6 +77,8 @@ def library() -> ctypes.CDLL:
     lib.lordba_adapter_forward.argtypes = [
         _vp, _i64, ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _i64,
         _i64, _vp, _int, _i64, _vp, _sz, _vp]
+    lib.dbf_workspace_check.restype = _int
+    lib.dbf_workspace_check.argtypes = [_vp, _vp]
     _lib_handle = lib
     return lib
 
@@ -147,6 +151,12 @@ def dbf_packed_bytes(rows: int, k: int) -> int:
 def dbf_workspace_bytes(N: int, M: int, R: int, n_terms: int, T: int,
                         path: int = DBF_PATH_AUTO) -> int:
     return int(library().dbf_workspace_bytes(N, M, R, n_terms, T, path))
+
+
+def dbf_workspace_check(ws: Optional[torch.Tensor], stream=None) -> None:
+    """Raise DbfError(DBF_ESTALLED) if a handoff wait of an earlier call on
+    this workspace gave up (the head is then cleared); waits for the stream."""
+    _check(library().dbf_workspace_check(_ptr(ws), _stream(stream)))
 
 
 def dbf_pack(src: torch.Tensor, out: Optional[torch.Tensor] = None,

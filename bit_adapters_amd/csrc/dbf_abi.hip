@@ -113,6 +113,22 @@ int dbf_abi_version(void) { return DBF_ABI_VERSION; }
 int dbf_layout_version(void) { return DBF_LAYOUT_VERSION; }
 const char* dbf_last_error(void) { return g_err; }
 
+int dbf_workspace_check(void* ws, hipStream_t stream) {
+  if (!ws) return fail(DBF_EINVAL, "workspace is NULL");
+  if (!aligned16(ws)) return fail(DBF_EALIGN, "workspace not 16-byte aligned");
+  // ctr[2] of the handoff head (dbf_lut.h, Sync)
+  unsigned flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, static_cast<unsigned char*>(ws) + 8, sizeof(flag),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DBF_ELAUNCH, "reading the workspace failed: %s", hipGetErrorString(e));
+  if (flag == 0) return DBF_OK;
+  e = hipMemsetAsync(ws, 0, DBF_WS_HEAD_BYTES, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DBF_ELAUNCH, "clearing the workspace failed: %s", hipGetErrorString(e));
+  return fail(DBF_ESTALLED, "a handoff wait gave up; the outputs of the calls since the last check are not valid");
+}
+
 size_t dbf_packed_bytes(int64_t rows, int64_t k) {
   if (rows <= 0 || k <= 0) return 0;
   return static_cast<size_t>(dbf::layout_words(rows, k)) * 4u;

@@ -279,9 +279,11 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
 // memory first (system-scope stores, store_shared), so no L2 writeback of the
 // whole cache is needed; it waits for them, then adds, also at system scope.
 // Consumers poll the counters with loads that bypass the caches (lane l of
-// wave 0 reads counter l), then invalidate their caches (agent-scope
-// acquire) before reading the results.  ctr[0] counts consumers past their
-// wait, ctr[2] is set if a wait gave up.
+// wave 0 reads counter l).  A consumer that reads the results only with
+// load_shared4 needs nothing more; one that reads them with ordinary loads
+// invalidates its caches first (agent-scope acquire).  ctr[0] counts
+// consumers past their wait; ctr[2] is set if a wait gave up (read by
+// dbf_workspace_check).
 struct Sync {
   unsigned* ctr;
   unsigned* slots;

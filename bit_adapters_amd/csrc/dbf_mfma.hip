@@ -21,8 +21,9 @@
 // and B agree.  u and v are stored with each 32 features reordered as pairs
 // (k, k + 16): position 2j holds k = j, position 2j + 1 holds k = j + 16.
 // A lane then builds its B fragment for pairs (k, k + 16) from one 32-bit
-// word of its packed sign row with one shift and one v_and_or_b32 per pair:
-// bits k and k + 16 land on the two fp16 sign bits.  With several terms,
+// word of its packed sign row with one shift and one bit merge per pair
+// (v_and_or_b32 in stage 1, where the magnitude is the constant 1;
+// v_bfi_b32 in stage 2): bits k and k + 16 land on the two fp16 sign bits.  With several terms,
 // stage 2 folds alpha into those values (+-|alpha_n|, exact), so all terms
 // accumulate into the same registers.
 //

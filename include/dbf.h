@@ -55,6 +55,7 @@ extern "C" {
 #define DBF_EDEVICE (-5)      /* current device is not gfx950, or no device */
 #define DBF_EUNSUPPORTED (-6) /* valid but not supported (e.g. int overflow) */
 #define DBF_ELAUNCH (-7)      /* a kernel launch failed */
+#define DBF_ESTALLED (-8)     /* a handoff wait gave up (dbf_workspace_check) */
 
 /* dtype codes */
 #define DBF_F16 1
@@ -64,7 +65,7 @@ extern "C" {
 #define DBF_I32 5
 
 /* execution paths for dbf_linear_forward / dbf_workspace_bytes */
-#define DBF_PATH_AUTO 0   /* chosen by T */
+#define DBF_PATH_AUTO 0   /* chosen by T * n_terms */
 #define DBF_PATH_DECODE 1 /* sign-accumulate over packed bits with 16-entry
                              signed subset-sum tables (fp32 throughout) */
 #define DBF_PATH_MFMA 2   /* +-1 tiles unpacked from the bits into MFMA
@@ -141,6 +142,18 @@ typedef struct dbf_term {
 #define DBF_WS_HEAD_BYTES 16640
 size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
                            int64_t T, int path);
+
+/* Health of a workspace after decode-path or adapter calls.  The consumer
+ * workgroups of those launches wait for the producer workgroups of the same
+ * launch (dispatched first, so the wait always ends); as a safety net a wait
+ * gives up after 2^26 polls (seconds), lets the kernel finish, and sets a
+ * flag in the workspace head.  The output of such a call is not valid.
+ *   ws      device workspace of earlier calls (not NULL, 16-byte aligned)
+ *   stream  the stream those calls ran on; this call waits for it
+ * Returns DBF_OK when no wait gave up.  Otherwise it zeroes the head (so the
+ * buffer is usable again) and returns DBF_ESTALLED.  Reads 4 bytes and
+ * synchronizes the stream, so it is not for use inside graph capture. */
+int dbf_workspace_check(void *ws, hipStream_t stream);
 
 /*
  * y (+)= sum_i Delta W_i x for T tokens.

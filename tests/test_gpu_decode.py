@@ -6,7 +6,7 @@ import torch
 import bit_adapters_amd as D
 import oracle as O
 from bit_adapters_amd import synth as S
-from dbfutil import (DEV, assert_close, device_terms, round_bf16, to_np, x64,
+from dbfutil import (DEV, assert_close, bf16_dev, device_terms, round_bf16, to_np, x64,
                      x_dev)
 
 pytestmark = pytest.mark.gpu
@@ -112,3 +112,28 @@ def test_partial_passes(N, M, R, L, T):
     y = to_np(run(layer, x))
     ref = O.default().forward(O.terms64(layer), x64(x))
     assert_close(y, ref)
+
+
+def test_shared_workspace_head_stays_clear():
+    # one workspace serves decode, MFMA and adapter (published-intermediate
+    # rank path) calls in turn: after each the handoff head is zero again and
+    # no wait gave up
+    N, M, R, L, T = 200, 1000, 64, 2, 5
+    layer, x = S.make_custom(N, M, R, L, T, seed=3, base=True, scale_lo=0.01,
+                             scale_hi=0.05)
+    terms = device_terms(layer)
+    nb = max(D.dbf_workspace_bytes(N, M, R, L, T, p)
+             for p in (D.DBF_PATH_DECODE, D.DBF_PATH_MFMA))
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    o = O.default()
+    ref = o.forward(O.terms64(layer), x64(x))
+    for path in (D.DBF_PATH_DECODE, D.DBF_PATH_MFMA, D.DBF_PATH_DECODE):
+        y = D.dbf_linear_forward(terms, N, M, R, x_dev(x), ws=ws, path=path)
+        D.dbf_workspace_check(ws)
+        assert not ws[:D.DBF_WS_HEAD_BYTES].any()
+        assert_close(to_np(y), ref)
+    w0 = bf16_dev(layer["w0"])
+    y = D.lordba_adapter_forward(w0, terms, N, M, R, x_dev(x), ws=ws)
+    D.dbf_workspace_check(ws)
+    assert not ws[:D.DBF_WS_HEAD_BYTES].any()
+    assert_close(to_np(y), ref + o.dense(O.widen_bf16(layer["w0"]), x64(x)))

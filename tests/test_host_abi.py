@@ -152,6 +152,13 @@ def test_adapter_validation(kw, code):
     assert ad(**kw) == code
 
 
+def test_workspace_check_validation():
+    assert L.dbf_workspace_check(None, None) == D.DBF_EINVAL
+    assert L.dbf_workspace_check(MIS, None) == D.DBF_EALIGN
+    m = re.search(r"#define DBF_WS_HEAD_BYTES (\d+)", open(HEADER).read())
+    assert D.DBF_WS_HEAD_BYTES == int(m.group(1))
+
+
 def test_pack_validation():
     assert L.dbf_pack(FAKE, 9, 4, 4, 4, FAKE, None) == D.DBF_EDTYPE
     assert L.dbf_pack(None, D.DBF_I8, 4, 4, 4, FAKE, None) == D.DBF_EINVAL
