@@ -171,7 +171,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     # the library's automatic choice: decode kernel while T * terms <= 32
     path = "adapter" if base else (
-        {1: "decode", 2: "mfma"}.get(args.path) or ("decode" if T * L <= 32 else "mfma"))
+        {1: "decode", 2: "mfma"}.get(args.path) or ("decode" if T <= 4 or L * ((T + 3) // 4) <= 5 else "mfma"))
     # achieved = algorithmic bytes (flops) per step / HIP-event time per step;
     # decode and adapter steps are one kernel launch each, the MFMA step is
     # three (prep, stage-1 GEMM, stage-2 GEMM) and is rated as a whole

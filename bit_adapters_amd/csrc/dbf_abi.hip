@@ -22,15 +22,17 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
 
-// Decode path up to this many tokens when the caller lets the library pick.
-// DBF_PATH_AUTO: the decode kernel while T * n_terms <= 32 (measured on the
-// 4096 x 4096 R 2048 layer and the three-term 11008 x 4096 layer: below it
-// the decode launch is faster, above it the MFMA products are).
-constexpr int64_t kAutoDecodeMaxWork = 32;
+// DBF_PATH_AUTO: the decode kernel while T <= 4 or n_terms * ceil(T / 4) <= 5,
+// else the MFMA products.  The decode launch's cost grows with the number
+// of (term, 4-token block) pairs, the MFMA path's barely at these sizes;
+// measured on the 4096 x 4096 R 2048 layer (decode faster up to 20 tokens)
+// and the three-term 11008 x 4096 layer (decode faster up to 4 tokens).
+constexpr int64_t kAutoDecodeBlocks = 5;
 
 int resolve_path(int path, int64_t T, int n_terms) {
   if (path != DBF_PATH_AUTO) return path;
-  return T * n_terms <= kAutoDecodeMaxWork ? DBF_PATH_DECODE : DBF_PATH_MFMA;
+  const bool decode = T <= 4 || n_terms * ((T + 3) / 4) <= kAutoDecodeBlocks;
+  return decode ? DBF_PATH_DECODE : DBF_PATH_MFMA;
 }
 
 constexpr int kMaxDevices = 64;

@@ -34,7 +34,11 @@
 // directly (two stages, one step ahead), the A rows XOR-swizzled for
 // conflict-free ds_read_b128 fragments.  Workgroup indices are remapped so
 // that consecutive tiles of one XCD share token rows (L2 reuse).  The tile
-// shape is chosen per launch so that at least ~256 workgroups run.
+// shape is chosen per launch so that at least ~256 workgroups run; with
+// fewer tiles than that (tens of tokens) K is split over the grid's z
+// dimension, each split writes an fp32 partial tile, and reduce1_kernel /
+// reduce2_kernel sum the splits in order and apply the scales.
+#include <algorithm>
 #include <type_traits>
 
 #include "dbf_internal.h"
@@ -179,6 +183,9 @@ struct GemmArgs {
   const _Float16* a;        // A operand [L][T][kp] in pair order
   const float* l1;          // [L][T]
   const float* bmax;        // [L]
+  int nsplit;               // K-splits (grid z); > 1: fp32 partials to `part`
+  float* part;              // [nsplit][terms in grid][T][ldp]
+  int64_t ldp;
   _Float16* v;              // stage-1 output [L][T][vp] in pair order
   int64_t vp;
   void* y;
@@ -283,6 +290,11 @@ gemm_kernel(GemmArgs p) {
   }
 
   const int spt = static_cast<int>(p.kp / BK);  // K steps per term
+  // this workgroup's K-split: steps [lo, hi) of the (term, step) sequence
+  const int split = static_cast<int>(blockIdx.z);
+  const int total = (term_end - term_first) * spt;
+  const int lo = static_cast<int>(static_cast<int64_t>(total) * split / p.nsplit);
+  const int hi = static_cast<int>(static_cast<int64_t>(total) * (split + 1) / p.nsplit);
 
   // this thread's A chunks: LDS chunk q * 256 + tid of a stage is row
   // (q * 256 + tid) / 16, slot tid % 16, and holds logical chunk
@@ -311,7 +323,7 @@ gemm_kernel(GemmArgs p) {
   for (int cb = 0; cb < CB; ++cb) bcol[cb] = col0 + (BN / 4) * wv + 32 * cb + li;
 
   // load cursor: (term, step within the term), advanced one step at a time
-  int lterm = term_first, lks = 0;
+  int lterm = term_first + lo / spt, lks = lo % spt;
   // LDS byte address of the stages (the low 32 bits of the shared-aperture
   // address are the LDS offset)
   const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem_raw));
@@ -360,11 +372,11 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
-  const int nsteps = (term_end - term_first) * spt;
+  const int nsteps = hi - lo;
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
     if (j < nsteps) issue(j);
-  int cterm = term_first, cks = 0;  // compute cursor
+  int cterm = term_first + lo / spt, cks = lo % spt;  // compute cursor
   set_term(cterm);
   for (int step = 0; step < nsteps; ++step) {
     // this step's copies are done once at most (later steps issued) * LPS
@@ -435,14 +447,23 @@ gemm_kernel(GemmArgs p) {
   __syncthreads();  // every wave is done with the stage buffers
   unsigned char* wbuf = smem_raw + wv * (BM * 32 * 4);
   // staged element: fp16 v; y as stored, or fp32 when adding to y (one
-  // rounding of old + new)
-  const int esize = STAGE == 1 ? 2 : ((p.y_dtype == DBF_F32 || p.accumulate) ? 4 : 2);
+  // rounding of old + new); fp32 partial sums when K is split
+  const bool partial = p.nsplit > 1;
+  const int esize = partial ? 4 : (STAGE == 1 ? 2 : ((p.y_dtype == DBF_F32 || p.accumulate) ? 4 : 2));
   const int cpr = 32 * esize / 16;  // 16-byte chunks per staged row
   const bool vec_y = STAGE == 2 && !p.accumulate && (p.ldy * esize) % 16 == 0;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int64_t c0 = col0 + (BN / 4) * wv + 32 * cb;  // first column of the block
-    if constexpr (STAGE == 1) {
+    if (partial) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+          reinterpret_cast<float*>(wbuf)[rl * 32 + li] = acc[rb][cb][r];
+        }
+    } else if constexpr (STAGE == 1) {
       // v = fp16(s_t * beta_r * acc) at the pair-order position of r
       const float bsc = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term_first][bcol[cb]]) : 0.f;
       const int pos = li < 16 ? 2 * li : 2 * (li - 16) + 1;
@@ -475,7 +496,12 @@ gemm_kernel(GemmArgs p) {
       const int64_t tok = tok0 + row;
       if (tok >= p.T) continue;
       const uint4 d = reinterpret_cast<const uint4*>(wbuf)[c];
-      if constexpr (STAGE == 1) {
+      if (partial) {
+        // 4 columns; columns past ncols (up to ldp) are never read
+        const int64_t col = c0 + 4 * ch;
+        const int64_t prow = (static_cast<int64_t>(split) * gridDim.y + blockIdx.y) * p.T + tok;
+        if (col < p.ldp) *reinterpret_cast<uint4*>(p.part + prow * p.ldp + col) = d;
+      } else if constexpr (STAGE == 1) {
         // 8 positions of the 32-position group of this block
         const int64_t pos = c0 + 8 * ch;
         if (pos < p.vp)
@@ -505,17 +531,150 @@ gemm_kernel(GemmArgs p) {
   }
 }
 
-// Tile shape for T tokens and `cols` output columns: the largest of
-// 128 x 256, 128 x 128, 64 x 128 that still gives >= 256 workgroups.
+// ---- K-split reductions ------------------------------------------------
+constexpr int kSplitTarget = 256;  // workgroups a split product aims for
+constexpr int kMaxSplit = 16;
+
+// Stage 1: v_i[t, pos] = fp16(s_t * beta_i[r] * sum_split part[split][i][t][r])
+// for the 8 pair-order positions of one 16-byte chunk (pairs j .. j + 3 of a
+// 32-feature group: r = 32 g + j and 32 g + 16 + j); zero past R.  The
+// splits are added in order, so the result does not depend on timing.
+struct Reduce1Args {
+  const float* part;
+  int64_t ldp, T, R, vp;
+  int L, nsplit;
+  const uint16_t* beta[DBF_MAX_TERMS];
+  const float* l1;
+  const float* bmax;
+  _Float16* v;
+};
+
+__global__ void __launch_bounds__(256) reduce1_kernel(Reduce1Args p) {
+  const int64_t nch = p.vp / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= p.L * p.T * nch) return;
+  const int64_t row = idx / nch;  // term * T + token
+  const int64_t c = idx - row * nch;
+  const int term = static_cast<int>(row / p.T);
+  const int64_t tok = row - static_cast<int64_t>(term) * p.T;
+  float bnd = 0.f;
+  for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
+  const float sc = scale_from_bound(bnd);
+  const int64_t r0[2] = {32 * (c >> 2) + 4 * (c & 3), 32 * (c >> 2) + 16 + 4 * (c & 3)};
+  const int64_t sstride = static_cast<int64_t>(p.L) * p.T * p.ldp;
+  // all splits' loads in flight at once, then the sums in split order
+  float4 q[kMaxSplit][2];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      q[sp][hh] = (sp < p.nsplit && r0[hh] < p.R)
+                      ? *reinterpret_cast<const float4*>(p.part + sp * sstride + row * p.ldp + r0[hh])
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  float sum[2][4] = {};
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      if (sp < p.nsplit) {
+        sum[hh][0] += q[sp][hh].x; sum[hh][1] += q[sp][hh].y;
+        sum[hh][2] += q[sp][hh].z; sum[hh][3] += q[sp][hh].w;
+      }
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    _Float16 hv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int64_t r = r0[hh] + e;
+      hv[hh] = r < p.R ? static_cast<_Float16>(sc * f16_bits_to_f32(p.beta[term][r]) * sum[hh][e])
+                       : static_cast<_Float16>(0.f);
+    }
+    o[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[0])) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[1])) << 16);
+  }
+  *reinterpret_cast<uint4*>(p.v + row * p.vp + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Stage 2: y[t, n] (+)= a_n / s_t * sum_split part[split][t][n], a_n = alpha_n
+// with one term (alpha not folded into the signs), else 1; 4 columns a thread.
+struct Reduce2Args {
+  const float* part;
+  int64_t ldp, T, N;
+  int L, nsplit;
+  const uint16_t* alpha;
+  const float* l1;
+  const float* bmax;
+  void* y;
+  int y_dtype;
+  int64_t ldy;
+  int accumulate;
+};
+
+__global__ void __launch_bounds__(256) reduce2_kernel(Reduce2Args p) {
+  const int64_t nch = (p.N + 3) / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= p.T * nch) return;
+  const int64_t tok = idx / nch;
+  const int64_t n0 = 4 * (idx - tok * nch);
+  float bnd = 0.f;
+  for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
+  const float sc = scale_from_bound(bnd);
+  float4 q[kMaxSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp)
+    q[sp] = sp < p.nsplit ? *reinterpret_cast<const float4*>(p.part + (sp * p.T + tok) * p.ldp + n0)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  float sum[4] = {};
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp)
+    if (sp < p.nsplit) {
+      sum[0] += q[sp].x; sum[1] += q[sp].y; sum[2] += q[sp].z; sum[3] += q[sp].w;
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t n = n0 + e;
+    if (n >= p.N) break;
+    const float a = p.L == 1 ? f16_bits_to_f32(p.alpha[n]) : 1.f;
+    store_out(p.y, p.y_dtype, tok * p.ldy + n, a * sum[e] / sc, p.accumulate);
+  }
+}
+
+// Tile shape and K-split of one product: the largest of 128 x 256,
+// 128 x 128, 64 x 128 that still gives >= 256 workgroups; with fewer tiles
+// than that, K is split (each split >= 2 steps, at most kMaxSplit) towards
+// kSplitTarget workgroups.  (Measured on MI355X for 16 to 256 tokens: a
+// target of 256 beat 512 and 1024; the split partials' traffic grows with
+// the split count.)
+
+struct Tiling {
+  int bm, bn, ntt, ntc, nsplit;
+};
+
+Tiling choose_tiling(int64_t T, int64_t cols, int terms_in_grid, int64_t steps) {
+  auto wgs = [&](int bm, int bn) { return cdiv(T, bm) * cdiv(cols, bn) * terms_in_grid; };
+  Tiling t{128, 256, 0, 0, 1};
+  if (wgs(128, 256) < 256) t.bn = 128;
+  if (wgs(128, 128) < 256) t.bm = 64;
+  t.ntt = static_cast<int>(cdiv(T, t.bm));
+  t.ntc = static_cast<int>(cdiv(cols, t.bn));
+  const int64_t tiles = wgs(t.bm, t.bn);
+  if (tiles < 256) {
+    int64_t sp = cdiv(kSplitTarget, tiles);
+    sp = std::min<int64_t>(sp, steps / 2);
+    sp = std::min<int64_t>(sp, kMaxSplit);
+    t.nsplit = static_cast<int>(std::max<int64_t>(sp, 1));
+  }
+  return t;
+}
+
+
 template <int STAGE, bool KW4>
-hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_t s) {
-  auto wgs = [&](int bm, int bn) { return cdiv(a.T, bm) * cdiv(cols, bn) * terms_in_grid; };
-  int bm = 128, bn = 256;
-  if (wgs(128, 256) < 256) { bn = 128; }
-  if (wgs(128, 128) < 256) { bm = 64; }
-  a.ntt = static_cast<int>(cdiv(a.T, bm));
-  a.ntc = static_cast<int>(cdiv(cols, bn));
-  const dim3 grid(static_cast<unsigned>(a.ntt * a.ntc), terms_in_grid);
+hipError_t launch_tiled(GemmArgs& a, const Tiling& tl, int terms_in_grid, hipStream_t s) {
+  a.ntt = tl.ntt;
+  a.ntc = tl.ntc;
+  a.nsplit = tl.nsplit;
+  const dim3 grid(static_cast<unsigned>(a.ntt * a.ntc), terms_in_grid, tl.nsplit);
   auto go = [&](auto kern, size_t lds) -> hipError_t {
     static bool attr_set = false;  // per instantiation; idempotent if raced
     if (!attr_set) {
@@ -532,37 +691,58 @@ hipError_t launch_tiled(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_
   auto lds_of = [](int bm_, int bn_, int nb_) {
     return static_cast<size_t>(nb_) * (static_cast<size_t>(bm_) * BK * 2 + (KW4 ? bn_ * 16 : 0));
   };
-  if (bm == 128 && bn == 256) return go(gemm_kernel<STAGE, KW4, 128, 256, kStages>, lds_of(128, 256, kStages));
-  if (bm == 128) return go(gemm_kernel<STAGE, KW4, 128, 128, kStages>, lds_of(128, 128, kStages));
+  if (tl.bm == 128 && tl.bn == 256) return go(gemm_kernel<STAGE, KW4, 128, 256, kStages>, lds_of(128, 256, kStages));
+  if (tl.bm == 128) return go(gemm_kernel<STAGE, KW4, 128, 128, kStages>, lds_of(128, 128, kStages));
   return go(gemm_kernel<STAGE, KW4, 64, 128, kStages>, lds_of(64, 128, kStages));
 }
 
 template <int STAGE>
-hipError_t launch_stage(GemmArgs& a, int64_t cols, int terms_in_grid, hipStream_t s) {
-  return a.kw == 4 ? launch_tiled<STAGE, true>(a, cols, terms_in_grid, s)
-                   : launch_tiled<STAGE, false>(a, cols, terms_in_grid, s);
+hipError_t launch_stage(GemmArgs& a, const Tiling& tl, int terms_in_grid, hipStream_t s) {
+  return a.kw == 4 ? launch_tiled<STAGE, true>(a, tl, terms_in_grid, s)
+                   : launch_tiled<STAGE, false>(a, tl, terms_in_grid, s);
+}
+
+int64_t round4(int64_t n) { return (n + 3) / 4 * 4; }
+
+// The two products' tilings (stage 1: R columns, one term per grid row,
+// kpad(M) / BK steps; stage 2: N columns, all terms, L kpad(R) / BK steps).
+struct Plan {
+  Tiling t1, t2;
+};
+
+Plan make_plan(int64_t N, int64_t M, int64_t R, int L, int64_t T) {
+  Plan pl;
+  pl.t1 = choose_tiling(T, R, L, kpad(M) / BK);
+  pl.t2 = choose_tiling(T, N, 1, L * (kpad(R) / BK));
+  return pl;
 }
 
 struct WsLayout {
-  size_t u, v, l1, bmax, total;
+  size_t u, v, l1, bmax, part, total;
 };
 
-WsLayout ws_layout(int64_t M, int64_t R, int L, int64_t T) {
+WsLayout ws_layout(int64_t N, int64_t M, int64_t R, int L, int64_t T) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  const Plan pl = make_plan(N, M, R, L, T);
   WsLayout w{};
   size_t off = kWsHeadBytes;
   w.u = off; off += al(static_cast<size_t>(L) * T * kpad(M) * 2);
   w.v = off; off += al(static_cast<size_t>(L) * T * kpad(R) * 2);
   w.l1 = off; off += al(static_cast<size_t>(L) * T * 4);
   w.bmax = off; off += al(static_cast<size_t>(L) * 4);
+  // split partials: stage 1's are consumed before stage 2 writes its own
+  size_t part = 0;
+  if (pl.t1.nsplit > 1) part = static_cast<size_t>(pl.t1.nsplit) * L * T * round4(R) * 4;
+  if (pl.t2.nsplit > 1) part = std::max(part, static_cast<size_t>(pl.t2.nsplit) * T * round4(N) * 4);
+  w.part = off; off += al(part);
   w.total = off;
   return w;
 }
 
 }  // namespace
 
-size_t mfma_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t T) {
-  return ws_layout(M, R, n_terms, T).total;
+size_t mfma_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T) {
+  return ws_layout(N, M, R, n_terms, T).total;
 }
 
 hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
@@ -570,7 +750,9 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                        void* y, int y_dtype, int64_t ldy, int accumulate,
                        void* ws, hipStream_t s) {
   unsigned char* base = static_cast<unsigned char*>(ws);
-  const WsLayout lay = ws_layout(M, R, t.n, T);
+  const WsLayout lay = ws_layout(N, M, R, t.n, T);
+  const Plan pl = make_plan(N, M, R, t.n, T);
+  float* part = reinterpret_cast<float*>(base + lay.part);
   _Float16* u = reinterpret_cast<_Float16*>(base + lay.u);
   _Float16* v = reinterpret_cast<_Float16*>(base + lay.v);
   float* l1 = reinterpret_cast<float*>(base + lay.l1);
@@ -598,8 +780,19 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
     a.colscale[i] = t.beta[i];
   }
   a.a = u; a.l1 = l1; a.bmax = bmax; a.v = v; a.vp = kpad(R);
-  e = launch_stage<1>(a, R, t.n, s);
+  a.part = part; a.ldp = round4(R);
+  e = launch_stage<1>(a, pl.t1, t.n, s);
   if (e != hipSuccess) return e;
+  if (pl.t1.nsplit > 1) {
+    Reduce1Args r{};
+    r.part = part; r.ldp = a.ldp; r.T = T; r.R = R; r.vp = a.vp; r.L = t.n;
+    r.nsplit = pl.t1.nsplit; r.l1 = l1; r.bmax = bmax; r.v = v;
+    for (int i = 0; i < t.n; ++i) r.beta[i] = t.beta[i];
+    const int64_t n = t.n * T * (a.vp / 8);
+    reduce1_kernel<<<dim3(static_cast<unsigned>(cdiv(n, 256))), 256, 0, s>>>(r);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   GemmArgs b = a;
   b.stage = 2; b.K = R; b.kp = kpad(R); b.ncols = N;
@@ -610,7 +803,15 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   }
   b.a = v;
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
-  return launch_stage<2>(b, N, 1, s);
+  b.ldp = round4(N);
+  e = launch_stage<2>(b, pl.t2, 1, s);
+  if (e != hipSuccess || pl.t2.nsplit == 1) return e;
+  Reduce2Args r{};
+  r.part = part; r.ldp = b.ldp; r.T = T; r.N = N; r.L = t.n; r.nsplit = pl.t2.nsplit;
+  r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax;
+  r.y = y; r.y_dtype = y_dtype; r.ldy = ldy; r.accumulate = accumulate;
+  reduce2_kernel<<<dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), 256, 0, s>>>(r);
+  return hipGetLastError();
 }
 
 }  // namespace dbf

@@ -65,7 +65,7 @@ extern "C" {
 #define DBF_I32 5
 
 /* execution paths for dbf_linear_forward / dbf_workspace_bytes */
-#define DBF_PATH_AUTO 0   /* chosen by T * n_terms */
+#define DBF_PATH_AUTO 0   /* chosen by T and n_terms */
 #define DBF_PATH_DECODE 1 /* sign-accumulate over packed bits with 16-entry
                              signed subset-sum tables (fp32 throughout) */
 #define DBF_PATH_MFMA 2   /* +-1 tiles unpacked from the bits into MFMA
@@ -167,9 +167,10 @@ int dbf_workspace_check(void *ws, hipStream_t stream);
  *   y                [T x N], y_dtype DBF_F32, DBF_BF16 or DBF_F16, ldy.
  *   accumulate       0: y = result; 1: y = y + result (in fp32).
  *   ws, ws_bytes     workspace of dbf_workspace_bytes(..., path) bytes.
- *   path             DBF_PATH_AUTO picks the decode path while
- *                    T * n_terms <= 32 and the MFMA path above; the others
- *                    force one (both are correct for every T >= 1).
+ *   path             DBF_PATH_AUTO picks the decode path while T <= 4 or
+ *                    n_terms * ceil(T / 4) <= 5, and the MFMA path above;
+ *                    the others force one (both are correct for every
+ *                    T >= 1).
  * Accumulation is fp32; the decode path keeps every intermediate in fp32,
  * the MFMA path rounds gamma*x and the scaled rank-R intermediate to fp16
  * (with an exact power-of-two scale per token).

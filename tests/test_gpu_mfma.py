@@ -123,3 +123,40 @@ def test_first_row_block_small_rank(R, seed):
     y = to_np(run(layer, x))
     ref = O.default().forward(O.terms64(layer), x64(x))
     assert_close(y, ref)
+
+
+# Few output tiles: K is split across workgroups and the fp32 partials are
+# summed in split order by a reduction kernel.  (300, 2000, 601, 3, 40):
+# stage 2 has 3 x 5 steps over 7 splits, so splits straddle term boundaries;
+# R and N not multiples of 4; (4096, 4096, 2048, 1, 33): 16 splits in stage 1.
+SPLIT = [(300, 2000, 601, 3, 40), (1000, 4096, 2048, 1, 64), (4096, 4096, 2048, 1, 33),
+         (701, 3000, 301, 2, 9), (130, 8192, 1030, 1, 2)]
+
+
+@pytest.mark.parametrize("N,M,R,L,T", SPLIT)
+def test_split_k(N, M, R, L, T):
+    print("mfma split", N, M, R, L, T, flush=True)
+    layer, x = S.make_custom(N, M, R, L, T, seed=N + 7 * R + L)
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    a = to_np(run(layer, x))
+    assert_close(a, ref)
+    assert np.array_equal(a, to_np(run(layer, x)))
+
+
+def test_split_k_output_dtypes_accumulate_strides():
+    N, M, R, L, T = 301, 3000, 300, 2, 20
+    layer, x = S.make_custom(N, M, R, L, T, seed=5)
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    terms = device_terms(layer)
+    big = torch.full((T, 320), 7.0, dtype=torch.float32, device=DEV)
+    base = torch.randn((T, N), dtype=torch.float32, device=DEV)
+    big[:, :N] = base
+    D.dbf_linear_forward(terms, N, M, R, x_dev(x), y=big[:, :N], accumulate=True, path=MF)
+    torch.cuda.synchronize()
+    assert_close(to_np(big[:, :N]), ref + to_np(base))
+    assert torch.all(big[:, N:] == 7.0)
+    yb = torch.full((T, 310), 3.0, dtype=torch.bfloat16, device=DEV)
+    D.dbf_linear_forward(terms, N, M, R, x_dev(x), y=yb[:, :N], path=MF)
+    torch.cuda.synchronize()
+    assert_close(to_np(yb[:, :N]), round_bf16(ref), rel_l2=4e-3)
+    assert torch.all(yb[:, N:] == 3.0)

@@ -55,10 +55,13 @@ def test_workspace_bytes():
     assert D.dbf_workspace_bytes(512, 512, 256, 1, 1, D.DBF_PATH_MFMA) > 0
 
 
-@pytest.mark.parametrize("T,L,path", [(1, 1, "decode"), (32, 1, "decode"), (33, 1, "mfma"),
-                                      (10, 3, "decode"), (11, 3, "mfma"), (4096, 1, "mfma")])
+@pytest.mark.parametrize("T,L,path", [(1, 1, "decode"), (20, 1, "decode"), (21, 1, "mfma"),
+                                      (4, 3, "decode"), (5, 3, "mfma"), (8, 2, "decode"),
+                                      (9, 2, "mfma"), (1, 8, "decode"), (4, 8, "decode"),
+                                      (5, 8, "mfma"), (4096, 1, "mfma")])
 def test_auto_path_rule(T, L, path):
-    # automatic choice: the decode kernel while T * n_terms <= 32
+    # automatic choice: the decode kernel while T <= 4 or
+    # n_terms * ceil(T / 4) <= 5
     want = D.DBF_PATH_DECODE if path == "decode" else D.DBF_PATH_MFMA
     auto = D.dbf_workspace_bytes(4096, 4096, 2048, L, T, D.DBF_PATH_AUTO)
     assert auto == D.dbf_workspace_bytes(4096, 4096, 2048, L, T, want)
