@@ -23,6 +23,7 @@ import numpy as np
 TENSOR_X, TENSOR_W0, TENSOR_B1, TENSOR_B2 = 0, 1, 2, 3
 TENSOR_ALPHA, TENSOR_BETA, TENSOR_GAMMA, TENSOR_XI8 = 4, 5, 6, 7
 TENSOR_SIGNS_GENERIC = 8
+TENSOR_WBOOL, TENSOR_SIN, TENSOR_SOUT = 9, 10, 11
 
 # Shapes: N output features, M input features, R inner rank, L terms, and the
 # token counts each configuration is run at.
@@ -39,6 +40,21 @@ CONFIGS = {
             lo=0.5, hi=1.5, x="bf16"),
     5: dict(name="dbf-8192-r6144", N=8192, M=8192, R=6144, L=1, T=(4096,),
             scales="absnormal", x="bf16"),
+}
+
+
+# Boolean-kernel layers of the Multi-Boolean form: K full N x M sign matrices,
+# each with a rank-one pair of fp16 scales (s_out [N], s_in [M]).  The
+# shapes are the Llama-7B 4096 x 4096 projection with K = 2 and the
+# 11008 x 4096 MLP up-projection with K = 3 (the page finds 2 to 4 kernels
+# enough).  The scales stand in for a successive SVID of an N(0, 0.02^2)
+# weight: near 0.12 on each side of the first kernel (sqrt of E|W| = 0.016),
+# each later kernel x0.6, with +-20% spread, positive (a leading singular
+# pair of a nonnegative matrix).
+BOOL_CONFIGS = {
+    6: dict(name="mbok-svid-4096-k2", N=4096, M=4096, K=2, T=(1, 4, 16, 256), x="bf16"),
+    7: dict(name="mbok-svid-11008x4096-k3", N=11008, M=4096, K=3, T=(1, 8, 64),
+            x="bf16"),
 }
 
 
@@ -106,7 +122,7 @@ def make_x(config: int, T: int, kind: str | None = None) -> np.ndarray:
     """Activations [T x M]: bf16 bit patterns (uint16), fp16, or int8 in
     [-127, 127].  Drawn for the largest T of the configuration, sliced by
     prefix."""
-    cfg = CONFIGS[config]
+    cfg = CONFIGS[config] if config in CONFIGS else BOOL_CONFIGS[config]
     M = cfg["M"]
     kind = kind or cfg["x"]
     tmax = max(max(cfg["T"]), T)
@@ -120,6 +136,36 @@ def make_x(config: int, T: int, kind: str | None = None) -> np.ndarray:
     if kind == "bf16":
         return f32_to_bf16_bits(v)
     raise ValueError(kind)
+
+
+def _bool_scale(g: np.random.Generator, k: int, n: int) -> np.ndarray:
+    return (0.12 * 0.6 ** k * g.uniform(0.8, 1.2, n)).astype(np.float16)
+
+
+def make_bool_layer(config: int) -> dict:
+    """Boolean kernels of a configuration: int8 signs w [N x M] and fp16
+    scales s_in [M], s_out [N] per kernel."""
+    cfg = BOOL_CONFIGS[config]
+    N, M = cfg["N"], cfg["M"]
+    kernels = [dict(w=signs(rng(config, TENSOR_WBOOL, k), (N, M)),
+                    s_in=_bool_scale(rng(config, TENSOR_SIN, k), k, M),
+                    s_out=_bool_scale(rng(config, TENSOR_SOUT, k), k, N))
+               for k in range(cfg["K"])]
+    return dict(config=config, N=N, M=M, kernels=kernels)
+
+
+def make_custom_bool(N: int, M: int, K: int, T: int, seed: int,
+                     x_kind: str = "bf16") -> tuple[dict, np.ndarray]:
+    """Boolean kernels and activations of arbitrary shape (edge cases)."""
+    kernels = []
+    for k in range(K):
+        g = np.random.default_rng([0xDBF, 103, seed, k, N, M])
+        kernels.append(dict(w=signs(g, (N, M)), s_in=_bool_scale(g, k, M),
+                            s_out=_bool_scale(g, k, N)))
+    g = np.random.default_rng([0xDBF, 104, seed, N, M, T])
+    v = g.standard_normal((T, M), dtype=np.float32)
+    x = v.astype(np.float16) if x_kind == "f16" else f32_to_bf16_bits(v)
+    return dict(config=0, N=N, M=M, kernels=kernels), x
 
 
 def make_custom(N: int, M: int, R: int, L: int, T: int, seed: int,

@@ -16,6 +16,11 @@ order); this module only widens the stored types to fp64 and calls it:
 * ``dense``     -- the frozen base W0 x of LoRDBA's unmerged adapter mode
   (LoRDBA sections 1 and 5);
 * ``forward_int`` -- exact integer sign sums for int8 activations;
+* ``bool_forward`` -- the Multi-Boolean form itself (technical summary,
+  section 2, items 1 and 2): y = sum_k s_out_k . (Wb_k (s_in_k . x)), each
+  kernel a full N x M sign matrix with a rank-one scale;
+* ``svid_extract`` -- successive SVID of a real matrix into such kernels
+  (same section, items 1 and 3), in numpy;
 * ``pack`` / ``unpack`` -- the uint32 bit layout written out from its
   definition, one bit at a time.
 
@@ -77,6 +82,10 @@ class Oracle:
         lib.dbf_oracle_pack.argtypes = [_dp, _i64, _i64, _u32p]
         lib.dbf_oracle_unpack.restype = None
         lib.dbf_oracle_unpack.argtypes = [_u32p, _i64, _i64, _i8p]
+        lib.dbf_oracle_bool_forward.restype = ctypes.c_int
+        lib.dbf_oracle_bool_forward.argtypes = [
+            ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(_i8p),
+            ctypes.POINTER(_dp), ctypes.POINTER(_dp), _dp, _dp]
         lib.dbf_oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -153,6 +162,30 @@ class Oracle:
                                         s2.ctypes.data_as(_i64p))
         return s1, s2
 
+    def bool_forward(self, kernels, x) -> np.ndarray:
+        """y [T x N] in fp64 for fp64 activations x [T x M] and a list of
+        boolean kernels (dicts with int8 w [N x M] and s_in [M], s_out [N]
+        convertible to fp64)."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        T, M = x.shape
+        K = len(kernels)
+        N = kernels[0]["w"].shape[0]
+        w = [np.ascontiguousarray(k["w"], dtype=np.int8) for k in kernels]
+        si = [np.ascontiguousarray(k["s_in"], dtype=np.float64) for k in kernels]
+        so = [np.ascontiguousarray(k["s_out"], dtype=np.float64) for k in kernels]
+        for a, b, c in zip(w, si, so):
+            assert a.shape == (N, M) and b.shape == (M,) and c.shape == (N,)
+        y = np.empty((T, N), dtype=np.float64)
+        W = (_i8p * K)(*[a.ctypes.data_as(_i8p) for a in w])
+        SI = (_dp * K)(*[a.ctypes.data_as(_dp) for a in si])
+        SO = (_dp * K)(*[a.ctypes.data_as(_dp) for a in so])
+        rc = self.lib.dbf_oracle_bool_forward(K, N, M, T, W, SI, SO,
+                                              x.ctypes.data_as(_dp),
+                                              y.ctypes.data_as(_dp))
+        if rc != 0:
+            raise MemoryError("oracle scratch allocation failed")
+        return y
+
     # -- the bit layout -------------------------------------------------
     def packed_words(self, rows: int, K: int) -> int:
         return int(self.lib.dbf_oracle_packed_words(rows, K))
@@ -176,6 +209,40 @@ class Oracle:
 
     def threads(self) -> int:
         return int(self.lib.dbf_oracle_threads())
+
+
+# -- successive SVID (numpy) ---------------------------------------------
+def svid_extract(w, n_kernels: int, round_fp16: bool = True) -> list:
+    """Successive sign-value-independent decomposition of a real N x M
+    matrix into boolean kernels, as the Multi-Boolean page describes it
+    (technical summary, section 2): item 1, Wb = sign(W) and a rank-one fit
+    W ~ Wb . (s_out s_in^T); item 3, each later kernel is extracted the same
+    way from the residual the earlier ones leave.
+
+    Readings where the page is silent: sign(0) is +1 (the bit rule of the
+    packed layout); the rank-one fit of |W| is its leading singular pair
+    (sigma, u, v), taken with the nonnegative sign (|W| is nonnegative, so
+    such a pair exists) and split evenly, s_out = sqrt(sigma) u and
+    s_in = sqrt(sigma) v; the scales are rounded to fp16 (their storage
+    type) before the residual is formed, so later kernels absorb that
+    rounding.  Returns [dict(w=int8 [N x M], s_in=fp16 [M], s_out=fp16 [N])].
+    """
+    r = np.array(w, dtype=np.float64)
+    out = []
+    for _ in range(n_kernels):
+        wb = np.where(r >= 0, 1, -1).astype(np.int8)
+        u, sv, vt = np.linalg.svd(np.abs(r), full_matrices=False)
+        lu, lv = u[:, 0], vt[0]
+        if lu.sum() + lv.sum() < 0:
+            lu, lv = -lu, -lv
+        s_out = np.sqrt(sv[0]) * lu
+        s_in = np.sqrt(sv[0]) * lv
+        if round_fp16:
+            s_out = s_out.astype(np.float16)
+            s_in = s_in.astype(np.float16)
+        r = r - wb * np.outer(np.asarray(s_out, np.float64), np.asarray(s_in, np.float64))
+        out.append(dict(w=wb, s_in=s_in, s_out=s_out))
+    return out
 
 
 # -- widening of the stored types to fp64 (exact) ------------------------

@@ -24,6 +24,9 @@
  *     boolean kernels, which is the L > 1 sum.
  *   - LoRDBA section 1 and 5: the adapter stays unmerged beside a frozen
  *     base weight W0, so the adapter-mode output is W0 x + Delta W x.
+ *   - Multi-Boolean page, section 2, items 1 and 2, read as written: each
+ *     boolean kernel is sign(W) with a rank-one scale s_out s_in^T, and the
+ *     weight is the sum of several such kernels (dbf_oracle_bool_forward).
  *
  * Signs are passed unpacked, as int8 +-1 (any value > 0 is +1), so nothing
  * here depends on a bit layout.  Each inner product is a plain sequential
@@ -109,6 +112,45 @@ int dbf_oracle_forward(int L, int64_t N, int64_t M, int64_t R, int64_t T,
     }
     free(u);
     free(v);
+    return 0;
+}
+
+/* The Multi-Boolean form ("Highly Efficient and Effective LLMs with
+ * Multi-Boolean Architectures", technical summary, section 2, items 1 and
+ * 2): kernel k is a sign matrix Wb_k in {+-1}^{N x M} carrying the rank-one
+ * scale s_out_k s_in_k^T, the weight is sum_k Wb_k . (s_out_k s_in_k^T), so
+ *   y[t][n] = sum_k s_out_k[n] * sum_m Wb_k[n,m] * (s_in_k[m] * x[t][m]).
+ * wb[k]: N x M row-major, s_in[k]: M, s_out[k]: N, x: T x M; y (T x N) is
+ * overwritten.  Returns 0, or -1 if scratch cannot be had. */
+int dbf_oracle_bool_forward(int K, int64_t N, int64_t M, int64_t T,
+                            const int8_t *const *wb, const double *const *s_in,
+                            const double *const *s_out, const double *x, double *y)
+{
+    double *xs = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    int64_t t, n, m;
+    int k;
+    if (!xs)
+        return -1;
+    for (t = 0; t < T; ++t) {
+        double *yt = y + t * N;
+        for (n = 0; n < N; ++n)
+            yt[n] = 0.0;
+        for (k = 0; k < K; ++k) {
+            /* diag(s_in) x */
+            for (m = 0; m < M; ++m)
+                xs[m] = s_in[k][m] * x[t * M + m];
+            /* the boolean kernel: a +-add over the inputs, then diag(s_out) */
+#pragma omp parallel for schedule(static)
+            for (int64_t o = 0; o < N; ++o) {
+                const int8_t *wrow = wb[k] + o * M;
+                double acc = 0.0;
+                for (int64_t q = 0; q < M; ++q)
+                    acc += (wrow[q] > 0) ? xs[q] : -xs[q];
+                yt[o] += s_out[k][o] * acc;
+            }
+        }
+    }
+    free(xs);
     return 0;
 }
 

@@ -308,10 +308,74 @@ def pin_pack_counts(o):
     assert np.array_equal(o.unpack(o.pack(v), 1, 7), [[1, 1, -1, -1, 1, -1, 1]])
 
 
+def _rand_bool(N, M, K, seed, integer=False):
+    g = np.random.default_rng([9, seed, N, M, K])
+    ks = []
+    for _ in range(K):
+        w = (g.integers(0, 2, (N, M)) * 2 - 1).astype(np.int8)
+        if integer:
+            si = g.integers(1, 4, M).astype(np.float64)
+            so = g.integers(1, 4, N).astype(np.float64)
+        else:
+            si = g.uniform(0.5, 1.5, M).astype(np.float16).astype(np.float64)
+            so = g.uniform(0.5, 1.5, N).astype(np.float16).astype(np.float64)
+        ks.append(dict(w=w, s_in=si, s_out=so))
+    return ks
+
+
+def _bool_dense(ks):
+    # the Multi-Boolean weight, sum_k Wb_k . (s_out_k s_in_k^T), with numpy
+    return sum(k["w"] * np.outer(k["s_out"], k["s_in"]) for k in ks)
+
+
+def pin_bool_bruteforce(o):
+    ks = _rand_bool(37, 53, 3, 1)
+    x = _rand_x(4, 53, 1)
+    ref = x @ _bool_dense(ks).T
+    y = o.bool_forward(ks, x)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # small integers: both sides are exact
+    ks = _rand_bool(29, 41, 2, 2, integer=True)
+    x = _rand_x(3, 41, 2, integer=True)
+    assert np.array_equal(o.bool_forward(ks, x), x @ _bool_dense(ks).T)
+
+
+def pin_bool_all_ones(o):
+    # all signs +1: y[t, n] = sum_k s_out_k[n] (s_in_k . x[t])
+    ks = _rand_bool(20, 30, 2, 3)
+    for k in ks:
+        k["w"][:] = 1
+    x = _rand_x(2, 30, 3)
+    ref = sum(np.outer(x @ k["s_in"], k["s_out"]) for k in ks)
+    assert np.allclose(o.bool_forward(ks, x), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_bool_row_flip(o):
+    # flipping row 5 of one kernel's signs negates that kernel's output 5
+    # and leaves every other output of the sum unchanged, exactly
+    ks = _rand_bool(16, 24, 2, 4)
+    x = _rand_x(3, 24, 4)
+    flipped = [ks[0], dict(ks[1], w=ks[1]["w"].copy())]
+    flipped[1]["w"][5] *= -1
+    y, y1 = o.bool_forward(ks, x), o.bool_forward(flipped, x)
+    rest = [n for n in range(16) if n != 5]
+    assert np.array_equal(y1[:, rest], y[:, rest])
+    assert np.array_equal(o.bool_forward(flipped[1:], x)[:, 5],
+                          -o.bool_forward(ks[1:], x)[:, 5])
+
+
+def pin_bool_additivity(o):
+    ks = _rand_bool(18, 26, 3, 5, integer=True)
+    x = _rand_x(2, 26, 5, integer=True)
+    parts = sum(o.bool_forward([k], x) for k in ks)
+    assert np.array_equal(o.bool_forward(ks, x), parts)
+
+
 PINS = [pin_bruteforce_real, pin_bruteforce_exact, pin_dbf_hadamard_form,
         pin_all_ones, pin_rank_one, pin_row_flip, pin_gauge, pin_column_flip,
         pin_permutation, pin_homogeneity, pin_additivity, pin_int_bigint,
-        pin_int_all_ones, pin_dense, pin_pack_golden, pin_pack_counts]
+        pin_int_all_ones, pin_dense, pin_pack_golden, pin_pack_counts,
+        pin_bool_bruteforce, pin_bool_all_ones, pin_bool_row_flip, pin_bool_additivity]
 
 
 @pytest.fixture(scope="module")
@@ -373,6 +437,14 @@ MUTANTS = [
     ("tile column-major", "return tile * 64 * kw + (r % 64) * kw + w;",
      "return tile * 64 * kw + w * 64 + (r % 64);"),
     ("unpack inverted", "& 1u) ? 1 : -1;", "& 1u) ? -1 : 1;"),
+    ("bool s_in dropped", "xs[m] = s_in[k][m] * x[t * M + m];", "xs[m] = x[t * M + m];"),
+    ("bool s_out dropped", "yt[o] += s_out[k][o] * acc;", "yt[o] += acc;"),
+    ("bool sign", "acc += (wrow[q] > 0) ? xs[q] : -xs[q];",
+     "acc += (wrow[q] > 0) ? xs[q] : xs[q];"),
+    ("bool read transposed", "acc += (wrow[q] > 0) ? xs[q] : -xs[q];",
+     "acc += (wb[k][q * N + o] > 0) ? xs[q] : -xs[q];"),
+    ("bool kernels overwrite", "yt[o] += s_out[k][o] * acc;", "yt[o] = s_out[k][o] * acc;"),
+    ("bool last kernel dropped", "for (k = 0; k < K; ++k)", "for (k = 0; k + 1 < K; ++k)"),
 ]
 
 
@@ -395,3 +467,57 @@ def test_mutants_are_caught():
                     failed.append(pin.__name__)
             assert failed, "planted mistake not caught: " + desc
     assert shutil.which("gcc")
+
+
+# -- successive SVID (Multi-Boolean page, technical summary, section 2) ----
+def test_svid_recovers_rank_one_scaled_signs():
+    # W = S . (a b^T) with a, b > 0: one kernel recovers S and a b^T
+    g = np.random.default_rng(41)
+    S = (g.integers(0, 2, (24, 40)) * 2 - 1).astype(np.int8)
+    a, b = g.uniform(0.5, 2.0, 24), g.uniform(0.5, 2.0, 40)
+    W = S * np.outer(a, b)
+    k = O.svid_extract(W, 1, round_fp16=False)[0]
+    assert np.array_equal(k["w"], S)
+    assert np.allclose(np.outer(k["s_out"], k["s_in"]), np.outer(a, b), rtol=1e-12)
+    # the fp16 storage of the scales costs at most their rounding
+    k = O.svid_extract(W, 1)[0]
+    assert k["s_in"].dtype == np.float16 and k["s_out"].dtype == np.float16
+    assert np.array_equal(k["w"], S)
+    rel = np.abs(np.outer(k["s_out"].astype(np.float64), k["s_in"].astype(np.float64))
+                 / np.outer(a, b) - 1)
+    assert rel.max() <= 2.0 ** -10
+
+
+def test_svid_residual_is_the_eckart_young_tail():
+    # |W - Wb . P| = ||W| - P| elementwise (|Wb| = 1), and the best rank-one
+    # P leaves the sum of the other squared singular values of |W|
+    g = np.random.default_rng(42)
+    W = g.standard_normal((30, 50))
+    k = O.svid_extract(W, 1, round_fp16=False)[0]
+    assert np.array_equal(k["w"], np.where(W >= 0, 1, -1))
+    res = W - k["w"] * np.outer(k["s_out"], k["s_in"])
+    sv = np.linalg.svd(np.abs(W), compute_uv=False)
+    assert np.isclose(np.sum(res ** 2), np.sum(sv[1:] ** 2), rtol=1e-10)
+    # the even split: s_out and s_in carry the same norm
+    assert np.isclose(np.linalg.norm(k["s_out"]), np.linalg.norm(k["s_in"]), rtol=1e-12)
+
+
+def test_svid_successive_kernels():
+    g = np.random.default_rng(43)
+    W = g.standard_normal((40, 64)) * 0.02
+    ks = O.svid_extract(W, 4)
+    r = W.copy()
+    x = g.standard_normal((3, 64))
+    o = O.default()
+    prev_err = np.linalg.norm(x @ W.T)
+    for i, k in enumerate(ks):
+        # each kernel takes the signs of what the earlier ones left
+        assert np.array_equal(k["w"], np.where(r >= 0, 1, -1))
+        assert np.all(k["s_in"] >= 0) and np.all(k["s_out"] >= 0)
+        nxt = r - k["w"] * np.outer(k["s_out"].astype(np.float64), k["s_in"].astype(np.float64))
+        assert np.linalg.norm(nxt) < np.linalg.norm(r)
+        r = nxt
+        # and the forward of the first i + 1 kernels approaches W x
+        err = np.linalg.norm(o.bool_forward(ks[:i + 1], x) - x @ W.T)
+        assert err < prev_err
+        prev_err = err
