@@ -14,7 +14,9 @@ output is checked against an eager call and against the fp64 oracle.
 
 Other workloads: --config 3 --rank {16,64} (LoRDBA adapter on a bf16 base),
 --config 4 (three-term layer), --config 5 (8192 x 8192, R = 6144, 4096
-tokens), with --tokens T.
+tokens), --config 6 / 7 (the Multi-Boolean form, dbf_bool_forward: two
+4096 x 4096 or three 11008 x 4096 sign kernels with rank-one scales), with
+--tokens T.
 """
 from __future__ import annotations
 
@@ -83,6 +85,18 @@ def algorithmic(cfg, N, M, R, L, T, base):
     return signs + scales + xy + w0, flops
 
 
+def algorithmic_bool(N, M, K, T):
+    """The same for K boolean kernels: N x M signs at one bit, s_in and s_out
+    in fp16, bf16 x and y; one sign-accumulate product per kernel."""
+    return K * N * M / 8.0 + 2.0 * K * (N + M) + 2.0 * T * (M + N), 2.0 * T * N * M * K
+
+
+def auto_path(T, L, blocks=5):
+    # the library's automatic choice (dbf_abi.hip, resolve_path); the boolean
+    # kernels switch to the MFMA path one 4-token block earlier
+    return "decode" if T <= 4 or L * ((T + 3) // 4) <= blocks else "mfma"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,21 +118,31 @@ def main():
               "across GPUs in this library", file=sys.stderr)
         sys.exit(2)
 
-    cfgd = S.CONFIGS[args.config]
+    boolk = args.config in S.BOOL_CONFIGS
+    cfgd = S.BOOL_CONFIGS[args.config] if boolk else S.CONFIGS[args.config]
     T = args.tokens if args.tokens is not None else min(cfgd["T"])
     base = bool(cfgd.get("base"))
-    layer = S.make_layer(args.config, R=args.rank if base else None)
-    N, M, R, L = layer["N"], layer["M"], layer["R"], len(layer["terms"])
     x_np = S.make_x(args.config, T)
     x = dev_x(x_np)
 
     # one packed copy, then clones for rotation
     terms0 = []
-    for t in layer["terms"]:
-        terms0.append(D.DbfTerm(
-            D.dbf_pack(torch.from_numpy(t["b1"]).to(DEV)),
-            D.dbf_pack(torch.from_numpy(t["b2"]).to(DEV)),
-            dev_f16(t["alpha"]), dev_f16(t["beta"]), dev_f16(t["gamma"])))
+    if boolk:
+        layer = S.make_bool_layer(args.config)
+        N, M, L = layer["N"], layer["M"], len(layer["kernels"])
+        R = None
+        for k in layer["kernels"]:
+            terms0.append(D.DbfBoolKernel(D.dbf_pack(torch.from_numpy(k["w"]).to(DEV)),
+                                          dev_f16(k["s_in"]), dev_f16(k["s_out"])))
+    else:
+        layer = S.make_layer(args.config, R=args.rank if base else None)
+        N, M, R, L = layer["N"], layer["M"], layer["R"], len(layer["terms"])
+        for t in layer["terms"]:
+            terms0.append(D.DbfTerm(
+                D.dbf_pack(torch.from_numpy(t["b1"]).to(DEV)),
+                D.dbf_pack(torch.from_numpy(t["b2"]).to(DEV)),
+                dev_f16(t["alpha"]), dev_f16(t["beta"]), dev_f16(t["gamma"])))
+    tcls = type(terms0[0])
     w0 = dev_bf16(layer["w0"]) if base else None
     copy_bytes = sum(sum(v.numel() * v.element_size() for v in t) for t in terms0)
     if base:
@@ -126,11 +150,13 @@ def main():
     ncopies = max(1, min(int(math.ceil(args.rotate_gib * 2 ** 30 / copy_bytes)), 4096))
     copies = [(terms0, w0)]
     for _ in range(ncopies - 1):
-        copies.append(([D.DbfTerm(*[v.clone() for v in t]) for t in terms0],
+        copies.append(([tcls(*[v.clone() for v in t]) for t in terms0],
                        w0.clone() if base else None))
 
     y = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
-    if base:
+    if boolk:
+        nws = D.dbf_bool_workspace_bytes(N, M, L, T, args.path)
+    elif base:
         nws = D.dbf_workspace_bytes(N, M, R, L, T, D.DBF_PATH_DECODE)
     else:
         nws = D.dbf_workspace_bytes(N, M, R, L, T, args.path)
@@ -138,7 +164,9 @@ def main():
 
     def step(i):
         terms, w = copies[i % ncopies]
-        if base:
+        if boolk:
+            D.dbf_bool_forward(terms, N, M, x, y=y, ws=ws, path=args.path)
+        elif base:
             D.lordba_adapter_forward(w, terms, N, M, R, x, y=y, ws=ws)
         else:
             D.dbf_linear_forward(terms, N, M, R, x, y=y, ws=ws, path=args.path)
@@ -165,13 +193,15 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    bytes_alg, flops = algorithmic(args.config, N, M, R, L, T, base)
+    if boolk:
+        bytes_alg, flops = algorithmic_bool(N, M, L, T)
+    else:
+        bytes_alg, flops = algorithmic(args.config, N, M, R, L, T, base)
     tok_s = T / (ms * 1e-3)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    # the library's automatic choice: decode kernel while T * terms <= 32
-    path = "adapter" if base else (
-        {1: "decode", 2: "mfma"}.get(args.path) or ("decode" if T <= 4 or L * ((T + 3) // 4) <= 5 else "mfma"))
+    path = "adapter" if base else ({1: "decode", 2: "mfma"}.get(args.path)
+                                   or auto_path(T, L, 4 if boolk else 5))
     # achieved = algorithmic bytes (flops) per step / HIP-event time per step;
     # decode and adapter steps are one kernel launch each, the MFMA step is
     # three (prep, stage-1 GEMM, stage-2 GEMM) and is rated as a whole
@@ -189,7 +219,7 @@ def main():
         check = verify(layer, x_np, x, y, copies[(args.steps - 1) % ncopies], base,
                        N, M, R, T, args, step_index=args.steps - 1, ws=ws)
 
-    cpu = None if args.no_cpu else cpu_baseline(layer, args.config, T, base)
+    cpu = None if args.no_cpu else cpu_baseline(layer, args.config, T, base, boolk)
 
     copy_probe = None
     if args.copy_probe:
@@ -200,6 +230,8 @@ def main():
         copy_probe = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4}
 
     name = cfgd["name"] + ("-r%d" % R if base else "")
+    shape = ({"N": N, "M": M, "kernels": L} if boolk else
+             {"N": N, "M": M, "R": R, "terms": L})
     out = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -215,7 +247,7 @@ def main():
         # MFMA products with fp32 sums (MFMA), bf16 MFMA products (adapter)
         "dtype": {"decode": "f32", "mfma": "f16", "adapter": "bf16"}[path],
         "data": "synthetic (seeded i.i.d. signs and scales of the configuration)",
-        "config": {"workload": name, "N": N, "M": M, "R": R, "terms": L,
+        "config": {"workload": name, **shape,
                    "tokens": T, "path": path,
                    "x_dtype": "f16" if x_np.dtype == np.float16 else "bf16",
                    "rotated_copies": ncopies,
@@ -254,7 +286,10 @@ def verify(layer, x_np, x, y, copy, base, N, M, R, T, args, step_index, ws):
     yg = y.clone()
     terms, w = copy
     ye = torch.empty_like(y)
-    if base:
+    boolk = args.config in S.BOOL_CONFIGS
+    if boolk:
+        D.dbf_bool_forward(terms, N, M, x, y=ye, ws=ws, path=args.path)
+    elif base:
         D.lordba_adapter_forward(w, terms, N, M, R, x, y=ye, ws=ws)
     else:
         D.dbf_linear_forward(terms, N, M, R, x, y=ye, ws=ws, path=args.path)
@@ -262,7 +297,10 @@ def verify(layer, x_np, x, y, copy, base, N, M, R, T, args, step_index, ws):
     same = bool(torch.equal(yg, ye))
     toks = list(range(min(T, 4)))
     xs = widen_x(x_np[toks])
-    ref = O.default().forward(O.terms64(layer), xs)
+    if boolk:
+        ref = O.default().bool_forward(bool64(layer), xs)
+    else:
+        ref = O.default().forward(O.terms64(layer), xs)
     if base:
         ref = ref + O.default().dense(O.widen_bf16(layer["w0"]), xs)
     from bit_adapters_amd.synth import f32_to_bf16_bits
@@ -278,19 +316,28 @@ def verify(layer, x_np, x, y, copy, base, N, M, R, T, args, step_index, ws):
             "rel_l2_vs_oracle_bf16": round(rel, 7), "max_abs": round(mx, 7), "ok": ok}
 
 
-def cpu_baseline(layer, config, T, base, budget_s=12.0):
+def bool64(layer):
+    return [dict(w=k["w"], s_in=np.asarray(k["s_in"], np.float64),
+                 s_out=np.asarray(k["s_out"], np.float64)) for k in layer["kernels"]]
+
+
+def cpu_baseline(layer, config, T, base, boolk=False, budget_s=12.0):
     """The fp64 oracle on the host cores over a bounded sample of the same
     workload: whole tokens of the same layer, until about budget_s seconds."""
     import oracle as O
 
     o = O.default()
-    terms = O.terms64(layer)
-    xs = widen_x(S.make_x(config, max(S.CONFIGS[config]["T"])))
+    cfgd = S.BOOL_CONFIGS[config] if boolk else S.CONFIGS[config]
+    terms = bool64(layer) if boolk else O.terms64(layer)
+    xs = widen_x(S.make_x(config, max(cfgd["T"])))
     w0 = O.widen_bf16(layer["w0"]) if base else None
     done, t0 = 0, time.perf_counter()
     while True:
         tok = xs[done % xs.shape[0]][None, :]
-        o.forward(terms, tok)
+        if boolk:
+            o.bool_forward(terms, tok)
+        else:
+            o.forward(terms, tok)
         if base:
             o.dense(w0, tok)
         done += 1

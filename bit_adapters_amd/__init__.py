@@ -33,7 +33,8 @@ DBF_WS_HEAD_BYTES = 16640
 EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
            "dbf_packed_bytes", "dbf_pack", "dbf_unpack", "dbf_workspace_bytes",
            "dbf_linear_forward", "dbf_linear_forward_i8",
-           "lordba_adapter_forward", "dbf_workspace_check")
+           "lordba_adapter_forward", "dbf_workspace_check",
+           "dbf_bool_workspace_bytes", "dbf_bool_forward")
 
 
 class _CTerm(ctypes.Structure):
@@ -79,6 +80,12 @@ def library() -> ctypes.CDLL:
         _i64, _vp, _int, _i64, _vp, _sz, _vp]
     lib.dbf_workspace_check.restype = _int
     lib.dbf_workspace_check.argtypes = [_vp, _vp]
+    lib.dbf_bool_workspace_bytes.restype = _sz
+    lib.dbf_bool_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int]
+    lib.dbf_bool_forward.restype = _int
+    lib.dbf_bool_forward.argtypes = [
+        ctypes.POINTER(_CBool), _int, _i64, _i64, _vp, _int, _i64, _i64, _vp,
+        _int, _i64, _int, _vp, _sz, _int, _vp]
     _lib_handle = lib
     return lib
 
@@ -124,6 +131,25 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+class DbfBoolKernel(NamedTuple):
+    """One boolean kernel of the Multi-Boolean form: packed signs w (N x M
+    layout), fp16 s_in (M) and s_out (N)."""
+    w: torch.Tensor
+    s_in: torch.Tensor
+    s_out: torch.Tensor
+
+
+class _CBool(ctypes.Structure):
+    _fields_ = [("w", _vp), ("s_in", _vp), ("s_out", _vp)]
+
+
+def _bool_kernels(kernels: Sequence[DbfBoolKernel]):
+    arr = (_CBool * max(1, len(kernels)))()
+    for i, k in enumerate(kernels):
+        arr[i] = _CBool(_ptr(k.w), _ptr(k.s_in), _ptr(k.s_out))
+    return arr
+
+
 def _terms(terms: Sequence[DbfTerm]):
     arr = (_CTerm * max(1, len(terms)))()
     for i, t in enumerate(terms):
@@ -151,6 +177,29 @@ def dbf_packed_bytes(rows: int, k: int) -> int:
 def dbf_workspace_bytes(N: int, M: int, R: int, n_terms: int, T: int,
                         path: int = DBF_PATH_AUTO) -> int:
     return int(library().dbf_workspace_bytes(N, M, R, n_terms, T, path))
+
+
+def dbf_bool_workspace_bytes(N: int, M: int, n_kernels: int, T: int,
+                             path: int = DBF_PATH_AUTO) -> int:
+    return int(library().dbf_bool_workspace_bytes(N, M, n_kernels, T, path))
+
+
+def dbf_bool_forward(kernels: Sequence[DbfBoolKernel], N: int, M: int,
+                     x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                     y_dtype: torch.dtype = torch.float32,
+                     accumulate: bool = False, ws: Optional[torch.Tensor] = None,
+                     path: int = DBF_PATH_AUTO, stream=None) -> torch.Tensor:
+    """y (+)= sum_k s_out_k . (Wb_k (s_in_k . x)) for x [T x M] (bf16 or f16)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=y_dtype, device=x.device)
+    ws, wsb = _workspace(dbf_bool_workspace_bytes(N, M, len(kernels), T, path),
+                         x.device, ws)
+    _check(library().dbf_bool_forward(
+        _bool_kernels(kernels), len(kernels), N, M, _ptr(x), _DT.get(x.dtype, -1),
+        T, _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), int(accumulate),
+        _ptr(ws), wsb, path, _stream(stream)))
+    return y
 
 
 def dbf_workspace_check(ws: Optional[torch.Tensor], stream=None) -> None:

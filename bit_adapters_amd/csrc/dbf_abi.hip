@@ -27,11 +27,16 @@ bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0
 // of (term, 4-token block) pairs, the MFMA path's barely at these sizes;
 // measured on the 4096 x 4096 R 2048 layer (decode faster up to 20 tokens)
 // and the three-term 11008 x 4096 layer (decode faster up to 4 tokens).
+// The boolean kernels (one product each, over a full N x M sign matrix)
+// cross over one step earlier: decode while T <= 4 or K * ceil(T / 4) <= 4
+// (measured on two 4096 x 4096 kernels, decode level with MFMA at 8 tokens,
+// and three 11008 x 4096 kernels, decode faster up to 4 tokens).
 constexpr int64_t kAutoDecodeBlocks = 5;
+constexpr int64_t kAutoBoolDecodeBlocks = 4;
 
-int resolve_path(int path, int64_t T, int n_terms) {
+int resolve_path(int path, int64_t T, int n_terms, int64_t blocks = kAutoDecodeBlocks) {
   if (path != DBF_PATH_AUTO) return path;
-  const bool decode = T <= 4 || n_terms * ((T + 3) / 4) <= kAutoDecodeBlocks;
+  const bool decode = T <= 4 || n_terms * ((T + 3) / 4) <= blocks;
   return decode ? DBF_PATH_DECODE : DBF_PATH_MFMA;
 }
 
@@ -115,18 +120,19 @@ int dbf_abi_version(void) { return DBF_ABI_VERSION; }
 int dbf_layout_version(void) { return DBF_LAYOUT_VERSION; }
 const char* dbf_last_error(void) { return g_err; }
 
-int dbf_workspace_check(void* ws, hipStream_t stream) {
+int dbf_workspace_check(void* ws, void* stream) {
   if (!ws) return fail(DBF_EINVAL, "workspace is NULL");
   if (!aligned16(ws)) return fail(DBF_EALIGN, "workspace not 16-byte aligned");
   // ctr[2] of the handoff head (dbf_lut.h, Sync)
   unsigned flag = 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(&flag, static_cast<unsigned char*>(ws) + 8, sizeof(flag),
-                                hipMemcpyDeviceToHost, stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(DBF_ELAUNCH, "reading the workspace failed: %s", hipGetErrorString(e));
   if (flag == 0) return DBF_OK;
-  e = hipMemsetAsync(ws, 0, DBF_WS_HEAD_BYTES, stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  e = hipMemsetAsync(ws, 0, DBF_WS_HEAD_BYTES, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(DBF_ELAUNCH, "clearing the workspace failed: %s", hipGetErrorString(e));
   return fail(DBF_ESTALLED, "a handoff wait gave up; the outputs of the calls since the last check are not valid");
 }
@@ -205,6 +211,63 @@ int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
                                      ldy, accumulate, ws, s));
   return launched(dbf::launch_decode(tp, N, M, R, x, x_dtype, T, ldx, y, y_dtype,
                                      ldy, accumulate, ws, s));
+}
+
+size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T, int path) {
+  if (N <= 0 || M <= 0 || n_kernels <= 0 || T <= 0) return 0;
+  if (resolve_path(path, T, n_kernels, kAutoBoolDecodeBlocks) == DBF_PATH_MFMA)
+    return dbf::mfma_bool_ws_bytes(N, M, n_kernels, T);
+  return dbf::decode_ws_bytes(N, M, N, n_kernels, T);
+}
+
+int dbf_bool_forward(const dbf_bool_kernel* kernels, int n_kernels, int64_t N, int64_t M,
+                     const void* x, int x_dtype, int64_t T, int64_t ldx, void* y,
+                     int y_dtype, int64_t ldy, int accumulate, void* ws, size_t ws_bytes,
+                     int path, void* stream) {
+  if (!kernels) return fail(DBF_EINVAL, "kernels is NULL");
+  if (n_kernels < 1 || n_kernels > DBF_MAX_TERMS)
+    return fail(DBF_EINVAL, "n_kernels %d outside 1..%d", n_kernels, DBF_MAX_TERMS);
+  for (int i = 0; i < n_kernels; ++i) {
+    const dbf_bool_kernel& k = kernels[i];
+    if (!k.w || !k.s_in || !k.s_out) return fail(DBF_EINVAL, "kernel %d: a pointer is NULL", i);
+    if (!aligned16(k.w)) return fail(DBF_EALIGN, "kernel %d: packed signs not 16-byte aligned", i);
+    if (!aligned2(k.s_in) || !aligned2(k.s_out))
+      return fail(DBF_EALIGN, "kernel %d: a scale vector is not 2-byte aligned", i);
+  }
+  if (N < 1 || M < 1) return fail(DBF_EINVAL, "N, M must be >= 1");
+  if (T < 0) return fail(DBF_EINVAL, "T < 0");
+  if (x_dtype != DBF_BF16 && x_dtype != DBF_F16)
+    return fail(DBF_EDTYPE, "x dtype %d unsupported (bf16 or f16)", x_dtype);
+  if (!out_dtype_ok(y_dtype)) return fail(DBF_EDTYPE, "y dtype %d unsupported", y_dtype);
+  if (accumulate != 0 && accumulate != 1) return fail(DBF_EINVAL, "accumulate must be 0 or 1");
+  if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_MFMA)
+    return fail(DBF_EINVAL, "unknown path %d", path);
+  if (T == 0) return DBF_OK;
+  if (!x || !y) return fail(DBF_EINVAL, "x or y is NULL");
+  if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
+  if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
+  if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
+  const int p = resolve_path(path, T, n_kernels, kAutoBoolDecodeBlocks);
+  int e = check_ws(ws, ws_bytes, dbf_bool_workspace_bytes(N, M, n_kernels, T, p));
+  if (e != DBF_OK) return e;
+  e = check_device();
+  if (e != DBF_OK) return e;
+  // the kernels in the roles of the double-binary path's sign matrices and
+  // scales: decode uses the stage-1 slots (b2, gamma, beta), MFMA the
+  // stage-2 ones (b1, alpha) plus gamma
+  dbf::TermPtrs tp{};
+  tp.n = n_kernels;
+  for (int i = 0; i < n_kernels; ++i) {
+    tp.b1[i] = tp.b2[i] = kernels[i].w;
+    tp.gamma[i] = static_cast<const uint16_t*>(kernels[i].s_in);
+    tp.alpha[i] = tp.beta[i] = static_cast<const uint16_t*>(kernels[i].s_out);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p == DBF_PATH_MFMA)
+    return launched(dbf::launch_bool_mfma(tp, N, M, x, x_dtype, T, ldx, y, y_dtype, ldy,
+                                          accumulate, ws, s));
+  return launched(dbf::launch_bool_decode(tp, N, M, x, x_dtype, T, ldx, y, y_dtype, ldy,
+                                          accumulate, ws, s));
 }
 
 int dbf_linear_forward_i8(const dbf_term* terms, int n_terms, int64_t N,

@@ -144,6 +144,66 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, 
 
 constexpr int64_t kStage1Wg = 512;
 
+// ---- boolean kernels (Multi-Boolean form) -------------------------------
+// The stage-1 role alone computes s_out . (Wb (s_in . x)) for each kernel
+// (Wb in the place of B2, s_in of gamma, s_out of beta, N rows), as K-split
+// partials; consumer workgroups then sum the partials of every kernel and
+// split into y.
+struct SumArgs {
+  int L, ks;
+  int64_t T, N, rs;
+  const float* ws;  // partials [L][ks][T][rs]
+  void* y;
+  int y_dtype;
+  int64_t ldy;
+  int accumulate;
+  Sync sync;
+  int64_t nrt;  // row tiles of N; consumer = (token block, row tile)
+};
+
+// Consumer `bid2`: 64 rows (lane) x TB tokens (wave).  Every partial of a
+// (row, token) is loaded before the sum, which runs in (kernel, split) order.
+template <int TB>
+__device__ __forceinline__ void sum_role(const SumArgs& p, int64_t bid2) {
+  const int64_t tblk = bid2 / p.nrt;
+  const int64_t rt = bid2 - tblk * p.nrt;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const unsigned ticket = wait_producers(p.sync, false);  // partials via system-scope loads
+  const int64_t row = rt * 64 + lane, tt = tblk * TB + wv;
+  if (wv < TB && row < p.N && tt < p.T) {
+    const int np = p.L * p.ks;
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(p.ws) + tt * p.rs + row;
+    float s = 0.f;
+    for (int j0 = 0; j0 < np; j0 += 16) {
+      uint32_t q[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        q[j] = j0 + j < np ? __hip_atomic_load(base + (j0 + j) * p.T * p.rs, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_SYSTEM)
+                           : 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < np) s += __uint_as_float(q[j]);
+    }
+    store_out(p.y, p.y_dtype, tt * p.ldy + row, s, p.accumulate);
+  }
+  consumer_done(p.sync, ticket);
+}
+
+template <int TB, int KW>
+__global__ void __launch_bounds__(kThreads) bool_decode_kernel(Stage1 s1, SumArgs s2, int n1) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* tbl = reinterpret_cast<float*>(smem);
+  float* red = tbl + tbl_elems<TB, KW>();
+  const int bid = blockIdx.x;
+  if (bid < n1) {
+    stage1_role<float, TB, KW, MODE_F>(s1, bid, tbl, red);
+    publish(s2.sync, static_cast<unsigned>(bid));
+    return;
+  }
+  sum_role<TB>(s2, bid - n1);
+}
+
 template <typename A, int MODE>
 hipError_t run(const Stage1& s1, const Stage2& s2, int n1, int n2, int run_stage2,
                int tb, int kw1, int kw2, hipStream_t s) {
@@ -228,6 +288,39 @@ hipError_t launch_decode(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
   return run<float, MODE_F>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T),
                             static_cast<int>(layout_kw(M)), static_cast<int>(layout_kw(R)), s);
+}
+
+hipError_t launch_bool_decode(const TermPtrs& t, int64_t N, int64_t M, const void* x,
+                              int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
+                              int64_t ldy, int accumulate, void* ws, hipStream_t s) {
+  int n1 = 0;
+  const Stage1 a = make_stage1(t, M, N, x, x_dtype, T, ldx, ws, true, &n1);
+  SumArgs b{};
+  b.L = t.n; b.ks = a.ks; b.T = T; b.N = N; b.rs = a.rs;
+  b.ws = static_cast<const float*>(a.ws);
+  b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
+  b.nrt = layout_nrt(N);
+  const int n2 = static_cast<int>(b.nrt * a.ntb);
+  b.sync = make_sync(ws, n1, n2);
+  const unsigned grid = static_cast<unsigned>(n1 + n2);
+  const int tb = pick_tb(T), kw = static_cast<int>(layout_kw(M));
+#define DBF_BOOL(TB_, KW_) \
+  bool_decode_kernel<TB_, KW_><<<dim3(grid), kThreads, lds_bytes<float, TB_, KW_>(), s>>>(a, b, n1)
+#define DBF_BOOL_KW(TB_)          \
+  switch (kw) {                   \
+    case 1: DBF_BOOL(TB_, 1); break; \
+    case 2: DBF_BOOL(TB_, 2); break; \
+    case 3: DBF_BOOL(TB_, 3); break; \
+    default: DBF_BOOL(TB_, 4); break; \
+  }
+  switch (tb) {
+    case 1: DBF_BOOL_KW(1); break;
+    case 2: DBF_BOOL_KW(2); break;
+    default: DBF_BOOL_KW(4); break;
+  }
+#undef DBF_BOOL_KW
+#undef DBF_BOOL
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_i8(const TermPtrs& t, int64_t N, int64_t M, int64_t R,

@@ -101,8 +101,21 @@ hipError_t launch_decode_i8(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                             int32_t* s1, int32_t* s2, void* y, int y_dtype,
                             int64_t ldy, void* ws, hipStream_t s);
 
+// Boolean kernels (Multi-Boolean form), decode path: t.b2 = the sign
+// matrices [N x M], t.gamma = s_in, t.beta = s_out; workspace as
+// decode_ws_bytes(N, M, N, n, T).
+hipError_t launch_bool_decode(const TermPtrs& t, int64_t N, int64_t M, const void* x,
+                              int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
+                              int64_t ldy, int accumulate, void* ws, hipStream_t s);
+
 // MFMA path.
 size_t mfma_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T);
+// Boolean kernels on the MFMA path: t.b1 = the sign matrices [N x M],
+// t.gamma = s_in, t.alpha = s_out.
+size_t mfma_bool_ws_bytes(int64_t N, int64_t M, int n_kernels, int64_t T);
+hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void* x,
+                            int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
+                            int64_t ldy, int accumulate, void* ws, hipStream_t s);
 hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                        const void* x, int x_dtype, int64_t T, int64_t ldx,
                        void* y, int y_dtype, int64_t ldy, int accumulate,

@@ -745,6 +745,82 @@ size_t mfma_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T) {
   return ws_layout(N, M, R, n_terms, T).total;
 }
 
+namespace {
+
+// Boolean kernels: u_k [L][T][kpad(M)], per-token sums, max|s| slots (zero),
+// then the split partials of the one product.
+struct BoolLayout {
+  size_t u, l1, bmax, part, total;
+  Tiling tl;
+};
+
+BoolLayout bool_layout(int64_t N, int64_t M, int L, int64_t T) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  BoolLayout w{};
+  w.tl = choose_tiling(T, N, 1, L * (kpad(M) / BK));
+  size_t off = kWsHeadBytes;
+  w.u = off; off += al(static_cast<size_t>(L) * T * kpad(M) * 2);
+  w.l1 = off; off += al(static_cast<size_t>(L) * T * 4);
+  w.bmax = off; off += al(static_cast<size_t>(L) * 4);
+  w.part = off;
+  if (w.tl.nsplit > 1) off += al(static_cast<size_t>(w.tl.nsplit) * T * round4(N) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t mfma_bool_ws_bytes(int64_t N, int64_t M, int n_kernels, int64_t T) {
+  return bool_layout(N, M, n_kernels, T).total;
+}
+
+// y = sum_k s_out_k . (Wb_k u_k), u_k = fp16(s_in_k . x): prep, then the
+// stage-2 product with the sign matrices in the place of B1 and u in the
+// place of v.  prep sees no beta (R = 0), so max|beta| is 0 and the token
+// scale is exactly 1: u is used as rounded, with no further scaling.
+hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void* x,
+                            int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
+                            int64_t ldy, int accumulate, void* ws, hipStream_t s) {
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  const BoolLayout lay = bool_layout(N, M, t.n, T);
+  _Float16* u = reinterpret_cast<_Float16*>(base + lay.u);
+  float* l1 = reinterpret_cast<float*>(base + lay.l1);
+  float* bmax = reinterpret_cast<float*>(base + lay.bmax);
+  float* part = reinterpret_cast<float*>(base + lay.part);
+
+  PrepArgs pa{};
+  pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
+  pa.R = 0; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
+  pa.vec = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  for (int i = 0; i < t.n; ++i) {
+    if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) pa.vec = 0;
+    pa.gamma[i] = t.gamma[i];
+    pa.beta[i] = nullptr;
+  }
+  prep_kernel<<<dim3(static_cast<unsigned>(t.n * T + t.n)), 256, 0, s>>>(pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  GemmArgs b{};
+  b.stage = 2; b.L = t.n; b.T = T; b.K = M; b.kp = kpad(M); b.ncols = N;
+  b.nkb = layout_nkb(M); b.nrt = layout_nrt(N); b.kw = static_cast<int>(layout_kw(M));
+  for (int i = 0; i < t.n; ++i) {
+    b.bits[i] = t.b1[i];
+    b.colscale[i] = t.alpha[i];
+  }
+  b.a = u; b.l1 = l1; b.bmax = bmax;
+  b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
+  b.part = part; b.ldp = round4(N);
+  e = launch_stage<2>(b, lay.tl, 1, s);
+  if (e != hipSuccess || lay.tl.nsplit == 1) return e;
+  Reduce2Args r{};
+  r.part = part; r.ldp = b.ldp; r.T = T; r.N = N; r.L = t.n; r.nsplit = lay.tl.nsplit;
+  r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax;
+  r.y = y; r.y_dtype = y_dtype; r.ldy = ldy; r.accumulate = accumulate;
+  reduce2_kernel<<<dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), 256, 0, s>>>(r);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                        const void* x, int x_dtype, int64_t T, int64_t ldx,
                        void* y, int y_dtype, int64_t ldy, int accumulate,

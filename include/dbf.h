@@ -153,7 +153,7 @@ size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
  * Returns DBF_OK when no wait gave up.  Otherwise it zeroes the head (so the
  * buffer is usable again) and returns DBF_ESTALLED.  Reads 4 bytes and
  * synchronizes the stream, so it is not for use inside graph capture. */
-int dbf_workspace_check(void *ws, hipStream_t stream);
+int dbf_workspace_check(void *ws, void *stream);
 
 /*
  * y (+)= sum_i Delta W_i x for T tokens.
@@ -218,6 +218,53 @@ int lordba_adapter_forward(const void *w0, int64_t ldw, const dbf_term *terms,
                            const void *x, int64_t T, int64_t ldx, void *y,
                            int y_dtype, int64_t ldy, void *ws,
                            size_t ws_bytes, void *stream);
+
+/*
+ * ---- Boolean kernels (the Multi-Boolean form) ---------------------------
+ * "Highly Efficient and Effective LLMs with Multi-Boolean Architectures",
+ * technical summary, section 2: item 1 approximates a weight by its sign
+ * matrix with a rank-one scale, W ~ sign(W) . (s_out s_in^T), item 2 sums
+ * several such kernels.  So
+ *
+ *   y = sum_{k=1..K} s_out_k . (Wb_k (s_in_k . x)),   Wb_k in {+-1}^{N x M},
+ *
+ * one sign-accumulate product per kernel over a full N x M sign matrix (the
+ * double-binary layer's stage S3 at R = M).  Extraction of the kernels from
+ * a real weight (successive SVID, item 3) is offline model conversion and
+ * not part of this library.
+ */
+typedef struct {
+    const uint32_t *w;  /* Wb_k, dbf_pack(rows = N, k = M) layout; 16-byte aligned */
+    const void *s_in;   /* fp16 [M], 2-byte aligned */
+    const void *s_out;  /* fp16 [N], 2-byte aligned */
+} dbf_bool_kernel;
+
+/* Bytes of workspace dbf_bool_forward needs (0 when T, N, M or n_kernels is
+ * not positive).  The head rule of dbf_workspace_bytes applies: its first
+ * DBF_WS_HEAD_BYTES must be zero before first use and every call leaves
+ * them zero, so one buffer may serve both kinds of call in turn. */
+size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T,
+                                int path);
+
+/*
+ * y (+)= sum_k s_out_k . (Wb_k (s_in_k . x)) for T tokens.
+ *   kernels          host array of n_kernels (1..DBF_MAX_TERMS) kernels.
+ *   x                [T x M], x_dtype DBF_BF16 or DBF_F16, row stride ldx.
+ *   y                [T x N], y_dtype DBF_F32, DBF_BF16 or DBF_F16, ldy.
+ *   accumulate       0: y = result; 1: y = y + result (in fp32).
+ *   ws, ws_bytes     workspace of dbf_bool_workspace_bytes(..., path) bytes.
+ *   path             DBF_PATH_AUTO picks the decode path while T <= 4 or
+ *                    n_kernels * ceil(T / 4) <= 4, and the MFMA path above;
+ *                    the others force one.
+ * The decode path keeps everything in fp32; the MFMA path rounds s_in . x
+ * to fp16 once, with fp32 accumulation.  x, y 16-byte aligned.  T = 0 is
+ * valid and does nothing.  Results are bitwise reproducible run to run.
+ */
+int dbf_bool_forward(const dbf_bool_kernel *kernels, int n_kernels, int64_t N,
+                     int64_t M, const void *x, int x_dtype, int64_t T,
+                     int64_t ldx, void *y, int y_dtype, int64_t ldy,
+                     int accumulate, void *ws, size_t ws_bytes, int path,
+                     void *stream);
 
 #ifdef __cplusplus
 }

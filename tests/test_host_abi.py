@@ -4,6 +4,7 @@ before making any HIP call (so these run without a GPU)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -153,6 +154,82 @@ def ad(w0=FAKE, ldw=8, terms=None, n=1, N=8, M=8, R=8, x=FAKE, T=1, ldx=8,
 ])
 def test_adapter_validation(kw, code):
     assert ad(**kw) == code
+
+
+def _bools(n=1, **over):
+    arr = (D._CBool * max(n, 1))()
+    for i in range(n):
+        f = dict(w=FAKE, s_in=FAKE, s_out=FAKE)
+        f.update(over)
+        arr[i] = D._CBool(**f)
+    return arr
+
+
+def bfwd(kernels=None, n=1, N=8, M=8, x=FAKE, xdt=D.DBF_BF16, T=1, ldx=8,
+         y=FAKE, ydt=D.DBF_F32, ldy=8, acc=0, ws=FAKE, wsb=1 << 30, path=0):
+    if kernels is None:
+        kernels = _bools(n)
+    return L.dbf_bool_forward(kernels, n, N, M, x, xdt, T, ldx, y, ydt, ldy, acc,
+                              ws, wsb, path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kernels=None, n=0), D.DBF_EINVAL), (dict(n=0), D.DBF_EINVAL),
+    (dict(n=9), D.DBF_EINVAL),
+    (dict(kernels=_bools(1, w=None)), D.DBF_EINVAL),
+    (dict(kernels=_bools(1, s_in=None)), D.DBF_EINVAL),
+    (dict(kernels=_bools(1, s_out=None)), D.DBF_EINVAL),
+    (dict(kernels=_bools(1, w=MIS)), D.DBF_EALIGN),
+    (dict(kernels=_bools(1, s_out=FAKE + 1)), D.DBF_EALIGN),
+    (dict(N=0), D.DBF_EINVAL), (dict(M=0), D.DBF_EINVAL), (dict(T=-1), D.DBF_EINVAL),
+    (dict(xdt=D.DBF_I8), D.DBF_EDTYPE), (dict(ydt=D.DBF_I32), D.DBF_EDTYPE),
+    (dict(acc=3), D.DBF_EINVAL), (dict(path=5), D.DBF_EINVAL),
+    (dict(ldx=7), D.DBF_EINVAL), (dict(ldy=7), D.DBF_EINVAL),
+    (dict(y=None), D.DBF_EINVAL), (dict(x=MIS), D.DBF_EALIGN),
+    (dict(ws=None), D.DBF_EWORKSPACE), (dict(wsb=100), D.DBF_EWORKSPACE),
+    (dict(ws=MIS), D.DBF_EALIGN),
+])
+def test_bool_forward_validation(kw, code):
+    assert bfwd(**kw) == code
+    assert D.dbf_last_error()
+
+
+def test_bool_zero_tokens_is_a_noop():
+    assert bfwd(T=0, x=None, y=None, ws=None, wsb=0) == D.DBF_OK
+
+
+def test_bool_workspace_bytes():
+    assert D.dbf_bool_workspace_bytes(4096, 4096, 2, 0) == 0
+    assert D.dbf_bool_workspace_bytes(0, 4096, 2, 1) == 0
+    # decode: the head plus fp32 partials of every kernel and K-split
+    dec = D.dbf_bool_workspace_bytes(4096, 4096, 2, 1, D.DBF_PATH_DECODE)
+    assert dec > D.DBF_WS_HEAD_BYTES and (dec - D.DBF_WS_HEAD_BYTES) % (2 * 4096 * 4) == 0
+    # MFMA: at least the fp16 u of every kernel and token
+    assert D.dbf_bool_workspace_bytes(4096, 4096, 2, 512, D.DBF_PATH_MFMA) >= 2 * 512 * 4096 * 2
+    assert (D.dbf_bool_workspace_bytes(4096, 4096, 2, 1) == dec)
+
+
+@pytest.mark.parametrize("T,K,path", [(1, 2, "decode"), (4, 3, "decode"), (8, 2, "decode"),
+                                      (9, 2, "mfma"), (5, 3, "mfma"), (16, 1, "decode"),
+                                      (17, 1, "mfma"), (4, 8, "decode")])
+def test_bool_auto_path_rule(T, K, path):
+    # decode while T <= 4 or n_kernels * ceil(T / 4) <= 4
+    want = D.DBF_PATH_DECODE if path == "decode" else D.DBF_PATH_MFMA
+    auto = D.dbf_bool_workspace_bytes(4096, 4096, K, T, D.DBF_PATH_AUTO)
+    assert auto == D.dbf_bool_workspace_bytes(4096, 4096, K, T, want)
+    other = D.DBF_PATH_MFMA if want == D.DBF_PATH_DECODE else D.DBF_PATH_DECODE
+    assert auto != D.dbf_bool_workspace_bytes(4096, 4096, K, T, other)
+
+
+def test_header_compiles_as_c(tmp_path):
+    # the ABI header is plain C: no HIP or C++ type in any declaration
+    src = tmp_path / "h.c"
+    src.write_text('#include "dbf.h"\nint main(void) { return 0; }\n')
+    inc = os.path.dirname(HEADER)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", inc, "-c", str(src), "-o", str(tmp_path / "h.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
 
 
 def test_workspace_check_validation():
