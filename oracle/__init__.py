@@ -16,6 +16,8 @@ order); this module only widens the stored types to fp64 and calls it:
 * ``dense``     -- the frozen base W0 x of LoRDBA's unmerged adapter mode
   (LoRDBA sections 1 and 5);
 * ``forward_int`` -- exact integer sign sums for int8 activations;
+* ``backward`` -- the chain rule through the layer: dx and the gradients of
+  the three scale vectors of every term;
 * ``bool_forward`` -- the Multi-Boolean form itself (technical summary,
   section 2, items 1 and 2): y = sum_k s_out_k . (Wb_k (s_in_k . x)), each
   kernel a full N x M sign matrix with a rank-one scale;
@@ -86,6 +88,12 @@ class Oracle:
         lib.dbf_oracle_bool_forward.argtypes = [
             ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(_i8p),
             ctypes.POINTER(_dp), ctypes.POINTER(_dp), _dp, _dp]
+        lib.dbf_oracle_backward.restype = ctypes.c_int
+        lib.dbf_oracle_backward.argtypes = [
+            ctypes.c_int, _i64, _i64, _i64, _i64,
+            ctypes.POINTER(_i8p), ctypes.POINTER(_i8p),
+            ctypes.POINTER(_dp), ctypes.POINTER(_dp), ctypes.POINTER(_dp),
+            _dp, _dp, _dp, _dp, _dp, _dp]
         lib.dbf_oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -125,6 +133,45 @@ class Oracle:
         if rc != 0:
             raise MemoryError("oracle scratch allocation failed")
         return y
+
+    def backward(self, terms, x, dy):
+        """Gradients of a loss with dL/dy = dy [T x N] through the layer:
+        (dx [T x M], dalpha [L x N], dbeta [L x R], dgamma [L x M]), fp64."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        dy = np.ascontiguousarray(dy, dtype=np.float64)
+        T, M = x.shape
+        L = len(terms)
+        N, R = terms[0]["b1"].shape
+        assert dy.shape == (T, N)
+        keep = []
+
+        def arr(a, dt):
+            a = np.ascontiguousarray(a, dtype=dt)
+            keep.append(a)
+            return a
+
+        b1 = [arr(t["b1"], np.int8) for t in terms]
+        b2 = [arr(t["b2"], np.int8) for t in terms]
+        al = [arr(t["alpha"], np.float64) for t in terms]
+        be = [arr(t["beta"], np.float64) for t in terms]
+        ga = [arr(t["gamma"], np.float64) for t in terms]
+        dx = np.empty((T, M)); da = np.empty((L, N)); db = np.empty((L, R)); dg = np.empty((L, M))
+        P8 = (_i8p * L)(*[a.ctypes.data_as(_i8p) for a in b1])
+        Q8 = (_i8p * L)(*[a.ctypes.data_as(_i8p) for a in b2])
+        A = (_dp * L)(*[a.ctypes.data_as(_dp) for a in al])
+        B = (_dp * L)(*[a.ctypes.data_as(_dp) for a in be])
+        G = (_dp * L)(*[a.ctypes.data_as(_dp) for a in ga])
+        rc = self.lib.dbf_oracle_backward(
+            L, N, M, R, T, P8, Q8, A, B, G, x.ctypes.data_as(_dp), dy.ctypes.data_as(_dp),
+            dx.ctypes.data_as(_dp), da.ctypes.data_as(_dp), db.ctypes.data_as(_dp),
+            dg.ctypes.data_as(_dp))
+        if rc != 0:
+            raise MemoryError("oracle scratch allocation failed")
+        return dx, da, db, dg
+
+    def transpose_packed(self, words, rows: int, K: int) -> np.ndarray:
+        """The packed layout of S^T for the packed S (rows x K)."""
+        return self.pack(self.unpack(words, rows, K).T.astype(np.float64))
 
     def dense(self, w0, x) -> np.ndarray:
         """W0 x for every token: [T x N] fp64."""

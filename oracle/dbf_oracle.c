@@ -154,6 +154,93 @@ int dbf_oracle_bool_forward(int K, int64_t N, int64_t M, int64_t T,
     return 0;
 }
 
+/* Backward of dbf_oracle_forward for a loss with gradient dy = dL/dy, by
+ * the chain rule through the LoRDBA parametrization (section 2,
+ * "Arquitetura Central"), read right to left per term i and token t:
+ *   u = gamma . x,  s = B2 u,  w = beta . s,  z = B1 w,  y += alpha . z
+ * so, going back,
+ *   e = alpha . dy,  g = B1^T e,  f = beta . g,  h = B2^T f
+ *   dalpha += dy . z,  dbeta += s . g,  dgamma += x . h,  dx += gamma . h
+ * (B^T v is a +-add down a column of B).  Every output is overwritten;
+ * token sums run in token order.  Returns 0, or -1 if scratch cannot be had. */
+int dbf_oracle_backward(int L, int64_t N, int64_t M, int64_t R, int64_t T,
+                        const int8_t *const *b1, const int8_t *const *b2,
+                        const double *const *alpha, const double *const *beta,
+                        const double *const *gamma, const double *x,
+                        const double *dy, double *dx, double *dalpha,
+                        double *dbeta, double *dgamma)
+{
+    double *u = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    double *sv = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    double *z = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double *g = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    double *h = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    int64_t t, idx;
+    int i;
+    if (!u || !sv || !z || !g || !h) {
+        free(u); free(sv); free(z); free(g); free(h);
+        return -1;
+    }
+    for (idx = 0; idx < T * M; ++idx)
+        dx[idx] = 0.0;
+    for (idx = 0; idx < (int64_t)L * N; ++idx)
+        dalpha[idx] = 0.0;
+    for (idx = 0; idx < (int64_t)L * R; ++idx)
+        dbeta[idx] = 0.0;
+    for (idx = 0; idx < (int64_t)L * M; ++idx)
+        dgamma[idx] = 0.0;
+    for (t = 0; t < T; ++t) {
+        const double *xt = x + t * M, *dyt = dy + t * N;
+        for (i = 0; i < L; ++i) {
+            const int8_t *B1 = b1[i], *B2 = b2[i];
+            const double *al = alpha[i], *be = beta[i], *ga = gamma[i];
+            /* forward intermediates s = B2 (gamma . x) and z = B1 (beta . s) */
+            for (int64_t m = 0; m < M; ++m)
+                u[m] = ga[m] * xt[m];
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < R; ++r) {
+                double acc = 0.0;
+                for (int64_t m = 0; m < M; ++m)
+                    acc += (B2[r * M + m] > 0) ? u[m] : -u[m];
+                sv[r] = acc;
+            }
+#pragma omp parallel for schedule(static)
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int64_t r = 0; r < R; ++r)
+                    acc += (B1[n * R + r] > 0) ? be[r] * sv[r] : -(be[r] * sv[r]);
+                z[n] = acc;
+            }
+            /* g = B1^T (alpha . dy): down column r of B1 */
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < R; ++r) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += (B1[n * R + r] > 0) ? al[n] * dyt[n] : -(al[n] * dyt[n]);
+                g[r] = acc;
+            }
+            /* h = B2^T (beta . g): down column m of B2 */
+#pragma omp parallel for schedule(static)
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t r = 0; r < R; ++r)
+                    acc += (B2[r * M + m] > 0) ? be[r] * g[r] : -(be[r] * g[r]);
+                h[m] = acc;
+            }
+            for (int64_t n = 0; n < N; ++n)
+                dalpha[(int64_t)i * N + n] += dyt[n] * z[n];
+            for (int64_t r = 0; r < R; ++r)
+                dbeta[(int64_t)i * R + r] += sv[r] * g[r];
+            for (int64_t m = 0; m < M; ++m) {
+                dgamma[(int64_t)i * M + m] += xt[m] * h[m];
+                dx[t * M + m] += ga[m] * h[m];
+            }
+        }
+    }
+    free(u); free(sv); free(z); free(g); free(h);
+    return 0;
+}
+
 /* The dense base of adapter mode: y[t] += W0 x[t], W0 is N x M row-major. */
 void dbf_oracle_dense(int64_t N, int64_t M, int64_t T, const double *w0,
                       const double *x, double *y)

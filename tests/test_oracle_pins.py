@@ -371,11 +371,48 @@ def pin_bool_additivity(o):
     assert np.array_equal(o.bool_forward(ks, x), parts)
 
 
+def pin_backward_adjoint(o):
+    # the layer is linear in x: <dy, F x> = <dx, x> (exact on small integers)
+    terms = _rand_layer(9, 11, 6, 2, 1400, integer=True)
+    x = _rand_x(3, 11, 1400, integer=True)
+    dy = _rand_x(3, 9, 1401, integer=True)
+    dx, _, _, _ = o.backward(terms, x, dy)
+    assert np.sum(dy * o.forward(terms, x)) == np.sum(dx * x)
+    # and dx = dy Delta W with Delta W materialised by numpy products
+    terms = _rand_layer(13, 17, 7, 2, 1402)
+    x = _rand_x(2, 17, 1402)
+    dy = _rand_x(2, 13, 1403)
+    W = sum(np.diag(t["alpha"]) @ t["b1"] @ np.diag(t["beta"]) @ t["b2"] @ np.diag(t["gamma"])
+            for t in terms)
+    dx, _, _, _ = o.backward(terms, x, dy)
+    assert np.max(np.abs(dx - dy @ W)) <= 1e-12 * np.max(np.abs(dy @ W))
+
+
+def pin_backward_scale_steps(o):
+    # the layer is linear in every single scale entry, so a unit step of
+    # alpha_i[n] (beta_i[r], gamma_i[m]) changes <dy, y> by exactly that
+    # entry's gradient; small integers keep both sides exact
+    terms = _rand_layer(5, 7, 4, 2, 1410, integer=True)
+    x = _rand_x(3, 7, 1410, integer=True)
+    dy = _rand_x(3, 5, 1411, integer=True)
+    _, da, db, dg = o.backward(terms, x, dy)
+    base = np.sum(dy * o.forward(terms, x))
+    for i in range(2):
+        for key, grad in (("alpha", da), ("beta", db), ("gamma", dg)):
+            for j in range(len(terms[i][key])):
+                v = terms[i][key].copy()
+                v[j] += 1.0
+                stepped = list(terms)
+                stepped[i] = dict(terms[i], **{key: v})
+                assert np.sum(dy * o.forward(stepped, x)) - base == grad[i, j], (key, i, j)
+
+
 PINS = [pin_bruteforce_real, pin_bruteforce_exact, pin_dbf_hadamard_form,
         pin_all_ones, pin_rank_one, pin_row_flip, pin_gauge, pin_column_flip,
         pin_permutation, pin_homogeneity, pin_additivity, pin_int_bigint,
         pin_int_all_ones, pin_dense, pin_pack_golden, pin_pack_counts,
-        pin_bool_bruteforce, pin_bool_all_ones, pin_bool_row_flip, pin_bool_additivity]
+        pin_bool_bruteforce, pin_bool_all_ones, pin_bool_row_flip, pin_bool_additivity,
+        pin_backward_adjoint, pin_backward_scale_steps]
 
 
 @pytest.fixture(scope="module")
@@ -445,6 +482,19 @@ MUTANTS = [
      "acc += (wb[k][q * N + o] > 0) ? xs[q] : -xs[q];"),
     ("bool kernels overwrite", "yt[o] += s_out[k][o] * acc;", "yt[o] = s_out[k][o] * acc;"),
     ("bool last kernel dropped", "for (k = 0; k < K; ++k)", "for (k = 0; k + 1 < K; ++k)"),
+    ("bwd alpha dropped", "acc += (B1[n * R + r] > 0) ? al[n] * dyt[n] : -(al[n] * dyt[n]);",
+     "acc += (B1[n * R + r] > 0) ? dyt[n] : -dyt[n];"),
+    ("bwd B1 read untransposed", "acc += (B1[n * R + r] > 0) ? al[n] * dyt[n] : -(al[n] * dyt[n]);",
+     "acc += (B1[r * N + n] > 0) ? al[n] * dyt[n] : -(al[n] * dyt[n]);"),
+    ("bwd beta dropped", "acc += (B2[r * M + m] > 0) ? be[r] * g[r] : -(be[r] * g[r]);",
+     "acc += (B2[r * M + m] > 0) ? g[r] : -g[r];"),
+    ("bwd dgamma with gamma", "dgamma[(int64_t)i * M + m] += xt[m] * h[m];",
+     "dgamma[(int64_t)i * M + m] += ga[m] * h[m];"),
+    ("bwd dx without gamma", "dx[t * M + m] += ga[m] * h[m];", "dx[t * M + m] += h[m];"),
+    ("bwd dbeta with beta", "dbeta[(int64_t)i * R + r] += sv[r] * g[r];",
+     "dbeta[(int64_t)i * R + r] += be[r] * sv[r] * g[r];"),
+    ("bwd dalpha with alpha", "dalpha[(int64_t)i * N + n] += dyt[n] * z[n];",
+     "dalpha[(int64_t)i * N + n] += dyt[n] * al[n] * z[n];"),
 ]
 
 
@@ -521,3 +571,13 @@ def test_svid_successive_kernels():
         err = np.linalg.norm(o.bool_forward(ks[:i + 1], x) - x @ W.T)
         assert err < prev_err
         prev_err = err
+
+
+def test_transpose_packed_round_trip():
+    o = O.default()
+    for rows, K in [(1, 1), (3, 70), (64, 128), (130, 33), (200, 513)]:
+        v = np.random.default_rng([44, rows, K]).standard_normal((rows, K))
+        w = o.pack(v)
+        wt = o.transpose_packed(w, rows, K)
+        assert np.array_equal(o.unpack(wt, K, rows), np.where(v >= 0, 1, -1).T)
+        assert np.array_equal(o.transpose_packed(wt, K, rows), w)
