@@ -91,6 +91,16 @@ def algorithmic_bool(N, M, K, T):
     return K * N * M / 8.0 + 2.0 * K * (N + M) + 2.0 * T * (M + N), 2.0 * T * N * M * K
 
 
+def algorithmic_backward(N, M, R, L, T):
+    """The backward: the packed signs twice (the factors and their
+    transposes), fp16 scales, bf16 x, dy and dx, fp32 scale gradients; four
+    sign-accumulate products per term."""
+    signs = 2 * L * R * (N + M) / 8.0
+    scales = 2.0 * L * (N + R + M) + 4.0 * L * (N + R + M)
+    io = 2.0 * T * (M + N) + 2.0 * T * M
+    return signs + scales + io, 4.0 * T * R * (N + M) * L
+
+
 def auto_path(T, L, blocks=5):
     # the library's automatic choice (dbf_abi.hip, resolve_path); the boolean
     # kernels switch to the MFMA path one 4-token block earlier
@@ -109,6 +119,8 @@ def main():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time dbf_linear_backward (dx and every scale gradient) instead")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -142,19 +154,39 @@ def main():
                 D.dbf_pack(torch.from_numpy(t["b1"]).to(DEV)),
                 D.dbf_pack(torch.from_numpy(t["b2"]).to(DEV)),
                 dev_f16(t["alpha"]), dev_f16(t["beta"]), dev_f16(t["gamma"])))
+    if args.backward and (boolk or base):
+        print("--backward is for the double-binary layers (configs 1, 2, 4, 5)", file=sys.stderr)
+        sys.exit(2)
+    if args.backward:
+        # each copy carries its packed transposes as well
+        terms0 = [(t, D.dbf_term_t(t, N, M, R)) for t in terms0]
+        dy = dev_bf16(S.f32_to_bf16_bits(np.random.default_rng([0xDBF, 106, T, N]).standard_normal(
+            (T, N), dtype=np.float32)))
     tcls = type(terms0[0])
     w0 = dev_bf16(layer["w0"]) if base else None
-    copy_bytes = sum(sum(v.numel() * v.element_size() for v in t) for t in terms0)
+    def nbytes(t):
+        if isinstance(t, tuple) and not hasattr(t, "_fields"):
+            return sum(nbytes(u) for u in t)
+        return sum(v.numel() * v.element_size() for v in t)
+
+    copy_bytes = sum(nbytes(t) for t in terms0)
     if base:
         copy_bytes += w0.numel() * 2
     ncopies = max(1, min(int(math.ceil(args.rotate_gib * 2 ** 30 / copy_bytes)), 4096))
     copies = [(terms0, w0)]
     for _ in range(ncopies - 1):
-        copies.append(([tcls(*[v.clone() for v in t]) for t in terms0],
-                       w0.clone() if base else None))
+        if args.backward:
+            copies.append(([(type(a)(*[v.clone() for v in a]), type(b)(*[v.clone() for v in b]))
+                            for a, b in terms0], None))
+        else:
+            copies.append(([tcls(*[v.clone() for v in t]) for t in terms0],
+                           w0.clone() if base else None))
 
     y = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
-    if boolk:
+    if args.backward:
+        nws = D.dbf_backward_workspace_bytes(N, M, R, L, T, args.path)
+        gdx = torch.empty((T, M), dtype=torch.bfloat16, device=DEV)
+    elif boolk:
         nws = D.dbf_bool_workspace_bytes(N, M, L, T, args.path)
     elif base:
         nws = D.dbf_workspace_bytes(N, M, R, L, T, D.DBF_PATH_DECODE)
@@ -164,7 +196,10 @@ def main():
 
     def step(i):
         terms, w = copies[i % ncopies]
-        if boolk:
+        if args.backward:
+            D.dbf_linear_backward([a for a, _ in terms], [b for _, b in terms], N, M, R, x, dy,
+                                  dx_dtype=torch.bfloat16, ws=ws, path=args.path)
+        elif boolk:
             D.dbf_bool_forward(terms, N, M, x, y=y, ws=ws, path=args.path)
         elif base:
             D.lordba_adapter_forward(w, terms, N, M, R, x, y=y, ws=ws)
@@ -193,15 +228,20 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    if boolk:
+    if args.backward:
+        bytes_alg, flops = algorithmic_backward(N, M, R, L, T)
+    elif boolk:
         bytes_alg, flops = algorithmic_bool(N, M, L, T)
     else:
         bytes_alg, flops = algorithmic(args.config, N, M, R, L, T, base)
     tok_s = T / (ms * 1e-3)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    path = "adapter" if base else ({1: "decode", 2: "mfma"}.get(args.path)
-                                   or auto_path(T, L, 4 if boolk else 5))
+    if args.backward:
+        path = {1: "decode", 2: "mfma"}.get(args.path) or auto_path(T, 1, 4)
+    else:
+        path = "adapter" if base else ({1: "decode", 2: "mfma"}.get(args.path)
+                                       or auto_path(T, L, 4 if boolk else 5))
     # achieved = algorithmic bytes (flops) per step / HIP-event time per step;
     # decode and adapter steps are one kernel launch each, the MFMA step is
     # three (prep, stage-1 GEMM, stage-2 GEMM) and is rated as a whole
@@ -215,11 +255,14 @@ def main():
     roof["traffic"] = traffic_for(args, T)
 
     check = None
+    if args.backward:
+        args.no_check = True  # parity of the backward: tests/test_gpu_backward.py
     if not args.no_check:
         check = verify(layer, x_np, x, y, copies[(args.steps - 1) % ncopies], base,
                        N, M, R, T, args, step_index=args.steps - 1, ws=ws)
 
-    cpu = None if args.no_cpu else cpu_baseline(layer, args.config, T, base, boolk)
+    cpu = None if args.no_cpu else cpu_baseline(layer, args.config, T, base, boolk,
+                                                backward=args.backward)
 
     copy_probe = None
     if args.copy_probe:
@@ -229,7 +272,7 @@ def main():
         torch.cuda.synchronize()
         copy_probe = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4}
 
-    name = cfgd["name"] + ("-r%d" % R if base else "")
+    name = cfgd["name"] + ("-r%d" % R if base else "") + ("-backward" if args.backward else "")
     shape = ({"N": N, "M": M, "kernels": L} if boolk else
              {"N": N, "M": M, "R": R, "terms": L})
     out = {
@@ -321,7 +364,7 @@ def bool64(layer):
                  s_out=np.asarray(k["s_out"], np.float64)) for k in layer["kernels"]]
 
 
-def cpu_baseline(layer, config, T, base, boolk=False, budget_s=12.0):
+def cpu_baseline(layer, config, T, base, boolk=False, budget_s=12.0, backward=False):
     """The fp64 oracle on the host cores over a bounded sample of the same
     workload: whole tokens of the same layer, until about budget_s seconds."""
     import oracle as O
@@ -336,6 +379,8 @@ def cpu_baseline(layer, config, T, base, boolk=False, budget_s=12.0):
         tok = xs[done % xs.shape[0]][None, :]
         if boolk:
             o.bool_forward(terms, tok)
+        elif backward:
+            o.backward(terms, tok, np.ones((1, layer["N"])))
         else:
             o.forward(terms, tok)
         if base:
@@ -346,7 +391,8 @@ def cpu_baseline(layer, config, T, base, boolk=False, budget_s=12.0):
             break
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": o.threads(),
             "kind": "oracle",
-            "sample": "%d single-token forwards of the same layer (%.1f s), fp64" % (done, el)}
+            "sample": "%d single-token %s of the same layer (%.1f s), fp64"
+                      % (done, "backwards" if backward else "forwards", el)}
 
 
 if __name__ == "__main__":

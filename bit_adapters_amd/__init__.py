@@ -34,7 +34,8 @@ EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
            "dbf_packed_bytes", "dbf_pack", "dbf_unpack", "dbf_workspace_bytes",
            "dbf_linear_forward", "dbf_linear_forward_i8",
            "lordba_adapter_forward", "dbf_workspace_check",
-           "dbf_bool_workspace_bytes", "dbf_bool_forward")
+           "dbf_bool_workspace_bytes", "dbf_bool_forward", "dbf_transpose_packed",
+           "dbf_backward_workspace_bytes", "dbf_linear_backward")
 
 
 class _CTerm(ctypes.Structure):
@@ -80,6 +81,15 @@ def library() -> ctypes.CDLL:
         _i64, _vp, _int, _i64, _vp, _sz, _vp]
     lib.dbf_workspace_check.restype = _int
     lib.dbf_workspace_check.argtypes = [_vp, _vp]
+    lib.dbf_transpose_packed.restype = _int
+    lib.dbf_transpose_packed.argtypes = [_vp, _i64, _i64, _vp, _vp]
+    lib.dbf_backward_workspace_bytes.restype = _sz
+    lib.dbf_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _i64, _int]
+    lib.dbf_linear_backward.restype = _int
+    lib.dbf_linear_backward.argtypes = [
+        ctypes.POINTER(_CTerm), ctypes.POINTER(_CTermT), _int, _i64, _i64, _i64,
+        _vp, _int, _i64, _vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp,
+        _vp, _sz, _int, _vp]
     lib.dbf_bool_workspace_bytes.restype = _sz
     lib.dbf_bool_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int]
     lib.dbf_bool_forward.restype = _int
@@ -129,6 +139,17 @@ def _ld(t: torch.Tensor) -> int:
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("expected a 2-D tensor with unit column stride")
     return t.stride(0)
+
+
+class DbfTermT(NamedTuple):
+    """The packed transposes of one term's factors: b1t (R x N layout) and
+    b2t (M x R layout), from dbf_transpose_packed."""
+    b1t: torch.Tensor
+    b2t: torch.Tensor
+
+
+class _CTermT(ctypes.Structure):
+    _fields_ = [("b1t", _vp), ("b2t", _vp)]
 
 
 class DbfBoolKernel(NamedTuple):
@@ -200,6 +221,56 @@ def dbf_bool_forward(kernels: Sequence[DbfBoolKernel], N: int, M: int,
         T, _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), int(accumulate),
         _ptr(ws), wsb, path, _stream(stream)))
     return y
+
+
+def dbf_transpose_packed(packed: torch.Tensor, rows: int, k: int,
+                         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The packed layout of S^T (k x rows) from that of S (rows x k)."""
+    if out is None:
+        out = torch.empty(dbf_packed_bytes(k, rows) // 4, dtype=torch.int32,
+                          device=packed.device)
+    _check(library().dbf_transpose_packed(_ptr(packed), rows, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def dbf_term_t(term: DbfTerm, N: int, M: int, R: int, stream=None) -> DbfTermT:
+    """The transposes a term's backward needs, packed on the device."""
+    return DbfTermT(dbf_transpose_packed(term.b1, N, R, stream=stream),
+                    dbf_transpose_packed(term.b2, R, M, stream=stream))
+
+
+def dbf_backward_workspace_bytes(N: int, M: int, R: int, n_terms: int, T: int,
+                                 path: int = DBF_PATH_AUTO) -> int:
+    return int(library().dbf_backward_workspace_bytes(N, M, R, n_terms, T, path))
+
+
+def dbf_linear_backward(terms: Sequence[DbfTerm], tterms: Sequence[DbfTermT], N: int,
+                        M: int, R: int, x: torch.Tensor, dy: torch.Tensor,
+                        dx_dtype: torch.dtype = torch.float32, want_dx: bool = True,
+                        want_scales: bool = True, ws: Optional[torch.Tensor] = None,
+                        path: int = DBF_PATH_AUTO, stream=None):
+    """(dx [T x M] or None, [(dalpha, dbeta, dgamma)] per term or None) for
+    dy = dL/dy [T x N]."""
+    T = x.shape[0]
+    L_ = len(terms)
+    dev = x.device
+    dx = torch.empty((T, M), dtype=dx_dtype, device=dev) if want_dx else None
+    da = db = dg = None
+    if want_scales:
+        da = torch.empty((L_, N), dtype=torch.float32, device=dev)
+        db = torch.empty((L_, R), dtype=torch.float32, device=dev)
+        dg = torch.empty((L_, M), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(dbf_backward_workspace_bytes(N, M, R, L_, T, path), dev, ws)
+    tt = (_CTermT * max(1, L_))()
+    for i, t in enumerate(tterms):
+        tt[i] = _CTermT(_ptr(t.b1t), _ptr(t.b2t))
+    _check(library().dbf_linear_backward(
+        _terms(terms), tt, L_, N, M, R, _ptr(x), _DT.get(x.dtype, -1), _ld(x), _ptr(dy),
+        _DT.get(dy.dtype, -1), _ld(dy), T, _ptr(dx), _DT.get(dx_dtype, -1),
+        _ld(dx) if dx is not None else M, _ptr(da), _ptr(db), _ptr(dg), _ptr(ws), wsb,
+        path, _stream(stream)))
+    scales = [(da[i], db[i], dg[i]) for i in range(L_)] if want_scales else None
+    return dx, scales
 
 
 def dbf_workspace_check(ws: Optional[torch.Tensor], stream=None) -> None:

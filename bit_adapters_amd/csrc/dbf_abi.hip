@@ -213,6 +213,73 @@ int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
                                      ldy, accumulate, ws, s));
 }
 
+int dbf_transpose_packed(const uint32_t* packed, int64_t rows, int64_t k, uint32_t* out,
+                         void* stream) {
+  if (rows < 0 || k < 0) return fail(DBF_EINVAL, "negative size");
+  if (rows == 0 || k == 0) return DBF_OK;
+  if (!packed || !out) return fail(DBF_EINVAL, "NULL pointer");
+  if (!aligned16(packed) || !aligned16(out)) return fail(DBF_EALIGN, "packed buffer not 16-byte aligned");
+  const int d = check_device();
+  if (d != DBF_OK) return d;
+  return launched(dbf::launch_transpose_packed(packed, rows, k, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t dbf_backward_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T,
+                                    int path) {
+  if (N <= 0 || M <= 0 || R <= 0 || n_terms <= 0 || T <= 0) return 0;
+  return dbf::backward_ws_bytes(N, M, R, n_terms, T, resolve_path(path, T, 1, kAutoBoolDecodeBlocks));
+}
+
+int dbf_linear_backward(const dbf_term* terms, const dbf_term_t* tterms, int n_terms, int64_t N,
+                        int64_t M, int64_t R, const void* x, int x_dtype, int64_t ldx,
+                        const void* dy, int dy_dtype, int64_t lddy, int64_t T, void* dx,
+                        int dx_dtype, int64_t lddx, float* dalpha, float* dbeta, float* dgamma,
+                        void* ws, size_t ws_bytes, int path, void* stream) {
+  int e = check_terms(terms, n_terms, true, true);
+  if (e != DBF_OK) return e;
+  if (!tterms) return fail(DBF_EINVAL, "tterms is NULL");
+  for (int i = 0; i < n_terms; ++i) {
+    if (!tterms[i].b1t || !tterms[i].b2t) return fail(DBF_EINVAL, "term %d: transposed factor is NULL", i);
+    if (!aligned16(tterms[i].b1t) || !aligned16(tterms[i].b2t))
+      return fail(DBF_EALIGN, "term %d: transposed factor not 16-byte aligned", i);
+  }
+  if (N < 1 || M < 1 || R < 1) return fail(DBF_EINVAL, "N, M, R must be >= 1");
+  if (T < 0) return fail(DBF_EINVAL, "T < 0");
+  if (x_dtype != DBF_BF16 && x_dtype != DBF_F16)
+    return fail(DBF_EDTYPE, "x dtype %d unsupported (bf16 or f16)", x_dtype);
+  if (dy_dtype != DBF_BF16 && dy_dtype != DBF_F16 && dy_dtype != DBF_F32)
+    return fail(DBF_EDTYPE, "dy dtype %d unsupported", dy_dtype);
+  if (dx && !out_dtype_ok(dx_dtype)) return fail(DBF_EDTYPE, "dx dtype %d unsupported", dx_dtype);
+  if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_MFMA)
+    return fail(DBF_EINVAL, "unknown path %d", path);
+  if (T == 0) return DBF_OK;
+  if (!x || !dy) return fail(DBF_EINVAL, "x or dy is NULL");
+  if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
+  if (lddy < N) return fail(DBF_EINVAL, "lddy %lld < N %lld", (long long)lddy, (long long)N);
+  if (dx && lddx < M) return fail(DBF_EINVAL, "lddx %lld < M %lld", (long long)lddx, (long long)M);
+  if (!aligned16(x) || !aligned16(dy) || (dx && !aligned16(dx)))
+    return fail(DBF_EALIGN, "x, dy or dx not 16-byte aligned");
+  if ((dalpha && (reinterpret_cast<uintptr_t>(dalpha) & 3u)) ||
+      (dbeta && (reinterpret_cast<uintptr_t>(dbeta) & 3u)) ||
+      (dgamma && (reinterpret_cast<uintptr_t>(dgamma) & 3u)))
+    return fail(DBF_EALIGN, "a scale gradient is not 4-byte aligned");
+  const int p = resolve_path(path, T, 1, kAutoBoolDecodeBlocks);
+  e = check_ws(ws, ws_bytes, dbf_backward_workspace_bytes(N, M, R, n_terms, T, p));
+  if (e != DBF_OK) return e;
+  e = check_device();
+  if (e != DBF_OK) return e;
+  const dbf::TermPtrs tp = to_ptrs(terms, n_terms);
+  const uint32_t* b1t[DBF_MAX_TERMS];
+  const uint32_t* b2t[DBF_MAX_TERMS];
+  for (int i = 0; i < n_terms; ++i) {
+    b1t[i] = tterms[i].b1t;
+    b2t[i] = tterms[i].b2t;
+  }
+  return launched(dbf::launch_backward(tp, b1t, b2t, N, M, R, x, x_dtype, ldx, dy, dy_dtype, lddy,
+                                       T, dx, dx_dtype, lddx, dalpha, dbeta, dgamma, p, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T, int path) {
   if (N <= 0 || M <= 0 || n_kernels <= 0 || T <= 0) return 0;
   if (resolve_path(path, T, n_kernels, kAutoBoolDecodeBlocks) == DBF_PATH_MFMA)

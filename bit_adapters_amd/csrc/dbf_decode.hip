@@ -261,7 +261,9 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
   a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Wg : 1, &per);
   a.kb_per_split = per;
   a.rs = ws_rstride(R);
-  a.vec4 = (ldx % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 8 == 0) && (M % 4 == 0);
+  // four 16-bit activations per 8-byte load (fp32 input takes the bounded path)
+  a.vec4 = (x_dtype != DBF_F32) && (ldx % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 8 == 0) &&
+           (M % 4 == 0);
   for (int i = 0; i < t.n; ++i)
     if (t.gamma[i] && reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) a.vec4 = 0;
   *n1 = static_cast<int>(a.nrt * a.ks * t.n * a.ntb);

@@ -47,8 +47,10 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __half_as_ushort(__float2half_rn(f));
 }
 
-// Load element i of an activation array of dtype code dt as fp32.
+// Load element i of an activation array of dtype code dt (bf16, f16, or
+// f32 for the backward's fp32 intermediates) as fp32.
 __device__ __forceinline__ float load_act(const void* p, int dt, int64_t i) {
+  if (dt == DBF_F32) return static_cast<const float*>(p)[i];
   const uint16_t v = static_cast<const uint16_t*>(p)[i];
   return dt == DBF_BF16 ? bf16_bits_to_f32(v) : f16_bits_to_f32(v);
 }
@@ -76,6 +78,9 @@ __device__ __forceinline__ void store_out(void* y, int dt, int64_t i, float v,
 
 hipError_t launch_pack(const void* src, int src_dtype, int64_t rows, int64_t k,
                        int64_t ld, uint32_t* packed, hipStream_t s);
+// out = the packed layout of S^T (k rows x `rows`) for the packed S.
+hipError_t launch_transpose_packed(const uint32_t* packed, int64_t rows, int64_t k,
+                                   uint32_t* out, hipStream_t s);
 hipError_t launch_unpack(const uint32_t* packed, int64_t rows, int64_t k,
                          int8_t* dst, int64_t ld, hipStream_t s);
 
@@ -120,6 +125,17 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                        const void* x, int x_dtype, int64_t T, int64_t ldx,
                        void* y, int y_dtype, int64_t ldy, int accumulate,
                        void* ws, hipStream_t s);
+
+// Backward (dx and the scale gradients) from four sign-accumulate products
+// per term; b1t / b2t are the packed transposes of B1 / B2; path is
+// DBF_PATH_DECODE or DBF_PATH_MFMA for every product.
+size_t backward_ws_bytes(int64_t N, int64_t M, int64_t R, int n_terms, int64_t T, int path);
+hipError_t launch_backward(const TermPtrs& t, const uint32_t* const* b1t,
+                           const uint32_t* const* b2t, int64_t N, int64_t M, int64_t R,
+                           const void* x, int x_dtype, int64_t ldx, const void* dy,
+                           int dy_dtype, int64_t lddy, int64_t T, void* dx, int dx_dtype,
+                           int64_t lddx, float* dalpha, float* dbeta, float* dgamma,
+                           int path, void* ws, hipStream_t s);
 
 // Adapter: y = W0 x + sum_i Delta W_i x in one launch (stage 1 of the
 // decode path plus the base product; ws as for the decode path).

@@ -791,7 +791,8 @@ hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void*
   PrepArgs pa{};
   pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
   pa.R = 0; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
-  pa.vec = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  // eight 16-bit activations per 16-byte load (fp32 input takes the bounded path)
+  pa.vec = (x_dtype != DBF_F32) && (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   for (int i = 0; i < t.n; ++i) {
     if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) pa.vec = 0;
     pa.gamma[i] = t.gamma[i];

@@ -266,6 +266,56 @@ int dbf_bool_forward(const dbf_bool_kernel *kernels, int n_kernels, int64_t N,
                      int accumulate, void *ws, size_t ws_bytes, int path,
                      void *stream);
 
+/*
+ * ---- Backward of dbf_linear_forward -------------------------------------
+ * For a loss L with dy = dL/dy, the chain rule through the LoRDBA
+ * parametrization (section 2, "Arquitetura Central"), per term i:
+ *   g_i = B1_i^T (alpha_i . dy),  h_i = B2_i^T (beta_i . g_i),
+ *   s_i = B2_i (gamma_i . x),     z_i = B1_i (beta_i . s_i),
+ *   dx = sum_i gamma_i . h_i,
+ *   dalpha_i = sum_t dy . z_i,  dbeta_i = sum_t s_i . g_i,  dgamma_i = sum_t x . h_i.
+ * The four products per term are sign-accumulates over B2, B1 and their
+ * transposes, which the caller packs once with dbf_transpose_packed.
+ */
+
+/* out = the packed layout of S^T (k rows x `rows` columns; dbf_packed_bytes(k,
+ * rows) bytes, 16-byte aligned) for `packed`, the layout of S (rows x k).
+ * Bit-exact; padding bits are 0. */
+int dbf_transpose_packed(const uint32_t *packed, int64_t rows, int64_t k,
+                         uint32_t *out, void *stream);
+
+typedef struct {
+    const uint32_t *b1t;  /* B1_i^T packed: rows R, k N */
+    const uint32_t *b2t;  /* B2_i^T packed: rows M, k R */
+} dbf_term_t;
+
+/* Workspace bytes of dbf_linear_backward (the head rule of
+ * dbf_workspace_bytes applies). */
+size_t dbf_backward_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
+                                    int64_t T, int path);
+
+/*
+ * Gradients for T tokens.
+ *   terms, tterms    n_terms forward terms (alpha, beta, gamma required) and
+ *                    their packed transposes.
+ *   x  [T x M], x_dtype DBF_BF16 or DBF_F16, ldx;  dy [T x N], dy_dtype
+ *   DBF_BF16, DBF_F16 or DBF_F32, lddy.
+ *   dx [T x M], dx_dtype DBF_F32/BF16/F16, lddx;  dalpha [n_terms x N],
+ *   dbeta [n_terms x R], dgamma [n_terms x M], fp32, contiguous.  Any of
+ *   the four outputs may be NULL (not computed); all are overwritten.
+ *   path             DBF_PATH_AUTO: decode products while T <= 16, MFMA
+ *                    products above; or forced.
+ * The products keep fp32 intermediates; on the MFMA path each product rounds
+ * its scaled input to fp16 once (fp32 sums).  Token sums run in fixed order,
+ * so results are bitwise reproducible.  T = 0 is valid and does nothing.
+ */
+int dbf_linear_backward(const dbf_term *terms, const dbf_term_t *tterms, int n_terms,
+                        int64_t N, int64_t M, int64_t R, const void *x, int x_dtype,
+                        int64_t ldx, const void *dy, int dy_dtype, int64_t lddy,
+                        int64_t T, void *dx, int dx_dtype, int64_t lddx, float *dalpha,
+                        float *dbeta, float *dgamma, void *ws, size_t ws_bytes, int path,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

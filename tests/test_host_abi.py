@@ -221,6 +221,63 @@ def test_bool_auto_path_rule(T, K, path):
     assert auto != D.dbf_bool_workspace_bytes(4096, 4096, K, T, other)
 
 
+def _tts(n=1, **over):
+    arr = (D._CTermT * max(n, 1))()
+    for i in range(n):
+        f = dict(b1t=FAKE, b2t=FAKE)
+        f.update(over)
+        arr[i] = D._CTermT(**f)
+    return arr
+
+
+def bwd(terms=None, tterms=None, n=1, N=8, M=8, R=8, x=FAKE, xdt=D.DBF_BF16, ldx=8,
+        dy=FAKE, dydt=D.DBF_F32, lddy=8, T=1, dx=FAKE, dxdt=D.DBF_F32, lddx=8,
+        da=FAKE, db=FAKE, dg=FAKE, ws=FAKE, wsb=1 << 30, path=0):
+    terms = _terms(n) if terms is None else terms
+    tterms = _tts(n) if tterms is None else tterms
+    return L.dbf_linear_backward(terms, tterms, n, N, M, R, x, xdt, ldx, dy, dydt, lddy, T,
+                                 dx, dxdt, lddx, da, db, dg, ws, wsb, path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), D.DBF_EINVAL), (dict(n=9), D.DBF_EINVAL),
+    (dict(terms=_terms(1, gamma=None)), D.DBF_EINVAL),
+    (dict(tterms=_tts(1, b1t=None)), D.DBF_EINVAL),
+    (dict(tterms=_tts(1, b2t=MIS)), D.DBF_EALIGN),
+    (dict(R=0), D.DBF_EINVAL), (dict(T=-1), D.DBF_EINVAL),
+    (dict(xdt=D.DBF_F32), D.DBF_EDTYPE), (dict(dydt=D.DBF_I8), D.DBF_EDTYPE),
+    (dict(dxdt=D.DBF_I32), D.DBF_EDTYPE), (dict(path=4), D.DBF_EINVAL),
+    (dict(ldx=7), D.DBF_EINVAL), (dict(lddy=7), D.DBF_EINVAL), (dict(lddx=7), D.DBF_EINVAL),
+    (dict(dy=None), D.DBF_EINVAL), (dict(dx=MIS), D.DBF_EALIGN),
+    (dict(db=FAKE + 2), D.DBF_EALIGN),
+    (dict(ws=None), D.DBF_EWORKSPACE), (dict(wsb=64), D.DBF_EWORKSPACE),
+])
+def test_backward_validation(kw, code):
+    assert bwd(**kw) == code
+    assert D.dbf_last_error()
+
+
+def test_backward_optional_outputs_and_zero_tokens():
+    # every output may be NULL; T = 0 does nothing
+    assert bwd(T=0, x=None, dy=None, ws=None, wsb=0) == D.DBF_OK
+    assert bwd(dx=None, lddx=0, da=None, db=None, dg=None, dxdt=99, T=0) == D.DBF_OK
+
+
+def test_transpose_packed_validation():
+    assert L.dbf_transpose_packed(None, 4, 4, FAKE, None) == D.DBF_EINVAL
+    assert L.dbf_transpose_packed(MIS, 4, 4, FAKE, None) == D.DBF_EALIGN
+    assert L.dbf_transpose_packed(FAKE, -1, 4, FAKE, None) == D.DBF_EINVAL
+    assert L.dbf_transpose_packed(FAKE, 0, 4, FAKE, None) == D.DBF_OK
+
+
+def test_backward_workspace_bytes():
+    assert D.dbf_backward_workspace_bytes(64, 64, 32, 1, 0) == 0
+    small = D.dbf_backward_workspace_bytes(512, 512, 256, 1, 8)
+    # at least the four fp32 intermediates
+    assert small >= 4 * 8 * (256 + 512 + 256 + 512)
+    assert D.dbf_backward_workspace_bytes(512, 512, 256, 2, 8) > small
+
+
 def test_header_compiles_as_c(tmp_path):
     # the ABI header is plain C: no HIP or C++ type in any declaration
     src = tmp_path / "h.c"
