@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--shared", action="store_true",
+                    help="LoRDBA's envelope form: every term on term 0's B1 and B2 "
+                         "(own scales); multi-term configurations")
     ap.add_argument("--backward", action="store_true",
                     help="time dbf_linear_backward (dx and every scale gradient) instead")
     ap.add_argument("--copy-probe", action="store_true",
@@ -149,6 +152,12 @@ def main():
     else:
         layer = S.make_layer(args.config, R=args.rank if base else None)
         N, M, R, L = layer["N"], layer["M"], layer["R"], len(layer["terms"])
+        if args.shared:
+            if L < 2:
+                print("--shared needs a multi-term configuration (4)", file=sys.stderr)
+                sys.exit(2)
+            for t in layer["terms"][1:]:
+                t["b1"], t["b2"] = layer["terms"][0]["b1"], layer["terms"][0]["b2"]
         for t in layer["terms"]:
             terms0.append(D.DbfTerm(
                 D.dbf_pack(torch.from_numpy(t["b1"]).to(DEV)),
@@ -169,6 +178,8 @@ def main():
             return sum(nbytes(u) for u in t)
         return sum(v.numel() * v.element_size() for v in t)
 
+    if args.shared:
+        terms0 = [terms0[0]] + [tcls(terms0[0].b1, terms0[0].b2, *t[2:]) for t in terms0[1:]]
     copy_bytes = sum(nbytes(t) for t in terms0)
     if base:
         copy_bytes += w0.numel() * 2
@@ -178,6 +189,9 @@ def main():
         if args.backward:
             copies.append(([(type(a)(*[v.clone() for v in a]), type(b)(*[v.clone() for v in b]))
                             for a, b in terms0], None))
+        elif args.shared:
+            b1, b2 = terms0[0].b1.clone(), terms0[0].b2.clone()
+            copies.append(([tcls(b1, b2, *[v.clone() for v in t[2:]]) for t in terms0], None))
         else:
             copies.append(([tcls(*[v.clone() for v in t]) for t in terms0],
                            w0.clone() if base else None))
@@ -230,6 +244,11 @@ def main():
 
     if args.backward:
         bytes_alg, flops = algorithmic_backward(N, M, R, L, T)
+    elif args.shared:
+        # the signs once, every term's scales
+        bytes_alg, flops = algorithmic(args.config, N, M, R, 1, T, False)
+        bytes_alg += 2.0 * (L - 1) * (N + R + M)
+        flops *= L
     elif boolk:
         bytes_alg, flops = algorithmic_bool(N, M, L, T)
     else:
@@ -273,6 +292,8 @@ def main():
         copy_probe = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4}
 
     name = cfgd["name"] + ("-r%d" % R if base else "") + ("-backward" if args.backward else "")
+    if args.shared:
+        name = "lordba-envelope-%dx%d-r%d-l%d-shared" % (N, M, R, L)
     shape = ({"N": N, "M": M, "kernels": L} if boolk else
              {"N": N, "M": M, "R": R, "terms": L})
     out = {

@@ -22,6 +22,24 @@ namespace {
 
 using namespace lut;
 
+// Shared carriers (LoRDBA's envelope form: every term has the same B1 and
+// the same B2, only the scales differ), up to kSharedTerms terms and
+// kSharedMaxT tokens: one workgroup runs all terms over one load of the
+// signs.  The one-token decode is bound by its table work and latency
+// rather than by the sign bytes, so this gains little (19.1 -> 18.4 us on
+// three terms of 11008 x 4096, R 2048, one token), and with more tokens the
+// folded workgroups are too few (8 tokens: 47 -> 51 us); above kSharedMaxT
+// tokens shared carriers take the per-term path.
+constexpr int kSharedTerms = 4;
+constexpr int64_t kSharedMaxT = 4;
+
+bool shared_carriers(const TermPtrs& t, int64_t T) {
+  if (t.n < 2 || t.n > kSharedTerms || T > kSharedMaxT) return false;
+  for (int i = 1; i < t.n; ++i)
+    if (t.b1[i] != t.b1[0] || t.b2[i] != t.b2[0]) return false;
+  return true;
+}
+
 struct Stage2 {
   TermPtrs t;
   int64_t T, N, R, nkb;
@@ -38,6 +56,97 @@ struct Stage2 {
   unsigned n2;
   int64_t nrt;      // row tiles of N; workgroup = (token block, row tile)
 };
+
+// The sum over the K-split partials of w_term[tok][k .. k + 4) (all partial
+// loads issued before the sum, summed in split order), as stage 2's act4.
+template <typename A, int MODE>
+__device__ __forceinline__ void w4(const Stage2& p, int term, int64_t tt, int64_t k, int64_t rt,
+                                   A* v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = A(0);
+  if (tt >= p.T || k >= p.R) return;
+  const int64_t base = (static_cast<int64_t>(term) * p.ks * p.T + tt) * p.rs + k;
+  using PT = typename std::conditional<MODE == MODE_F, float, int32_t>::type;
+  using PT4 = typename std::conditional<MODE == MODE_F, float4, int4>::type;
+  const PT* wsp = static_cast<const PT*>(p.ws);
+  PT4 q[kMaxKS];
+#pragma unroll
+  for (int s = 0; s < kMaxKS; ++s)
+    if (s < p.ks) q[s] = load_shared4<PT4>(wsp + base + s * p.T * p.rs);
+  PT4 sum = q[0];
+#pragma unroll
+  for (int s = 1; s < kMaxKS; ++s)
+    if (s < p.ks) {
+      sum.x += q[s].x; sum.y += q[s].y; sum.z += q[s].z; sum.w += q[s].w;
+    }
+  const PT sv[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (k + j >= p.R) continue;
+    if constexpr (MODE == MODE_I8_BETA)
+      v[j] = f16_bits_to_f32(p.t.beta[term][k + j]) * static_cast<float>(sv[j]);
+    else
+      v[j] = sv[j];
+    if constexpr (MODE != MODE_F) {
+      if (rt == 0 && p.s1_out) p.s1_out[(term * p.T + tt) * p.R + k + j] = sv[j];
+    }
+  }
+}
+
+// Shared carriers (every term's B1 is the same matrix): each pass's sign
+// words are loaded once and serve the tables of all the terms.
+template <typename A, int TB, int KW, int NI>
+__device__ __forceinline__ void stage2_shared_role(const Stage2& p, int64_t bid2, A* tbl, A* red) {
+  constexpr int PW = pw_of(TB);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t tblk = bid2 / p.nrt;
+  const int64_t rt = bid2 - tblk * p.nrt;
+  const int64_t row = rt * 64 + lane;
+  uint32_t wd[PW][KW];
+  load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
+  const unsigned ticket = wait_producers(p.sync, false);  // partials via load_shared4
+  const int64_t tok0 = tblk * TB;
+  A acc[NI][TB];
+#pragma unroll
+  for (int q = 0; q < NI; ++q)
+#pragma unroll
+    for (int i = 0; i < TB; ++i) acc[q][i] = A(0);
+  bool have_bits = true;
+  for (int64_t kp = 0; kp < p.nkb; kp += kWaves * PW) {
+    if (!have_bits) load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, kp, p.nkb, wd);
+    have_bits = false;
+    const int64_t kb_end = min(p.nkb, kp + kWaves * PW);
+    const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
+    const int64_t kbase = kp * 32 * KW;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      if (q >= p.t.n) break;
+      auto act4 = [&](int tok, int g, A* v) { w4<A, MODE_F>(p, q, tok0 + tok, kbase + 4 * g, rt, v); };
+      tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc[q]);
+    }
+  }
+  float yacc[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) yacc[i] = 0.f;
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    if (q >= p.t.n) break;
+    reduce_waves<A, TB>(red, acc[q]);
+    if (wv == 0 && row < p.N) {
+      const float a_n = f16_bits_to_f32(p.t.alpha[q][row]);
+#pragma unroll
+      for (int tok = 0; tok < TB; ++tok) yacc[tok] += a_n * static_cast<float>(acc[q][tok]);
+    }
+  }
+  if (wv == 0 && row < p.N) {
+#pragma unroll
+    for (int tok = 0; tok < TB; ++tok) {
+      const int64_t tt = tok0 + tok;
+      if (tt < p.T) store_out(p.y, p.y_dtype, tt * p.ldy + row, yacc[tok], p.accumulate);
+    }
+  }
+  consumer_done(p.sync, ticket);
+}
 
 template <typename A, int TB, int KW, int MODE>
 __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tbl, A* red) {
@@ -65,40 +174,8 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
         const int64_t kb_end = min(p.nkb, kp + kWaves * PW);
         const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
         const int64_t kbase = kp * 32 * KW;
-        // group g of the pass: w[tok][k .. k + 4) summed over the K-split
-        // partials (all partial loads issued before the sum, summed in order)
-        auto act4 = [&](int tok, int g, A* v) {
-          const int64_t tt = tok0 + tok, k = kbase + 4 * g;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = A(0);
-          if (tt >= p.T || k >= p.R) return;
-          const int64_t base = (static_cast<int64_t>(term) * p.ks * p.T + tt) * p.rs + k;
-          using PT = typename std::conditional<MODE == MODE_F, float, int32_t>::type;
-          using PT4 = typename std::conditional<MODE == MODE_F, float4, int4>::type;
-          const PT* wsp = static_cast<const PT*>(p.ws);
-          PT4 q[kMaxKS];
-#pragma unroll
-          for (int s = 0; s < kMaxKS; ++s)
-            if (s < p.ks) q[s] = load_shared4<PT4>(wsp + base + s * p.T * p.rs);
-          PT4 sum = q[0];
-#pragma unroll
-          for (int s = 1; s < kMaxKS; ++s)
-            if (s < p.ks) {
-              sum.x += q[s].x; sum.y += q[s].y; sum.z += q[s].z; sum.w += q[s].w;
-            }
-          const PT sv[4] = {sum.x, sum.y, sum.z, sum.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (k + j >= p.R) continue;
-            if constexpr (MODE == MODE_I8_BETA)
-              v[j] = f16_bits_to_f32(p.t.beta[term][k + j]) * static_cast<float>(sv[j]);
-            else
-              v[j] = sv[j];
-            if constexpr (MODE != MODE_F) {
-              if (rt == 0 && p.s1_out) p.s1_out[(term * p.T + tt) * p.R + k + j] = sv[j];
-            }
-          }
-        };
+        // group g of the pass: w[tok][k .. k + 4) of this term
+        auto act4 = [&](int tok, int g, A* v) { w4<A, MODE>(p, term, tok0 + tok, kbase + 4 * g, rt, v); };
         tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc);
       }
       reduce_waves<A, TB>(red, acc);
@@ -126,7 +203,8 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   consumer_done(p.sync, ticket);
 }
 
-template <typename A, int TB, int KW1, int KW2, int MODE>
+// NI > 1: shared carriers, up to NI terms on the same signs per workgroup.
+template <typename A, int TB, int KW1, int KW2, int MODE, int NI = 1>
 __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, int n1,
                                                           int run_stage2) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -135,11 +213,14 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, 
   A* red = tbl + tbl_elems<TB, KWM>();
   const int bid = blockIdx.x;
   if (bid < n1) {
-    stage1_role<A, TB, KW1, MODE>(s1, bid, tbl, red);
+    stage1_role<A, TB, KW1, MODE, NI>(s1, bid, tbl, red);
     if (run_stage2) publish(s2.sync, static_cast<unsigned>(bid));
     return;
   }
-  stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
+  if constexpr (NI > 1)
+    stage2_shared_role<A, TB, KW2, NI>(s2, bid - n1, tbl, red);
+  else
+    stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
 }
 
 constexpr int64_t kStage1Wg = 512;
@@ -204,12 +285,12 @@ __global__ void __launch_bounds__(kThreads) bool_decode_kernel(Stage1 s1, SumArg
   sum_role<TB>(s2, bid - n1);
 }
 
-template <typename A, int MODE>
+template <typename A, int MODE, int NI = 1>
 hipError_t run(const Stage1& s1, const Stage2& s2, int n1, int n2, int run_stage2,
                int tb, int kw1, int kw2, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(n1 + (run_stage2 ? n2 : 0));
 #define DBF_LAUNCH(TB_, K1_, K2_)                                                        \
-  decode_kernel<A, TB_, K1_, K2_, MODE>                                                  \
+  decode_kernel<A, TB_, K1_, K2_, MODE, NI>                                              \
       <<<dim3(grid), kThreads, lds_bytes<A, TB_, (K1_ > K2_ ? K1_ : K2_)>(), s>>>(        \
           s1, s2, n1, run_stage2)
 #define DBF_K2(TB_, K1_)                     \
@@ -251,14 +332,16 @@ Stage2 make_stage2(const TermPtrs& t, const Stage1& s1, int64_t N, int64_t R, in
 }  // namespace
 
 lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, int x_dtype,
-                        int64_t T, int64_t ldx, void* ws, bool split, int* n1) {
+                        int64_t T, int64_t ldx, void* ws, bool split, int* n1,
+                        bool allow_shared) {
   lut::Stage1 a{};
   a.t = t; a.x = x; a.x_dtype = x_dtype; a.ldx = ldx; a.T = T; a.M = M; a.R = R;
   a.nkb = layout_nkb(M);
   a.nrt = layout_nrt(R);
   int64_t per = 0;
   a.ntb = static_cast<int>((T + lut::pick_tb(T) - 1) / lut::pick_tb(T));
-  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Wg : 1, &per);
+  a.inner = allow_shared && shared_carriers(t, T) ? t.n : 1;
+  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n / a.inner, a.nkb, split ? kStage1Wg : 1, &per);
   a.kb_per_split = per;
   a.rs = ws_rstride(R);
   // four 16-bit activations per 8-byte load (fp32 input takes the bounded path)
@@ -266,7 +349,7 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
            (M % 4 == 0);
   for (int i = 0; i < t.n; ++i)
     if (t.gamma[i] && reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) a.vec4 = 0;
-  *n1 = static_cast<int>(a.nrt * a.ks * t.n * a.ntb);
+  *n1 = static_cast<int>(a.nrt * a.ks * (t.n / a.inner) * a.ntb);
   a.ws = static_cast<unsigned char*>(ws) + kWsHeadBytes;
   return a;
 }
@@ -274,8 +357,11 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
 size_t decode_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t T) {
   int64_t per = 0;
   const int64_t ntb = (T + lut::pick_tb(T) - 1) / lut::pick_tb(T);
-  const int ks = std::max(lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
-                          lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per));
+  // the most splits any call of these sizes picks: with separate carriers,
+  // or with shared ones (one workgroup per row tile for all terms)
+  const int ks = std::max({lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
+                           lut::pick_ks(layout_nrt(R) * ntb, 1, layout_nkb(M), kStage1Wg, &per),
+                           lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per)});
   return kWsHeadBytes + static_cast<size_t>(n_terms) * ks * static_cast<size_t>(T) *
                                    static_cast<size_t>(ws_rstride(R)) * 4u;
 }
@@ -285,11 +371,14 @@ hipError_t launch_decode(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                          void* y, int y_dtype, int64_t ldy, int accumulate,
                          void* ws, hipStream_t s) {
   int n1 = 0;
-  const Stage1 a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1);
+  const Stage1 a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1, true);
   Stage2 b = make_stage2(t, a, N, R, T, ws, n1);
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
-  return run<float, MODE_F>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T),
-                            static_cast<int>(layout_kw(M)), static_cast<int>(layout_kw(R)), s);
+  const int kw1 = static_cast<int>(layout_kw(M)), kw2 = static_cast<int>(layout_kw(R));
+  if (a.inner > 1)
+    return run<float, MODE_F, kSharedTerms>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1,
+                                            kw2, s);
+  return run<float, MODE_F>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1, kw2, s);
 }
 
 hipError_t launch_bool_decode(const TermPtrs& t, int64_t N, int64_t M, const void* x,

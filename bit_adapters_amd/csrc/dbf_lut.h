@@ -185,29 +185,34 @@ struct Stage1 {
   int64_t nkb, kb_per_split, nrt;
   int ks;
   int ntb;        // token blocks (of TB tokens), one per workgroup
+  int inner;      // terms one workgroup runs over the same signs (shared
+                  // carriers: all L; otherwise 1)
   void* ws;       // partials [L][ks][T][rs]
   int64_t rs;
   int vec4;       // x rows allow 8-byte loads of four activations
 };
 
-// Stage-1 workgroup `bid` in [0, ntb * L * nrt * ks): its token block, row
-// tile of B2_term and K-blocks [kb0, kb1) of its split (one or more passes).
-template <typename A, int TB, int KW, int MODE>
+// Stage-1 workgroup `bid` in [0, ntb * (L / inner) * nrt * ks): its token
+// block, row tile of B2, K-blocks [kb0, kb1) of its split (one or more
+// passes) and terms [term0, term0 + inner).  With shared carriers
+// (inner = L <= NI) every pass's sign words are loaded once and serve the
+// tables of all the terms.
+template <typename A, int TB, int KW, int MODE, int NI = 1>
 __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
   constexpr int PW = pw_of(TB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int per_tb = p.t.n * static_cast<int>(p.nrt) * p.ks;
+  const int inner = NI > 1 ? p.inner : 1;
+  const int per_tb = (p.t.n / inner) * static_cast<int>(p.nrt) * p.ks;
   const int tblk = bid / per_tb;
   bid -= tblk * per_tb;
   const int per_term = static_cast<int>(p.nrt) * p.ks;
-  const int term = bid / per_term;
-  const int rem = bid - term * per_term;
+  const int term0 = (bid / per_term) * inner;
+  const int rem = bid - (term0 / inner) * per_term;
   const int64_t rt = rem / p.ks;
   const int split = rem - static_cast<int>(rt) * p.ks;
   const int64_t kb0 = static_cast<int64_t>(split) * p.kb_per_split;
   const int64_t kb1 = min(p.nkb, kb0 + p.kb_per_split);
-  const uint16_t* gam = p.t.gamma[term];
-  const uint32_t* bits = p.t.b2[term];
+  const uint32_t* bits = p.t.b2[term0];
   const int64_t row = rt * 64 + lane;
 
   uint32_t wd[PW][KW];
@@ -215,15 +220,21 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
   bool have_bits = true;
   {
     const int64_t tok0 = static_cast<int64_t>(tblk) * TB;
-    A acc[TB];
+    A acc[NI][TB];
 #pragma unroll
-    for (int i = 0; i < TB; ++i) acc[i] = A(0);
+    for (int q = 0; q < NI; ++q)
+#pragma unroll
+      for (int i = 0; i < TB; ++i) acc[q][i] = A(0);
     for (int64_t kp = kb0; kp < kb1; kp += kWaves * PW) {
       if (!have_bits) load_pass_bits<TB, KW>(bits, rt, p.nkb, kp, kb1, wd);
       have_bits = false;
       const int64_t kb_end = min(kb1, kp + kWaves * PW);
       const int64_t k0 = kp * 32 * KW;
       const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
+#pragma unroll
+      for (int q = 0; q < NI; ++q) {
+      if (q >= inner) break;
+      const uint16_t* gam = p.t.gamma[term0 + q];
       auto act4 = [&](int tok, int g, A* a) {
         const int64_t tt = tok0 + tok, k = k0 + 4 * g;
         if constexpr (MODE == MODE_F) {
@@ -254,19 +265,25 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
           a[j] = v;
         }
       };
-      tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc);
+      tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc[q]);
+      }
     }
-    reduce_waves<A, TB>(red, acc);
-    if (wv == 0 && row < p.R) {
 #pragma unroll
-      for (int tok = 0; tok < TB; ++tok) {
-        const int64_t tt = tok0 + tok;
-        if (tt < p.T) {
-          const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
-          if constexpr (MODE == MODE_F)
-            store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(p.t.beta[term][row]) * acc[tok]);
-          else
-            store_shared(static_cast<int32_t*>(p.ws) + o, static_cast<int32_t>(acc[tok]));
+    for (int q = 0; q < NI; ++q) {
+      if (q >= inner) break;
+      const int term = term0 + q;
+      reduce_waves<A, TB>(red, acc[q]);
+      if (wv == 0 && row < p.R) {
+#pragma unroll
+        for (int tok = 0; tok < TB; ++tok) {
+          const int64_t tt = tok0 + tok;
+          if (tt < p.T) {
+            const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
+            if constexpr (MODE == MODE_F)
+              store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(p.t.beta[term][row]) * acc[q][tok]);
+            else
+              store_shared(static_cast<int32_t*>(p.ws) + o, static_cast<int32_t>(acc[q][tok]));
+          }
         }
       }
     }
@@ -381,8 +398,11 @@ inline int pick_ks(int64_t nrt, int n_terms, int64_t nkb, int64_t want_wg,
 // stage 1 has enough workgroups when `split`, else as few splits as the
 // partial buffer allows); *n1 = its number of workgroups.  ws is the
 // caller's workspace (counters first).
+// allow_shared: the caller's kernel folds the terms of shared carriers
+// into one workgroup (stage1_role with NI > 1); other kernels must pass
+// false.
 lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x,
                         int x_dtype, int64_t T, int64_t ldx, void* ws, bool split,
-                        int* n1);
+                        int* n1, bool allow_shared = false);
 
 }  // namespace dbf

@@ -137,3 +137,50 @@ def test_shared_workspace_head_stays_clear():
     D.dbf_workspace_check(ws)
     assert not ws[:D.DBF_WS_HEAD_BYTES].any()
     assert_close(to_np(y), ref + o.dense(O.widen_bf16(layer["w0"]), x64(x)))
+
+
+def _shared_layer(N, M, R, L, T, seed, share_b2=True):
+    # LoRDBA's envelope form: every term on the same B1 (and B2), own scales
+    layer, x = S.make_custom(N, M, R, L, T, seed=seed)
+    for t in layer["terms"][1:]:
+        t["b1"] = layer["terms"][0]["b1"]
+        if share_b2:
+            t["b2"] = layer["terms"][0]["b2"]
+    return layer, x
+
+
+def _shared_terms(layer, share_b2=True):
+    terms = device_terms(layer)
+    out = [terms[0]]
+    for t in terms[1:]:
+        out.append(D.DbfTerm(terms[0].b1, terms[0].b2 if share_b2 else t.b2, t.alpha,
+                             t.beta, t.gamma))
+    return out
+
+
+@pytest.mark.parametrize("N,M,R,L,T", [(256, 512, 128, 2, 1), (300, 1000, 96, 3, 5),
+                                       (65, 33, 17, 4, 3), (4096, 4096, 2048, 3, 1),
+                                       (1000, 4096, 512, 4, 3), (1000, 4096, 512, 4, 16), (130, 300, 70, 5, 2),
+                                       (512, 2048, 256, 2, 20)])
+def test_shared_carriers(N, M, R, L, T):
+    # up to 4 terms and 4 tokens one workgroup runs all terms over one load
+    # of the signs; five terms, or more tokens, take the per-term path
+    print("shared carriers", N, M, R, L, T, flush=True)
+    layer, x = _shared_layer(N, M, R, L, T, seed=L + N)
+    terms = _shared_terms(layer)
+    y = D.dbf_linear_forward(terms, N, M, R, x_dev(x), path=PATH)
+    torch.cuda.synchronize()
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close(to_np(y), ref)
+    y2 = D.dbf_linear_forward(terms, N, M, R, x_dev(x), path=PATH)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+def test_partly_shared_carriers():
+    # B1 shared, B2 not: the per-term path
+    layer, x = _shared_layer(200, 700, 64, 3, 4, seed=77, share_b2=False)
+    terms = _shared_terms(layer, share_b2=False)
+    y = D.dbf_linear_forward(terms, 200, 700, 64, x_dev(x), path=PATH)
+    torch.cuda.synchronize()
+    assert_close(to_np(y), O.default().forward(O.terms64(layer), x64(x)))
