@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--shared", action="store_true",
                     help="LoRDBA's envelope form: every term on term 0's B1 and B2 "
                          "(own scales); multi-term configurations")
+    ap.add_argument("--multi", type=int, default=0,
+                    help="config 3: K adapters beside one base, token t on adapter t %% K "
+                         "(lordba_multi_adapter_forward)")
     ap.add_argument("--backward", action="store_true",
                     help="time dbf_linear_backward (dx and every scale gradient) instead")
     ap.add_argument("--copy-probe", action="store_true",
@@ -171,6 +174,16 @@ def main():
         terms0 = [(t, D.dbf_term_t(t, N, M, R)) for t in terms0]
         dy = dev_bf16(S.f32_to_bf16_bits(np.random.default_rng([0xDBF, 106, T, N]).standard_normal(
             (T, N), dtype=np.float32)))
+    multi = args.multi
+    if multi:
+        if not base or multi > D.DBF_MAX_ADAPTERS:
+            print("--multi K needs config 3 and 1 <= K <= %d" % D.DBF_MAX_ADAPTERS, file=sys.stderr)
+            sys.exit(2)
+        # K adapters of the configuration's rank: adapter 0 is the layer's own,
+        # the others are its clones (same values, separate memory)
+        terms0 = [terms0[0]] + [type(terms0[0])(*[v.clone() for v in terms0[0]])
+                                for _ in range(multi - 1)]
+        midx = torch.arange(T, dtype=torch.int32, device=DEV) % multi
     tcls = type(terms0[0])
     w0 = dev_bf16(layer["w0"]) if base else None
     def nbytes(t):
@@ -210,7 +223,9 @@ def main():
 
     def step(i):
         terms, w = copies[i % ncopies]
-        if args.backward:
+        if multi:
+            D.lordba_multi_adapter_forward(w, terms, N, M, R, midx, x, y=y, ws=ws)
+        elif args.backward:
             D.dbf_linear_backward([a for a, _ in terms], [b for _, b in terms], N, M, R, x, dy,
                                   dx_dtype=torch.bfloat16, ws=ws, path=args.path)
         elif boolk:
@@ -244,6 +259,11 @@ def main():
 
     if args.backward:
         bytes_alg, flops = algorithmic_backward(N, M, R, L, T)
+    elif multi:
+        # W0 once, each adapter the batch uses once, x and y
+        bytes_alg, flops = algorithmic(args.config, N, M, R, 1, T, True)
+        used = min(multi, T)
+        bytes_alg += (used - 1) * (R * (N + M) / 8.0 + 2.0 * (N + R + M))
     elif args.shared:
         # the signs once, every term's scales
         bytes_alg, flops = algorithmic(args.config, N, M, R, 1, T, False)
@@ -294,6 +314,8 @@ def main():
     name = cfgd["name"] + ("-r%d" % R if base else "") + ("-backward" if args.backward else "")
     if args.shared:
         name = "lordba-envelope-%dx%d-r%d-l%d-shared" % (N, M, R, L)
+    if multi:
+        name += "-multi%d" % multi
     shape = ({"N": N, "M": M, "kernels": L} if boolk else
              {"N": N, "M": M, "R": R, "terms": L})
     out = {
@@ -351,7 +373,10 @@ def verify(layer, x_np, x, y, copy, base, N, M, R, T, args, step_index, ws):
     terms, w = copy
     ye = torch.empty_like(y)
     boolk = args.config in S.BOOL_CONFIGS
-    if boolk:
+    if args.multi:
+        midx = torch.arange(T, dtype=torch.int32, device=DEV) % args.multi
+        D.lordba_multi_adapter_forward(w, terms, N, M, R, midx, x, y=ye, ws=ws)
+    elif boolk:
         D.dbf_bool_forward(terms, N, M, x, y=ye, ws=ws, path=args.path)
     elif base:
         D.lordba_adapter_forward(w, terms, N, M, R, x, y=ye, ws=ws)

@@ -29,13 +29,15 @@ DBF_F16, DBF_BF16, DBF_F32, DBF_I8, DBF_I32 = 1, 2, 3, 4, 5
 DBF_PATH_AUTO, DBF_PATH_DECODE, DBF_PATH_MFMA = 0, 1, 2
 DBF_MAX_TERMS = 8
 DBF_WS_HEAD_BYTES = 16640
+DBF_MAX_ADAPTERS = 32
 
 EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
            "dbf_packed_bytes", "dbf_pack", "dbf_unpack", "dbf_workspace_bytes",
            "dbf_linear_forward", "dbf_linear_forward_i8",
            "lordba_adapter_forward", "dbf_workspace_check",
            "dbf_bool_workspace_bytes", "dbf_bool_forward", "dbf_transpose_packed",
-           "dbf_backward_workspace_bytes", "dbf_linear_backward")
+           "dbf_backward_workspace_bytes", "dbf_linear_backward",
+           "lordba_multi_adapter_forward")
 
 
 class _CTerm(ctypes.Structure):
@@ -90,6 +92,10 @@ def library() -> ctypes.CDLL:
         ctypes.POINTER(_CTerm), ctypes.POINTER(_CTermT), _int, _i64, _i64, _i64,
         _vp, _int, _i64, _vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp,
         _vp, _sz, _int, _vp]
+    lib.lordba_multi_adapter_forward.restype = _int
+    lib.lordba_multi_adapter_forward.argtypes = [
+        _vp, _i64, ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _vp, _i64, _i64,
+        _vp, _int, _i64, _vp, _sz, _vp]
     lib.dbf_bool_workspace_bytes.restype = _sz
     lib.dbf_bool_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int]
     lib.dbf_bool_forward.restype = _int
@@ -271,6 +277,24 @@ def dbf_linear_backward(terms: Sequence[DbfTerm], tterms: Sequence[DbfTermT], N:
         path, _stream(stream)))
     scales = [(da[i], db[i], dg[i]) for i in range(L_)] if want_scales else None
     return dx, scales
+
+
+def lordba_multi_adapter_forward(w0: torch.Tensor, adapters: Sequence[DbfTerm], N: int,
+                                 M: int, R: int, adapter_idx: torch.Tensor, x: torch.Tensor,
+                                 y: Optional[torch.Tensor] = None,
+                                 y_dtype: torch.dtype = torch.float32,
+                                 ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[t] = W0 x[t] + Delta W_{adapter_idx[t]} x[t] (int32 indices on the
+    device, -1 = base only)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=y_dtype, device=x.device)
+    ws, wsb = _workspace(dbf_workspace_bytes(N, M, R, 1, T, DBF_PATH_DECODE), x.device, ws)
+    _check(library().lordba_multi_adapter_forward(
+        _ptr(w0), _ld(w0), _terms(adapters), len(adapters), N, M, R, _ptr(adapter_idx),
+        _ptr(x), T, _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), _ptr(ws), wsb,
+        _stream(stream)))
+    return y
 
 
 def dbf_workspace_check(ws: Optional[torch.Tensor], stream=None) -> None:

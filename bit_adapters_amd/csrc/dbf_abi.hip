@@ -123,18 +123,21 @@ const char* dbf_last_error(void) { return g_err; }
 int dbf_workspace_check(void* ws, void* stream) {
   if (!ws) return fail(DBF_EINVAL, "workspace is NULL");
   if (!aligned16(ws)) return fail(DBF_EALIGN, "workspace not 16-byte aligned");
-  // ctr[2] of the handoff head (dbf_lut.h, Sync)
-  unsigned flag = 0;
+  // ctr[2] (a wait gave up) and ctr[3] (an adapter index out of range) of
+  // the handoff head (dbf_lut.h, Sync)
+  unsigned flag[2] = {0, 0};
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(&flag, static_cast<unsigned char*>(ws) + 8, sizeof(flag),
+  hipError_t e = hipMemcpyAsync(flag, static_cast<unsigned char*>(ws) + 8, sizeof(flag),
                                 hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(DBF_ELAUNCH, "reading the workspace failed: %s", hipGetErrorString(e));
-  if (flag == 0) return DBF_OK;
+  if (flag[0] == 0 && flag[1] == 0) return DBF_OK;
   e = hipMemsetAsync(ws, 0, DBF_WS_HEAD_BYTES, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(DBF_ELAUNCH, "clearing the workspace failed: %s", hipGetErrorString(e));
-  return fail(DBF_ESTALLED, "a handoff wait gave up; the outputs of the calls since the last check are not valid");
+  if (flag[0] != 0)
+    return fail(DBF_ESTALLED, "a handoff wait gave up; the outputs of the calls since the last check are not valid");
+  return fail(DBF_EINVAL, "an adapter index was outside [-1, n_adapters); those tokens got the base alone");
 }
 
 size_t dbf_packed_bytes(int64_t rows, int64_t k) {
@@ -278,6 +281,42 @@ int dbf_linear_backward(const dbf_term* terms, const dbf_term_t* tterms, int n_t
   return launched(dbf::launch_backward(tp, b1t, b2t, N, M, R, x, x_dtype, ldx, dy, dy_dtype, lddy,
                                        T, dx, dx_dtype, lddx, dalpha, dbeta, dgamma, p, ws,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int lordba_multi_adapter_forward(const void* w0, int64_t ldw, const dbf_term* adapters,
+                                 int n_adapters, int64_t N, int64_t M, int64_t R,
+                                 const int32_t* adapter_idx, const void* x, int64_t T, int64_t ldx,
+                                 void* y, int y_dtype, int64_t ldy, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (n_adapters < 1 || n_adapters > DBF_MAX_ADAPTERS)
+    return fail(DBF_EINVAL, "n_adapters %d outside 1..%d", n_adapters, DBF_MAX_ADAPTERS);
+  if (!adapters) return fail(DBF_EINVAL, "adapters is NULL");
+  for (int a = 0; a < n_adapters; ++a) {
+    const int e = check_terms(adapters + a, 1, true, true);
+    if (e != DBF_OK) return e;
+  }
+  if (!w0) return fail(DBF_EINVAL, "w0 is NULL");
+  if (N < 1 || M < 1 || R < 1) return fail(DBF_EINVAL, "N, M, R must be >= 1");
+  if (T < 0) return fail(DBF_EINVAL, "T < 0");
+  if (ldw < M) return fail(DBF_EINVAL, "ldw %lld < M %lld", (long long)ldw, (long long)M);
+  if (!out_dtype_ok(y_dtype)) return fail(DBF_EDTYPE, "y dtype %d unsupported", y_dtype);
+  if (!aligned16(w0)) return fail(DBF_EALIGN, "w0 not 16-byte aligned");
+  if (T == 0) return DBF_OK;
+  if (!x || !y || !adapter_idx) return fail(DBF_EINVAL, "x, y or adapter_idx is NULL");
+  if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
+  if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
+  if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(adapter_idx) & 3u)
+    return fail(DBF_EALIGN, "adapter_idx not 4-byte aligned");
+  int e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, 1, T, DBF_PATH_DECODE));
+  if (e != DBF_OK) return e;
+  e = check_device();
+  if (e != DBF_OK) return e;
+  dbf::TermPtrs tp[DBF_MAX_ADAPTERS];
+  for (int a = 0; a < n_adapters; ++a) tp[a] = to_ptrs(adapters + a, 1);
+  return launched(dbf::launch_multi_adapter(static_cast<const uint16_t*>(w0), ldw, tp, n_adapters,
+                                            N, M, R, adapter_idx, x, T, ldx, y, y_dtype, ldy, ws,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T, int path) {

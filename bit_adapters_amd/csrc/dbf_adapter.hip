@@ -73,7 +73,13 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p, int64_t k) {
 constexpr int kMainWaves = lut::kWaves;
 constexpr int kMainThreads = lut::kThreads;
 
-__device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds) {
+// MULTI: each token has its own adapter (tab, idx; one term each) instead of
+// the terms p.t shared by every token.
+// (ptrs: [kMaxAdapters] B1 then [kMaxAdapters] alpha pointers in LDS.)
+template <bool MULTI = false>
+__device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds,
+                                          const void* const* ptrs = nullptr, int nad = 0,
+                                          const int32_t* idx = nullptr) {
   // [waves][16][16] partials of the base, then w staged as [16][kRChunk]
   float (*red)[16][16] = reinterpret_cast<float (*)[16][16]>(lds);
   float* wst = lds + kMainWaves * 16 * 16;
@@ -128,14 +134,23 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
 #pragma unroll
     for (int q = 0; q < kMainWaves; ++q) v += red[q][i][j];
 
-    if (p.t.n > 0) {
+    if (MULTI || p.t.n > 0) {
       if (!waited) {
         ticket = lut::wait_producers(p.sync);
         waited = true;
       }
       const int64_t kw = layout_kw(p.R), nkb = layout_nkb(p.R);
       const int64_t rt = n >> 6, rin = n & 63;
-      for (int term = 0; term < p.t.n; ++term) {
+      // this owner's adapter (MULTI; -1: none)
+      int am = -1;
+      if constexpr (MULTI) {
+        if (owner && tt < p.T) {
+          am = idx[tt];
+          if (am < -1 || am >= nad) am = -1;  // flagged by the stage-1 workgroups
+        }
+      }
+      const int nterms = MULTI ? 1 : p.t.n;
+      for (int term = 0; term < nterms; ++term) {
         float z = 0.f;
         for (int64_t r0 = 0; r0 < p.R; r0 += kRChunk) {
           const int nr = static_cast<int>(min<int64_t>(kRChunk, p.R - r0));
@@ -158,8 +173,8 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
             wst[jt * kRChunk + rr] = s;
           }
           __syncthreads();
-          if (owner && n < p.N && tt < p.T) {
-            const uint32_t* b1 = p.t.b1[term];
+          if (owner && n < p.N && tt < p.T && (!MULTI || am >= 0)) {
+            const uint32_t* b1 = MULTI ? static_cast<const uint32_t*>(ptrs[am]) : p.t.b1[term];
             for (int r1 = 0; r1 < nr; r1 += 32) {
               const int64_t r = r0 + r1;
               const int64_t kb = r / (32 * kw), w = (r % (32 * kw)) / 32;
@@ -171,7 +186,12 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
           }
           __syncthreads();
         }
-        if (n < p.N) v += f16_bits_to_f32(p.t.alpha[term][n]) * z;
+        if constexpr (MULTI) {
+          if (am >= 0 && n < p.N)
+            v += f16_bits_to_f32(static_cast<const uint16_t*>(ptrs[kMaxAdapters + am])[n]) * z;
+        } else {
+          if (n < p.N) v += f16_bits_to_f32(p.t.alpha[term][n]) * z;
+        }
       }
     }
     if (owner && n < p.N && tt < p.T) store_out(p.y, p.y_dtype, tt * p.ldy + n, v, 0);
@@ -191,6 +211,45 @@ __global__ void __launch_bounds__(kMainThreads) adapter_fused(lut::Stage1 s1, Ma
     return;
   }
   main_role(m, static_cast<int64_t>(blockIdx.x) - n1, reinterpret_cast<float*>(smem));
+}
+
+// Several adapters, one per token, beside the one base: stage-1 workgroups
+// hold one token each and run its adapter's B2 (or nothing for -1); the row
+// workgroups stream W0 once for every token, then add each token's
+// alpha . (B1 w) from its own adapter.
+template <int KW>
+__global__ void __launch_bounds__(kMainThreads) adapter_multi(lut::Stage1 s1, Main m,
+                                                              lut::AdapterTable tab,
+                                                              const int32_t* idx, int n1) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid < n1) {
+    // the workgroup's adapter, wave-uniform (so its pointers come from the
+    // arguments by scalar loads)
+    const int a = __builtin_amdgcn_readfirstlane(
+        lut::token_adapter(idx, bid / (static_cast<int>(s1.nrt) * s1.ks), tab, m.sync, true));
+    if (a >= 0) {
+      float* tbl = reinterpret_cast<float*>(smem);
+      float* red = tbl + lut::tbl_elems<1, KW>();
+      lut::stage1_role_src<float, 1, KW, lut::MODE_F>(
+          s1, lut::OneTerm{tab.b2[a], tab.gamma[a], tab.beta[a]}, bid, tbl, red);
+    }
+    lut::publish(m.sync, static_cast<unsigned>(bid));
+    return;
+  }
+  // the adapters' B1 and alpha pointers in LDS (copied by constant index),
+  // for the per-token reads of the row role
+  const void** ptrs = reinterpret_cast<const void**>(
+      smem + sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk));
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int q = 0; q < kMaxAdapters; ++q) {
+      ptrs[q] = tab.b1[q];
+      ptrs[kMaxAdapters + q] = tab.alpha[q];
+    }
+  }
+  __syncthreads();
+  main_role<true>(m, bid - n1, reinterpret_cast<float*>(smem), ptrs, tab.n, idx);
 }
 
 // ---- small ranks: every workgroup derives w itself ------------------------
@@ -462,6 +521,58 @@ __global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
 }
 
 }  // namespace
+
+hipError_t launch_multi_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs* adapters,
+                                int n_adapters, int64_t N, int64_t M, int64_t R,
+                                const int32_t* idx, const void* x, int64_t T, int64_t ldx,
+                                void* y, int y_dtype, int64_t ldy, void* ws, hipStream_t s) {
+  lut::AdapterTable tab{};
+  tab.n = n_adapters;
+  for (int a = 0; a < n_adapters; ++a) {
+    tab.b1[a] = adapters[a].b1[0];
+    tab.b2[a] = adapters[a].b2[0];
+    tab.alpha[a] = adapters[a].alpha[0];
+    tab.beta[a] = adapters[a].beta[0];
+    tab.gamma[a] = adapters[a].gamma[0];
+  }
+  Main m{};
+  m.w0 = w0; m.ldw = ldw; m.N = N; m.M = M; m.R = R; m.T = T;
+  m.ldx = ldx; m.x = static_cast<const uint16_t*>(x); m.y = y;
+  m.y_dtype = y_dtype; m.ldy = ldy;
+  m.kq = ((M + kMainWaves - 1) / kMainWaves + 31) / 32 * 32;
+  m.vec = (ldw % 8 == 0) && (ldx % 8 == 0) &&
+          (reinterpret_cast<uintptr_t>(w0) % 16 == 0) &&
+          (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  m.nmain = static_cast<unsigned>((N + 15) / 16);
+  // stage 1 in one-token blocks (each token its own adapter)
+  int n1 = 0;
+  lut::Stage1 a = make_stage1(adapters[0], M, R, x, DBF_BF16, T, ldx, ws, true, &n1);
+  int64_t per = 0;
+  a.ntb = static_cast<int>(T);
+  for (int q = 0; q < n_adapters; ++q)  // 8-byte gamma loads for every adapter
+    if (reinterpret_cast<uintptr_t>(adapters[q].gamma[0]) % 8 != 0) a.vec4 = 0;
+  a.ks = lut::pick_ks(a.nrt * T, 1, a.nkb, 512, &per);
+  a.kb_per_split = per;
+  n1 = static_cast<int>(a.nrt * a.ks * T);
+  m.ws = static_cast<const float*>(a.ws);
+  m.ks = a.ks;
+  m.rs = a.rs;
+  m.sync = lut::make_sync(ws, n1, m.nmain);
+  const size_t main_lds = sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk) +
+                          2 * kMaxAdapters * sizeof(void*);
+  const int kw = static_cast<int>(layout_kw(M));
+  const dim3 grid(static_cast<unsigned>(n1) + m.nmain);
+#define DBF_MA(KW_) \
+  adapter_multi<KW_><<<grid, kMainThreads, std::max(main_lds, lut::lds_bytes<float, 1, KW_>()), s>>>(a, m, tab, idx, n1)
+  switch (kw) {
+    case 1: DBF_MA(1); break;
+    case 2: DBF_MA(2); break;
+    case 3: DBF_MA(3); break;
+    default: DBF_MA(4); break;
+  }
+#undef DBF_MA
+  return hipGetLastError();
+}
 
 hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
                           int64_t N, int64_t M, int64_t R, const void* x,

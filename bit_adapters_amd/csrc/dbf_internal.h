@@ -137,6 +137,16 @@ hipError_t launch_backward(const TermPtrs& t, const uint32_t* const* b1t,
                            int64_t lddx, float* dalpha, float* dbeta, float* dgamma,
                            int path, void* ws, hipStream_t s);
 
+// Several adapters, one per token (idx[t] in [-1, n_adapters), -1 = base
+// only), in one launch: one-token stage-1 workgroups each run their
+// token's adapter, the row workgroups stream the base once for every token
+// and add each token's adapter term (adapters[a] has n = 1).
+constexpr int kMaxAdapters = DBF_MAX_ADAPTERS;
+hipError_t launch_multi_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs* adapters,
+                                int n_adapters, int64_t N, int64_t M, int64_t R,
+                                const int32_t* idx, const void* x, int64_t T, int64_t ldx,
+                                void* y, int y_dtype, int64_t ldy, void* ws, hipStream_t s);
+
 // Adapter: y = W0 x + sum_i Delta W_i x in one launch (stage 1 of the
 // decode path plus the base product; ws as for the decode path).
 hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,

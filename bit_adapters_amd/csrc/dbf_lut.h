@@ -197,12 +197,42 @@ struct Stage1 {
 // passes) and terms [term0, term0 + inner).  With shared carriers
 // (inner = L <= NI) every pass's sign words are loaded once and serve the
 // tables of all the terms.
+// Where stage 1 takes a term's B2, gamma and beta from: the term table of
+// the launch, or (OneTerm) a single term's pointers, e.g. the adapter of a
+// workgroup's token.
+struct TermSrc {
+  const TermPtrs& t;
+  __device__ const uint32_t* b2(int i) const { return t.b2[i]; }
+  __device__ const uint16_t* gamma(int i) const { return t.gamma[i]; }
+  __device__ const uint16_t* beta(int i) const { return t.beta[i]; }
+  __device__ int n() const { return t.n; }
+};
+struct OneTerm {
+  const uint32_t* b2_;
+  const uint16_t* gamma_;
+  const uint16_t* beta_;
+  __device__ const uint32_t* b2(int) const { return b2_; }
+  __device__ const uint16_t* gamma(int) const { return gamma_; }
+  __device__ const uint16_t* beta(int) const { return beta_; }
+  __device__ int n() const { return 1; }
+};
+
+template <typename A, int TB, int KW, int MODE, int NI = 1, class Src = TermSrc>
+__device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src, int bid, A* tbl,
+                                                A* red);
+
 template <typename A, int TB, int KW, int MODE, int NI = 1>
 __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
+  stage1_role_src<A, TB, KW, MODE, NI>(p, TermSrc{p.t}, bid, tbl, red);
+}
+
+template <typename A, int TB, int KW, int MODE, int NI, class Src>
+__device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src, int bid, A* tbl,
+                                                A* red) {
   constexpr int PW = pw_of(TB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int inner = NI > 1 ? p.inner : 1;
-  const int per_tb = (p.t.n / inner) * static_cast<int>(p.nrt) * p.ks;
+  const int per_tb = (src.n() / inner) * static_cast<int>(p.nrt) * p.ks;
   const int tblk = bid / per_tb;
   bid -= tblk * per_tb;
   const int per_term = static_cast<int>(p.nrt) * p.ks;
@@ -212,7 +242,7 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
   const int split = rem - static_cast<int>(rt) * p.ks;
   const int64_t kb0 = static_cast<int64_t>(split) * p.kb_per_split;
   const int64_t kb1 = min(p.nkb, kb0 + p.kb_per_split);
-  const uint32_t* bits = p.t.b2[term0];
+  const uint32_t* bits = src.b2(term0);
   const int64_t row = rt * 64 + lane;
 
   uint32_t wd[PW][KW];
@@ -234,7 +264,7 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
 #pragma unroll
       for (int q = 0; q < NI; ++q) {
       if (q >= inner) break;
-      const uint16_t* gam = p.t.gamma[term0 + q];
+      const uint16_t* gam = src.gamma(term0 + q);
       auto act4 = [&](int tok, int g, A* a) {
         const int64_t tt = tok0 + tok, k = k0 + 4 * g;
         if constexpr (MODE == MODE_F) {
@@ -280,7 +310,7 @@ __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A*
           if (tt < p.T) {
             const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
             if constexpr (MODE == MODE_F)
-              store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(p.t.beta[term][row]) * acc[q][tok]);
+              store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(src.beta(term)[row]) * acc[q][tok]);
             else
               store_shared(static_cast<int32_t*>(p.ws) + o, static_cast<int32_t>(acc[q][tok]));
           }
@@ -376,6 +406,31 @@ __device__ __forceinline__ void consumer_done(const Sync& s, unsigned ticket) {
       if (threadIdx.x == 0) __hip_atomic_store(s.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
+}
+
+// ---- several adapters, one per token (multi-adapter serving) ------------
+// The adapter table travels in the kernel arguments.  token_adapter reads a
+// token's adapter index; an index outside [-1, n) is taken as -1 (no
+// adapter) and raises flag ctr[3] of the workspace head.
+struct AdapterTable {
+  const uint32_t* b1[kMaxAdapters];
+  const uint32_t* b2[kMaxAdapters];
+  const uint16_t* alpha[kMaxAdapters];
+  const uint16_t* beta[kMaxAdapters];
+  const uint16_t* gamma[kMaxAdapters];
+  int n;
+};
+
+__device__ __forceinline__ int token_adapter(const int32_t* idx, int64_t tok,
+                                             const AdapterTable& tab, const Sync& sync,
+                                             bool flag) {
+  const int a = idx[tok];
+  if (a < -1 || a >= tab.n) {
+    if (flag && threadIdx.x == 0)
+      __hip_atomic_fetch_or(sync.ctr + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return -1;
+  }
+  return a;
 }
 
 // Splits of stage 1 along M (at most kMaxKS, whole K-block groups of 4)

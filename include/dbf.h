@@ -151,7 +151,8 @@ size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
  *   ws      device workspace of earlier calls (not NULL, 16-byte aligned)
  *   stream  the stream those calls ran on; this call waits for it
  * Returns DBF_OK when no wait gave up.  Otherwise it zeroes the head (so the
- * buffer is usable again) and returns DBF_ESTALLED.  Reads 4 bytes and
+ * buffer is usable again) and returns DBF_ESTALLED; or DBF_EINVAL when a
+ * lordba_multi_adapter_forward call met an adapter index out of range.  Reads 4 bytes and
  * synchronizes the stream, so it is not for use inside graph capture. */
 int dbf_workspace_check(void *ws, void *stream);
 
@@ -315,6 +316,36 @@ int dbf_linear_backward(const dbf_term *terms, const dbf_term_t *tterms, int n_t
                         int64_t T, void *dx, int dx_dtype, int64_t lddx, float *dalpha,
                         float *dbeta, float *dgamma, void *ws, size_t ws_bytes, int path,
                         void *stream);
+
+/*
+ * ---- Several adapters in one batch --------------------------------------
+ * LoRDBA's adapters are small enough to keep many beside one frozen base
+ * (section 1: cheap to swap and to communicate).  Each token t uses adapter
+ * adapter_idx[t] of the table, or none (-1):
+ *
+ *   y[t] = W0 x[t] + Delta W_{adapter_idx[t]} x[t].
+ */
+#define DBF_MAX_ADAPTERS 32
+
+/*
+ *   w0, ldw          bf16 base [N x M], shared by every token.
+ *   adapters         host array of n_adapters (1..DBF_MAX_ADAPTERS) one-term
+ *                    adapters of rank R (alpha, beta, gamma required).
+ *   adapter_idx      device int32 [T]: the token's adapter, or -1 for the
+ *                    base alone.  An index outside [-1, n_adapters) is
+ *                    treated as -1 and raises a flag that dbf_workspace_check
+ *                    reports as DBF_EINVAL.
+ *   x                bf16 [T x M], ldx;  y [T x N], y_dtype, ldy.
+ *   ws, ws_bytes     dbf_workspace_bytes(N, M, R, 1, T, DBF_PATH_DECODE).
+ * One launch: one-token workgroups run each token's adapter B2 product while
+ * the row workgroups stream W0 once for every token, then add each token's
+ * alpha . (B1 w) from its own adapter.
+ */
+int lordba_multi_adapter_forward(const void *w0, int64_t ldw, const dbf_term *adapters,
+                                 int n_adapters, int64_t N, int64_t M, int64_t R,
+                                 const int32_t *adapter_idx, const void *x, int64_t T,
+                                 int64_t ldx, void *y, int y_dtype, int64_t ldy, void *ws,
+                                 size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -173,6 +173,16 @@ class Oracle:
         """The packed layout of S^T for the packed S (rows x K)."""
         return self.pack(self.unpack(words, rows, K).T.astype(np.float64))
 
+    def multi_adapter(self, w0, adapters, idx, x) -> np.ndarray:
+        """Several adapters beside one base: y[t] = W0 x[t] + Delta W_a x[t]
+        with a = idx[t] (-1: the base alone), from dense and forward."""
+        y = self.dense(w0, x)
+        idx = np.asarray(idx)
+        for a in sorted(set(int(v) for v in idx if v >= 0)):
+            rows = np.nonzero(idx == a)[0]
+            y[rows] += self.forward([adapters[a]], x[rows])
+        return y
+
     def dense(self, w0, x) -> np.ndarray:
         """W0 x for every token: [T x N] fp64."""
         w0 = np.ascontiguousarray(w0, dtype=np.float64)

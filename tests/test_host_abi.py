@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 import torch
 
@@ -276,6 +277,51 @@ def test_backward_workspace_bytes():
     # at least the four fp32 intermediates
     assert small >= 4 * 8 * (256 + 512 + 256 + 512)
     assert D.dbf_backward_workspace_bytes(512, 512, 256, 2, 8) > small
+
+
+def madd(w0=FAKE, ldw=8, adapters=None, n=2, N=8, M=8, R=8, idx=FAKE, x=FAKE, T=1, ldx=8,
+         y=FAKE, ydt=D.DBF_F32, ldy=8, ws=FAKE, wsb=1 << 30):
+    adapters = _terms(max(n, 1)) if adapters is None else adapters
+    return L.lordba_multi_adapter_forward(w0, ldw, adapters, n, N, M, R, idx, x, T, ldx, y,
+                                          ydt, ldy, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), D.DBF_EINVAL), (dict(n=33), D.DBF_EINVAL),
+    (dict(adapters=_terms(2, beta=None)), D.DBF_EINVAL),
+    (dict(adapters=_terms(2, b1=MIS)), D.DBF_EALIGN),
+    (dict(w0=None), D.DBF_EINVAL), (dict(w0=MIS), D.DBF_EALIGN), (dict(ldw=7), D.DBF_EINVAL),
+    (dict(R=0), D.DBF_EINVAL), (dict(T=-1), D.DBF_EINVAL), (dict(ydt=D.DBF_I8), D.DBF_EDTYPE),
+    (dict(idx=None), D.DBF_EINVAL), (dict(idx=FAKE + 2), D.DBF_EALIGN),
+    (dict(ldx=7), D.DBF_EINVAL), (dict(ldy=7), D.DBF_EINVAL), (dict(x=MIS), D.DBF_EALIGN),
+    (dict(ws=None), D.DBF_EWORKSPACE),
+])
+def test_multi_adapter_validation(kw, code):
+    assert madd(**kw) == code
+    assert D.dbf_last_error()
+
+
+def test_multi_adapter_oracle_composition():
+    # several adapters beside one base, composed from the pinned oracle
+    # functions: all -1 is the base, one adapter for all is adapter mode,
+    # and each token matches its own single-token evaluation
+    o = O.default()
+    from bit_adapters_amd import synth as S
+    ads = [S.make_custom(24, 40, 8, 1, 1, seed=s)[0]["terms"][0] for s in range(3)]
+    layer, x = S.make_custom(24, 40, 8, 1, 7, seed=9, base=True)
+    w0 = O.widen_bf16(layer["w0"])
+    xx = O.widen_bf16(x)
+    ads64 = [dict(b1=a["b1"], b2=a["b2"], alpha=a["alpha"].astype(np.float64),
+                  beta=a["beta"].astype(np.float64), gamma=a["gamma"].astype(np.float64))
+             for a in ads]
+    assert np.array_equal(o.multi_adapter(w0, ads64, [-1] * 7, xx), o.dense(w0, xx))
+    assert np.allclose(o.multi_adapter(w0, ads64, [1] * 7, xx), o.adapter(w0, [ads64[1]], xx),
+                       rtol=1e-13, atol=1e-15)
+    idx = [0, -1, 2, 2, 1, -1, 0]
+    y = o.multi_adapter(w0, ads64, idx, xx)
+    for t, a in enumerate(idx):
+        ref = o.dense(w0, xx[t:t + 1]) + (o.forward([ads64[a]], xx[t:t + 1]) if a >= 0 else 0)
+        assert np.allclose(y[t], ref[0], rtol=1e-13, atol=1e-15)
 
 
 def test_header_compiles_as_c(tmp_path):
