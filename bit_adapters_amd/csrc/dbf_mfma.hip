@@ -76,7 +76,7 @@ struct PrepArgs {
   _Float16* u;  // [L][T][mpad]
   float* l1;    // [L][T]
   float* bmax;  // [L]
-  int vec;      // 16-byte loads of x and gamma allowed
+  int vec;      // 16-byte loads of x and gamma allowed (2: x is fp32)
 };
 
 constexpr int kPrepSeg = 8192;  // features of a row staged in LDS at a time
@@ -103,7 +103,17 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
       for (int64_t c = tid; c < segn / 8; c += 256) {
         const int64_t k0 = seg + 8 * c;
         float a[8];
-        if (p.vec && k0 + 8 <= p.M) {
+        if (p.vec == 2 && k0 + 8 <= p.M) {
+          const float* xf32 = static_cast<const float*>(p.x) + tok * p.ldx + k0;
+          const float4 x0 = *reinterpret_cast<const float4*>(xf32);
+          const float4 x1 = *reinterpret_cast<const float4*>(xf32 + 4);
+          const uint4 gv = *reinterpret_cast<const uint4*>(g + k0);
+          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            a[i] = f16_bits_to_f32(static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)))) * xs[i];
+        } else if (p.vec == 1 && k0 + 8 <= p.M) {
           const uint4 xv = *reinterpret_cast<const uint4*>(xr + k0);
           const uint4 gv = *reinterpret_cast<const uint4*>(g + k0);
           const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -791,8 +801,10 @@ hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void*
   PrepArgs pa{};
   pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
   pa.R = 0; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
-  // eight 16-bit activations per 16-byte load (fp32 input takes the bounded path)
-  pa.vec = (x_dtype != DBF_F32) && (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  // eight 16-bit activations per 16-byte load, or eight fp32 ones per two
+  pa.vec = reinterpret_cast<uintptr_t>(x) % 16 != 0 ? 0
+           : x_dtype == DBF_F32                    ? (ldx % 4 == 0 ? 2 : 0)
+                                                   : (ldx % 8 == 0 ? 1 : 0);
   for (int i = 0; i < t.n; ++i) {
     if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) pa.vec = 0;
     pa.gamma[i] = t.gamma[i];
