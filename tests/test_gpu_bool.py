@@ -140,3 +140,10 @@ def test_zero_tokens():
     x = torch.empty((0, 8), dtype=torch.bfloat16, device=DEV)
     y = D.dbf_bool_forward(dev_kernels(layer), 8, 8, x)
     assert y.shape == (0, 8)
+
+
+@pytest.mark.parametrize("path", [DEC, MF])
+def test_maximum_kernels(path):
+    layer, x = S.make_custom_bool(150, 700, D.DBF_MAX_TERMS, 5, seed=99)
+    y = to_np(run(layer, x, path))
+    assert_close(y, O.default().bool_forward(oracle_kernels(layer), x64(x)))

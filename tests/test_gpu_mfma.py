@@ -160,3 +160,12 @@ def test_split_k_output_dtypes_accumulate_strides():
     torch.cuda.synchronize()
     assert_close(to_np(yb[:, :N]), round_bf16(ref), rel_l2=4e-3)
     assert torch.all(yb[:, N:] == 3.0)
+
+
+@pytest.mark.parametrize("path", [D.DBF_PATH_DECODE, MF])
+def test_maximum_terms(path):
+    # DBF_MAX_TERMS terms, separate carriers
+    L = D.DBF_MAX_TERMS
+    layer, x = S.make_custom(200, 640, 96, L, 6, seed=88)
+    y = to_np(run(layer, x, path=path))
+    assert_close(y, O.default().forward(O.terms64(layer), x64(x)))
