@@ -42,6 +42,53 @@ struct PartArgs {
   float* part;                 // [chunks][L (N + R + M)]
 };
 
+// Four activations at element i (i a multiple of 4): one 16-byte load for
+// fp32, one 8-byte load for bf16 / f16.
+__device__ __forceinline__ float4 load4_act(const void* p, int dt, int64_t i) {
+  if (dt == DBF_F32) return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  const uint16_t h[4] = {uint16_t(v.x), uint16_t(v.x >> 16), uint16_t(v.y), uint16_t(v.y >> 16)};
+  float f[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = dt == DBF_BF16 ? bf16_bits_to_f32(h[e]) : f16_bits_to_f32(h[e]);
+  return make_float4(f[0], f[1], f[2], f[3]);
+}
+
+// Four adjacent columns of one segment and term per thread (every segment
+// length a multiple of 4, dy and x rows aligned for load4_act); the same
+// sums as grad_partial_kernel.
+__global__ void __launch_bounds__(256) grad_partial4_kernel(PartArgs p) {
+  const int64_t ncol = p.L * (p.N + p.R + p.M);
+  const int64_t col = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+  if (col >= ncol) return;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kTokChunk;
+  const int64_t t1 = min(p.T, t0 + kTokChunk);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fma4 = [&](const float4 a, const float4 b) {
+    acc.x += a.x * b.x; acc.y += a.y * b.y; acc.z += a.z * b.z; acc.w += a.w * b.w;
+  };
+  int64_t c = col;
+  if (c < p.L * p.N) {  // dalpha: dy . z
+    const int64_t i = c / p.N, n = c - i * p.N;
+    const float* z = p.z + i * p.T * p.N + n;
+    for (int64_t t = t0; t < t1; ++t)
+      fma4(load4_act(p.dy, p.dy_dtype, t * p.lddy + n), *reinterpret_cast<const float4*>(z + t * p.N));
+  } else if ((c -= p.L * p.N) < p.L * p.R) {  // dbeta: s . g
+    const int64_t i = c / p.R, r = c - i * p.R;
+    const float* s = p.s + i * p.T * p.R + r;
+    const float* g = p.g + i * p.T * p.R + r;
+    for (int64_t t = t0; t < t1; ++t)
+      fma4(*reinterpret_cast<const float4*>(s + t * p.R), *reinterpret_cast<const float4*>(g + t * p.R));
+  } else {  // dgamma: x . h
+    c -= p.L * p.R;
+    const int64_t i = c / p.M, m = c - i * p.M;
+    const float* h = p.h + i * p.T * p.M + m;
+    for (int64_t t = t0; t < t1; ++t)
+      fma4(load4_act(p.x, p.x_dtype, t * p.ldx + m), *reinterpret_cast<const float4*>(h + t * p.M));
+  }
+  *reinterpret_cast<float4*>(p.part + static_cast<int64_t>(blockIdx.y) * ncol + col) = acc;
+}
+
 __global__ void __launch_bounds__(256) grad_partial_kernel(PartArgs p) {
   const int64_t ncol = p.L * (p.N + p.R + p.M);
   const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -87,6 +134,25 @@ __global__ void __launch_bounds__(256) grad_final_kernel(const float* part, int6
   } else if (dgamma) {
     dgamma[c - L * R] = acc;
   }
+}
+
+// dx[t][m .. m + 4) = sum_i gamma_i[m ..] h_i[t][m ..], in term order (M a
+// multiple of 4).
+__global__ void __launch_bounds__(256) grad_dx4_kernel(const float* h, int L, int64_t T,
+                                                        int64_t M, TermPtrs tp, void* dx,
+                                                        int dx_dtype, int64_t lddx) {
+  const int64_t idx = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+  if (idx >= T * M) return;
+  const int64_t t = idx / M, m = idx - t * M;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < L; ++i) {
+    const float4 hv = *reinterpret_cast<const float4*>(h + (i * T + t) * M + m);
+    const float hs[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += f16_bits_to_f32(tp.gamma[i][m + e]) * hs[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_out(dx, dx_dtype, t * lddx + m + e, acc[e], 0);
 }
 
 // dx[t][m] = sum_i gamma_i[m] h_i[t][m], in term order.
@@ -198,12 +264,26 @@ hipError_t launch_backward(const TermPtrs& t, const uint32_t* const* b1t,
     pa.part = reinterpret_cast<float*>(base + lay.part);
     const int64_t ncol = t.n * (N + R + M);
     const int nchunks = static_cast<int>((T + kTokChunk - 1) / kTokChunk);
-    grad_partial_kernel<<<dim3(static_cast<unsigned>((ncol + 255) / 256), nchunks), 256, 0, s>>>(pa);
+    // four columns a thread when no group of four crosses a segment or term
+    // and dy rows are 16-byte aligned fp32
+    auto rows4 = [](const void* p, int dt, int64_t ld) {
+      return ld % 4 == 0 && reinterpret_cast<uintptr_t>(p) % (dt == DBF_F32 ? 16 : 8) == 0;
+    };
+    const bool four = N % 4 == 0 && R % 4 == 0 && M % 4 == 0 && rows4(dy, dy_dtype, lddy) &&
+                      rows4(x, x_dtype, ldx);
+    if (four)
+      grad_partial4_kernel<<<dim3(static_cast<unsigned>((ncol / 4 + 255) / 256), nchunks), 256, 0, s>>>(pa);
+    else
+      grad_partial_kernel<<<dim3(static_cast<unsigned>((ncol + 255) / 256), nchunks), 256, 0, s>>>(pa);
     grad_final_kernel<<<dim3(static_cast<unsigned>((ncol + 255) / 256)), 256, 0, s>>>(
         pa.part, ncol, nchunks, t.n, N, R, M, dalpha, dbeta, dgamma);
     if ((e = hipGetLastError())) return e;
   }
-  if (dx) {
+  if (dx && M % 4 == 0) {
+    grad_dx4_kernel<<<dim3(static_cast<unsigned>((T * M / 4 + 255) / 256)), 256, 0, s>>>(
+        hv, t.n, T, M, t, dx, dx_dtype, lddx);
+    if ((e = hipGetLastError())) return e;
+  } else if (dx) {
     grad_dx_kernel<<<dim3(static_cast<unsigned>((T * M + 255) / 256)), 256, 0, s>>>(
         hv, t.n, T, M, t, dx, dx_dtype, lddx);
     if ((e = hipGetLastError())) return e;
