@@ -101,10 +101,17 @@ def algorithmic_backward(N, M, R, L, T):
     return signs + scales + io, 4.0 * T * R * (N + M) * L
 
 
-def auto_path(T, L, blocks=5):
-    # the library's automatic choice (dbf_abi.hip, resolve_path); the boolean
-    # kernels switch to the MFMA path one 4-token block earlier
+def auto_path(T, L, blocks):
+    # the library's automatic choice for the boolean kernels and the
+    # backward products (dbf_abi.hip, resolve_path)
     return "decode" if T <= 4 or L * ((T + 3) // 4) <= blocks else "mfma"
+
+
+def auto_dbf_path(N, M, R, L, T):
+    # the library's automatic choice for the double-binary forward
+    # (dbf_abi.hip, resolve_dbf_path): decode while T <= 4 or the sign work
+    # of the 4-token blocks is at most 1.5e8 lookups
+    return "decode" if T <= 4 or L * ((T + 3) // 4) * R * (N + M) <= 1.5e8 else "mfma"
 
 
 def main():
@@ -280,7 +287,8 @@ def main():
         path = {1: "decode", 2: "mfma"}.get(args.path) or auto_path(T, 1, 4)
     else:
         path = "adapter" if base else ({1: "decode", 2: "mfma"}.get(args.path)
-                                       or auto_path(T, L, 4 if boolk else 5))
+                                       or (auto_path(T, L, 4) if boolk
+                                           else auto_dbf_path(N, M, R, L, T)))
     # achieved = algorithmic bytes (flops) per step / HIP-event time per step;
     # decode and adapter steps are one kernel launch each, the MFMA step is
     # three (prep, stage-1 GEMM, stage-2 GEMM) and is rated as a whole

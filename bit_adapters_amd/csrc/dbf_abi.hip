@@ -22,22 +22,36 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
 
-// DBF_PATH_AUTO: the decode kernel while T <= 4 or n_terms * ceil(T / 4) <= 5,
-// else the MFMA products.  The decode launch's cost grows with the number
-// of (term, 4-token block) pairs, the MFMA path's barely at these sizes;
-// measured on the 4096 x 4096 R 2048 layer (decode faster up to 20 tokens)
-// and the three-term 11008 x 4096 layer (decode faster up to 4 tokens).
-// The boolean kernels (one product each, over a full N x M sign matrix)
-// cross over one step earlier: decode while T <= 4 or K * ceil(T / 4) <= 4
-// (measured on two 4096 x 4096 kernels, decode level with MFMA at 8 tokens,
-// and three 11008 x 4096 kernels, decode faster up to 4 tokens).
-constexpr int64_t kAutoDecodeBlocks = 5;
+// DBF_PATH_AUTO for the double-binary layer: the decode kernel while T <= 4
+// or its sign work, n_terms * ceil(T / 4) * R * (N + M) sign lookups (every
+// 4-token block runs both products of every term), is at most
+// kAutoDecodeWork; else the MFMA products, whose cost at these token counts
+// is nearly flat.  Measured, decode vs MFMA, each path forced:
+//   512 x 512, R 256: decode faster through 64 tokens (10.8 vs 22.0 us);
+//   4096 x 4096, R 2048: faster through 32 tokens (29.2 vs 31.0 us), slower
+//     from 36 (41.2 vs 31.7 us: stage 1 then runs unsplit);
+//   11008 x 4096, R 2048, three terms: faster at 4 tokens (30.3 vs 42.3 us),
+//     slower from 5 (44.7 vs 42.2 us);
+//   8192 x 8192, R 6144: faster at 4 tokens (29.6 vs 46.5 us), slower at 8
+//     (52.7 vs 46.8 us).
+// The boolean kernels (one product each, over a full N x M sign matrix):
+// decode while T <= 4 or K * ceil(T / 4) <= 4 (two 4096 x 4096 kernels:
+// decode faster at 8 tokens, 16.9 vs 18.5 us, slower at 16; three 11008 x
+// 4096 kernels: faster at 4 tokens, slower at 5).
+constexpr double kAutoDecodeWork = 1.5e8;
 constexpr int64_t kAutoBoolDecodeBlocks = 4;
 
-int resolve_path(int path, int64_t T, int n_terms, int64_t blocks = kAutoDecodeBlocks) {
+int resolve_path(int path, int64_t T, int n_terms, int64_t blocks) {
   if (path != DBF_PATH_AUTO) return path;
   const bool decode = T <= 4 || n_terms * ((T + 3) / 4) <= blocks;
   return decode ? DBF_PATH_DECODE : DBF_PATH_MFMA;
+}
+
+int resolve_dbf_path(int path, int64_t N, int64_t M, int64_t R, int64_t T, int n_terms) {
+  if (path != DBF_PATH_AUTO) return path;
+  const double work = static_cast<double>(n_terms) * static_cast<double>((T + 3) / 4) *
+                      static_cast<double>(R) * (static_cast<double>(N) + static_cast<double>(M));
+  return T <= 4 || work <= kAutoDecodeWork ? DBF_PATH_DECODE : DBF_PATH_MFMA;
 }
 
 constexpr int kMaxDevices = 64;
@@ -177,7 +191,7 @@ int dbf_unpack(const uint32_t* packed, int64_t rows, int64_t k, int8_t* dst,
 size_t dbf_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms,
                            int64_t T, int path) {
   if (N <= 0 || M <= 0 || R <= 0 || n_terms <= 0 || T <= 0) return 0;
-  if (resolve_path(path, T, n_terms) == DBF_PATH_MFMA)
+  if (resolve_dbf_path(path, N, M, R, T, n_terms) == DBF_PATH_MFMA)
     return dbf::mfma_ws_bytes(N, M, R, n_terms, T);
   return dbf::decode_ws_bytes(N, M, R, n_terms, T);
 }
@@ -202,7 +216,7 @@ int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
   if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
   if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
   if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
-  const int p = resolve_path(path, T, n_terms);
+  const int p = resolve_dbf_path(path, N, M, R, T, n_terms);
   e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, n_terms, T, p));
   if (e != DBF_OK) return e;
   e = check_device();

@@ -93,7 +93,6 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
   const int64_t kend = min(p.M, kbeg + p.kq);
   const bool vec = p.vec != 0;
   bool waited = false;
-  unsigned ticket = 0;
 
   for (int64_t tb0 = 0; tb0 < p.T; tb0 += 16) {
     const int64_t tok = tb0 + li;
@@ -136,7 +135,7 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
 
     if (MULTI || p.t.n > 0) {
       if (!waited) {
-        ticket = lut::wait_producers(p.sync);
+        lut::wait_producers(p.sync);
         waited = true;
       }
       const int64_t kw = layout_kw(p.R), nkb = layout_nkb(p.R);
@@ -197,7 +196,9 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
     if (owner && n < p.N && tt < p.T) store_out(p.y, p.y_dtype, tt * p.ldy + n, v, 0);
     __syncthreads();
   }
-  if (waited) lut::consumer_done(p.sync, ticket);
+  // the ticket at the end: a wave's loads return in order, and one taken
+  // right after the wait would hold up this wave's loads of the partials
+  if (waited) lut::consumer_done(p.sync, lut::take_ticket(p.sync));
 }
 
 template <int TB, int KW>

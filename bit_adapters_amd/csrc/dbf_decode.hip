@@ -22,24 +22,6 @@ namespace {
 
 using namespace lut;
 
-// Shared carriers (LoRDBA's envelope form: every term has the same B1 and
-// the same B2, only the scales differ), up to kSharedTerms terms and
-// kSharedMaxT tokens: one workgroup runs all terms over one load of the
-// signs.  The one-token decode is bound by its table work and latency
-// rather than by the sign bytes, so this gains little (19.1 -> 18.4 us on
-// three terms of 11008 x 4096, R 2048, one token), and with more tokens the
-// folded workgroups are too few (8 tokens: 47 -> 51 us); above kSharedMaxT
-// tokens shared carriers take the per-term path.
-constexpr int kSharedTerms = 4;
-constexpr int64_t kSharedMaxT = 4;
-
-bool shared_carriers(const TermPtrs& t, int64_t T) {
-  if (t.n < 2 || t.n > kSharedTerms || T > kSharedMaxT) return false;
-  for (int i = 1; i < t.n; ++i)
-    if (t.b1[i] != t.b1[0] || t.b2[i] != t.b2[0]) return false;
-  return true;
-}
-
 struct Stage2 {
   TermPtrs t;
   int64_t T, N, R, nkb;
@@ -57,9 +39,10 @@ struct Stage2 {
   int64_t nrt;      // row tiles of N; workgroup = (token block, row tile)
 };
 
-// The sum over the K-split partials of w_term[tok][k .. k + 4) (all partial
-// loads issued before the sum, summed in split order), as stage 2's act4.
-template <typename A, int MODE>
+// The sum over the K-split partials of w_term[tok][k .. k + 4) (loads issued
+// BATCH splits at a time, to bound the registers they hold; summed in split
+// order), as stage 2's act4.
+template <typename A, int MODE, int BATCH = 4>
 __device__ __forceinline__ void w4(const Stage2& p, int term, int64_t tt, int64_t k, int64_t rt,
                                    A* v) {
 #pragma unroll
@@ -69,16 +52,35 @@ __device__ __forceinline__ void w4(const Stage2& p, int term, int64_t tt, int64_
   using PT = typename std::conditional<MODE == MODE_F, float, int32_t>::type;
   using PT4 = typename std::conditional<MODE == MODE_F, float4, int4>::type;
   const PT* wsp = static_cast<const PT*>(p.ws);
-  PT4 q[kMaxKS];
+  // at most BATCH splits' loads in flight (registers); more splits take
+  // further rounds
+  constexpr int kBatch = BATCH;
+  PT4 sum;
+  {
+    PT4 q[kBatch];
 #pragma unroll
-  for (int s = 0; s < kMaxKS; ++s)
-    if (s < p.ks) q[s] = load_shared4<PT4>(wsp + base + s * p.T * p.rs);
-  PT4 sum = q[0];
+    for (int s = 0; s < kBatch; ++s)
+      if (s < p.ks) q[s] = load_shared4<PT4>(wsp + base + s * p.T * p.rs);
+    sum = q[0];
 #pragma unroll
-  for (int s = 1; s < kMaxKS; ++s)
-    if (s < p.ks) {
-      sum.x += q[s].x; sum.y += q[s].y; sum.z += q[s].z; sum.w += q[s].w;
-    }
+    for (int s = 1; s < kBatch; ++s)
+      if (s < p.ks) {
+        sum.x += q[s].x; sum.y += q[s].y; sum.z += q[s].z; sum.w += q[s].w;
+      }
+  }
+#pragma unroll
+  for (int s0 = kBatch; s0 < kMaxKS; s0 += kBatch) {
+    if (s0 >= p.ks) break;
+    PT4 q[kBatch];
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s)
+      if (s0 + s < p.ks) q[s] = load_shared4<PT4>(wsp + base + (s0 + s) * p.T * p.rs);
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s)
+      if (s0 + s < p.ks) {
+        sum.x += q[s].x; sum.y += q[s].y; sum.z += q[s].z; sum.w += q[s].w;
+      }
+  }
   const PT sv[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -93,61 +95,6 @@ __device__ __forceinline__ void w4(const Stage2& p, int term, int64_t tt, int64_
   }
 }
 
-// Shared carriers (every term's B1 is the same matrix): each pass's sign
-// words are loaded once and serve the tables of all the terms.
-template <typename A, int TB, int KW, int NI>
-__device__ __forceinline__ void stage2_shared_role(const Stage2& p, int64_t bid2, A* tbl, A* red) {
-  constexpr int PW = pw_of(TB);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t tblk = bid2 / p.nrt;
-  const int64_t rt = bid2 - tblk * p.nrt;
-  const int64_t row = rt * 64 + lane;
-  uint32_t wd[PW][KW];
-  load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
-  const unsigned ticket = wait_producers(p.sync, false);  // partials via load_shared4
-  const int64_t tok0 = tblk * TB;
-  A acc[NI][TB];
-#pragma unroll
-  for (int q = 0; q < NI; ++q)
-#pragma unroll
-    for (int i = 0; i < TB; ++i) acc[q][i] = A(0);
-  bool have_bits = true;
-  for (int64_t kp = 0; kp < p.nkb; kp += kWaves * PW) {
-    if (!have_bits) load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, kp, p.nkb, wd);
-    have_bits = false;
-    const int64_t kb_end = min(p.nkb, kp + kWaves * PW);
-    const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
-    const int64_t kbase = kp * 32 * KW;
-#pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      if (q >= p.t.n) break;
-      auto act4 = [&](int tok, int g, A* v) { w4<A, MODE_F>(p, q, tok0 + tok, kbase + 4 * g, rt, v); };
-      tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc[q]);
-    }
-  }
-  float yacc[TB];
-#pragma unroll
-  for (int i = 0; i < TB; ++i) yacc[i] = 0.f;
-#pragma unroll
-  for (int q = 0; q < NI; ++q) {
-    if (q >= p.t.n) break;
-    reduce_waves<A, TB>(red, acc[q]);
-    if (wv == 0 && row < p.N) {
-      const float a_n = f16_bits_to_f32(p.t.alpha[q][row]);
-#pragma unroll
-      for (int tok = 0; tok < TB; ++tok) yacc[tok] += a_n * static_cast<float>(acc[q][tok]);
-    }
-  }
-  if (wv == 0 && row < p.N) {
-#pragma unroll
-    for (int tok = 0; tok < TB; ++tok) {
-      const int64_t tt = tok0 + tok;
-      if (tt < p.T) store_out(p.y, p.y_dtype, tt * p.ldy + row, yacc[tok], p.accumulate);
-    }
-  }
-  consumer_done(p.sync, ticket);
-}
-
 template <typename A, int TB, int KW, int MODE>
 __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tbl, A* red) {
   constexpr int PW = pw_of(TB);
@@ -155,10 +102,23 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   const int64_t tblk = bid2 / p.nrt;
   const int64_t rt = bid2 - tblk * p.nrt;
   const int64_t row = rt * 64 + lane;
-  uint32_t wd[PW][KW];
+  constexpr int E = ents_per_thread<TB, KW>();
+  constexpr int64_t step = kWaves * PW;
+  // alpha of this lane's row for every term, two to a register (inputs:
+  // read before the wait, which waits for them anyway, by every lane with
+  // the row clamped; none means 1)
+  const int64_t arow = row < p.N ? row : p.N - 1;
+  uint32_t aln[DBF_MAX_TERMS / 2];
+#pragma unroll
+  for (int q = 0; q < DBF_MAX_TERMS; q += 2) {
+    const uint32_t lo = q < p.t.n && p.t.alpha[q] ? p.t.alpha[q][arow] : 0x3C00u;
+    const uint32_t hi = q + 1 < p.t.n && p.t.alpha[q + 1] ? p.t.alpha[q + 1][arow] : 0x3C00u;
+    aln[q / 2] = lo | (hi << 16);
+  }
+  uint32_t wd[PW][KW], wdn[PW][KW];
   load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
-  const unsigned ticket = wait_producers(p.sync, false);  // partials via load_shared4
-  bool have_bits = true;
+  wait_producers(p.sync, false);  // partials via load_shared4
+  unsigned ticket = 0;
   {
     const int64_t tok0 = tblk * TB;
     float yacc[TB];
@@ -168,27 +128,44 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
       A acc[TB];
 #pragma unroll
       for (int i = 0; i < TB; ++i) acc[i] = A(0);
-      for (int64_t kp = 0; kp < p.nkb; kp += kWaves * PW) {
-        if (!have_bits) load_pass_bits<TB, KW>(p.t.b1[term], rt, p.nkb, kp, p.nkb, wd);
-        have_bits = false;
-        const int64_t kb_end = min(p.nkb, kp + kWaves * PW);
+      for (int64_t kp = 0; kp < p.nkb; kp += step) {
+        const int64_t kb_end = min(p.nkb, kp + step);
         const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
         const int64_t kbase = kp * 32 * KW;
         // group g of the pass: w[tok][k .. k + 4) of this term
         auto act4 = [&](int tok, int g, A* v) { w4<A, MODE>(p, term, tok0 + tok, kbase + 4 * g, rt, v); };
-        tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc);
+        A v[E][4];
+        load_acts<A, TB, KW>(act4, ng, v);
+        // issued after the partials, so their round trips overlap the tables
+        // and lookups: the ticket and the next pass's signs (this term's next
+        // K-blocks or the next term's first)
+        if (kp == 0 && term == 0) ticket = take_ticket(p.sync);
+        const bool more = kp + step < p.nkb, next_term = !more && term + 1 < p.t.n;
+        if (more || next_term)  // one call: the two cases load the same registers
+          load_pass_bits<TB, KW>(p.t.b1[more ? term : term + 1], rt, p.nkb, more ? kp + step : 0,
+                                 p.nkb, wdn);
+        tables_and_lookups_v<A, TB, KW>(v, tbl, ng, kp, kb_end, wd, acc);
+        if (more || next_term) {
+#pragma unroll
+          for (int j = 0; j < PW; ++j)
+#pragma unroll
+            for (int w = 0; w < KW; ++w) wd[j][w] = wdn[j][w];
+        }
       }
       reduce_waves<A, TB>(red, acc);
       if (wv == 0 && row < p.N) {
-        const uint16_t* al = p.t.alpha[term];
-        const float a_n = al ? f16_bits_to_f32(al[row]) : 1.0f;
+        uint32_t a2 = aln[0];
+#pragma unroll
+        for (int q = 1; q < DBF_MAX_TERMS / 2; ++q)
+          if (q == term / 2) a2 = aln[q];
+        const uint16_t a_n = static_cast<uint16_t>(term & 1 ? a2 >> 16 : a2);
 #pragma unroll
         for (int tok = 0; tok < TB; ++tok) {
           if constexpr (MODE == MODE_I8) {
             const int64_t tt = tok0 + tok;
             if (tt < p.T && p.s2_out) p.s2_out[(term * p.T + tt) * p.N + row] = acc[tok];
           }
-          yacc[tok] += a_n * static_cast<float>(acc[tok]);
+          yacc[tok] += f16_bits_to_f32(a_n) * static_cast<float>(acc[tok]);
         }
       }
     }
@@ -203,8 +180,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   consumer_done(p.sync, ticket);
 }
 
-// NI > 1: shared carriers, up to NI terms on the same signs per workgroup.
-template <typename A, int TB, int KW1, int KW2, int MODE, int NI = 1>
+template <typename A, int TB, int KW1, int KW2, int MODE>
 __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, int n1,
                                                           int run_stage2) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -213,14 +189,11 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, 
   A* red = tbl + tbl_elems<TB, KWM>();
   const int bid = blockIdx.x;
   if (bid < n1) {
-    stage1_role<A, TB, KW1, MODE, NI>(s1, bid, tbl, red);
+    stage1_role<A, TB, KW1, MODE>(s1, bid, tbl, red);
     if (run_stage2) publish(s2.sync, static_cast<unsigned>(bid));
     return;
   }
-  if constexpr (NI > 1)
-    stage2_shared_role<A, TB, KW2, NI>(s2, bid - n1, tbl, red);
-  else
-    stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
+  stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
 }
 
 constexpr int64_t kStage1Wg = 512;
@@ -249,7 +222,9 @@ __device__ __forceinline__ void sum_role(const SumArgs& p, int64_t bid2) {
   const int64_t tblk = bid2 / p.nrt;
   const int64_t rt = bid2 - tblk * p.nrt;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const unsigned ticket = wait_producers(p.sync, false);  // partials via system-scope loads
+  wait_producers(p.sync, false);  // partials via system-scope loads
+  unsigned ticket = 0;
+  bool took = false;
   const int64_t row = rt * 64 + lane, tt = tblk * TB + wv;
   if (wv < TB && row < p.N && tt < p.T) {
     const int np = p.L * p.ks;
@@ -262,12 +237,18 @@ __device__ __forceinline__ void sum_role(const SumArgs& p, int64_t bid2) {
         q[j] = j0 + j < np ? __hip_atomic_load(base + (j0 + j) * p.T * p.rs, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_SYSTEM)
                            : 0u;
+      // after the first partials' loads, so its round trip overlaps them
+      if (!took) {
+        ticket = take_ticket(p.sync);
+        took = true;
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (j0 + j < np) s += __uint_as_float(q[j]);
     }
     store_out(p.y, p.y_dtype, tt * p.ldy + row, s, p.accumulate);
   }
+  if (!took) ticket = take_ticket(p.sync);
   consumer_done(p.sync, ticket);
 }
 
@@ -285,12 +266,12 @@ __global__ void __launch_bounds__(kThreads) bool_decode_kernel(Stage1 s1, SumArg
   sum_role<TB>(s2, bid - n1);
 }
 
-template <typename A, int MODE, int NI = 1>
+template <typename A, int MODE>
 hipError_t run(const Stage1& s1, const Stage2& s2, int n1, int n2, int run_stage2,
                int tb, int kw1, int kw2, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(n1 + (run_stage2 ? n2 : 0));
 #define DBF_LAUNCH(TB_, K1_, K2_)                                                        \
-  decode_kernel<A, TB_, K1_, K2_, MODE, NI>                                              \
+  decode_kernel<A, TB_, K1_, K2_, MODE>                                                  \
       <<<dim3(grid), kThreads, lds_bytes<A, TB_, (K1_ > K2_ ? K1_ : K2_)>(), s>>>(        \
           s1, s2, n1, run_stage2)
 #define DBF_K2(TB_, K1_)                     \
@@ -332,16 +313,14 @@ Stage2 make_stage2(const TermPtrs& t, const Stage1& s1, int64_t N, int64_t R, in
 }  // namespace
 
 lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, int x_dtype,
-                        int64_t T, int64_t ldx, void* ws, bool split, int* n1,
-                        bool allow_shared) {
+                        int64_t T, int64_t ldx, void* ws, bool split, int* n1) {
   lut::Stage1 a{};
   a.t = t; a.x = x; a.x_dtype = x_dtype; a.ldx = ldx; a.T = T; a.M = M; a.R = R;
   a.nkb = layout_nkb(M);
   a.nrt = layout_nrt(R);
   int64_t per = 0;
   a.ntb = static_cast<int>((T + lut::pick_tb(T) - 1) / lut::pick_tb(T));
-  a.inner = allow_shared && shared_carriers(t, T) ? t.n : 1;
-  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n / a.inner, a.nkb, split ? kStage1Wg : 1, &per);
+  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Wg : 1, &per);
   a.kb_per_split = per;
   a.rs = ws_rstride(R);
   // four 16-bit activations per 8-byte load (fp32 input takes the bounded path)
@@ -349,7 +328,7 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
            (M % 4 == 0);
   for (int i = 0; i < t.n; ++i)
     if (t.gamma[i] && reinterpret_cast<uintptr_t>(t.gamma[i]) % 8 != 0) a.vec4 = 0;
-  *n1 = static_cast<int>(a.nrt * a.ks * (t.n / a.inner) * a.ntb);
+  *n1 = static_cast<int>(a.nrt * a.ks * t.n * a.ntb);
   a.ws = static_cast<unsigned char*>(ws) + kWsHeadBytes;
   return a;
 }
@@ -357,11 +336,9 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
 size_t decode_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t T) {
   int64_t per = 0;
   const int64_t ntb = (T + lut::pick_tb(T) - 1) / lut::pick_tb(T);
-  // the most splits any call of these sizes picks: with separate carriers,
-  // or with shared ones (one workgroup per row tile for all terms)
-  const int ks = std::max({lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
-                           lut::pick_ks(layout_nrt(R) * ntb, 1, layout_nkb(M), kStage1Wg, &per),
-                           lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per)});
+  // the most splits any call of these sizes picks (split or not)
+  const int ks = std::max(lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
+                          lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per));
   return kWsHeadBytes + static_cast<size_t>(n_terms) * ks * static_cast<size_t>(T) *
                                    static_cast<size_t>(ws_rstride(R)) * 4u;
 }
@@ -371,13 +348,10 @@ hipError_t launch_decode(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                          void* y, int y_dtype, int64_t ldy, int accumulate,
                          void* ws, hipStream_t s) {
   int n1 = 0;
-  const Stage1 a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1, true);
+  const Stage1 a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1);
   Stage2 b = make_stage2(t, a, N, R, T, ws, n1);
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
   const int kw1 = static_cast<int>(layout_kw(M)), kw2 = static_cast<int>(layout_kw(R));
-  if (a.inner > 1)
-    return run<float, MODE_F, kSharedTerms>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1,
-                                            kw2, s);
   return run<float, MODE_F>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1, kw2, s);
 }
 

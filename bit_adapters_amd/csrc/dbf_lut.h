@@ -109,25 +109,51 @@ __device__ __forceinline__ void load_pass_bits(const uint32_t* __restrict__ bits
   }
 }
 
-// Tables for the groups of the pass (ng groups of four activations per
-// token, act4(tok, g, a) writes group g's four values) built straight into
-// LDS, then this lane's lookups of the pass: acc[tok] += sum over the pass
-// of S[row, k] * act[tok][k].  Two accumulators per token keep the adds of
-// consecutive nibbles independent, so many LDS reads are in flight.  Ends
-// with a barrier, so the tables may be overwritten afterwards.
+// Table entries of a pass, [TB][ng] (ng groups of four activations per
+// token), and how many of them one thread builds.
+template <int TB, int KW>
+__host__ __device__ constexpr int ents_per_thread() {
+  return (TB * kWaves * pw_of(TB) * 8 * KW + kThreads - 1) / kThreads;
+}
+
+// The four activations of each table entry this thread builds (entry
+// threadIdx.x + i * kThreads; act4(tok, g, a) writes group g's four values).
+// Vector loads return in order within a wave, so a caller issues these loads
+// before loads whose data it needs later (the pass's sign words), and the
+// table build need not wait for those.
 template <typename A, int TB, int KW, typename Act4>
-__device__ __forceinline__ void tables_and_lookups(Act4 act4, A* tbl, int ng, int64_t kp,
-                                                   int64_t kb_end,
-                                                   const uint32_t (&wd)[pw_of(TB)][KW],
-                                                   A* acc) {
+__device__ __forceinline__ void load_acts(Act4 act4, int ng,
+                                          A (&v)[ents_per_thread<TB, KW>()][4]) {
+#pragma unroll
+  for (int i = 0; i < ents_per_thread<TB, KW>(); ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    if (e < TB * ng) {
+      const int tok = e / ng, g = e - tok * ng;
+      act4(tok, g, v[i]);
+    }
+  }
+}
+
+// Tables for the groups of the pass built from the loaded activations
+// straight into LDS, then this lane's lookups of the pass: acc[tok] += sum
+// over the pass of S[row, k] * act[tok][k].  Two accumulators per token keep
+// the adds of consecutive nibbles independent, so many LDS reads are in
+// flight.  Ends with a barrier, so the tables may be overwritten afterwards.
+template <typename A, int TB, int KW>
+__device__ __forceinline__ void tables_and_lookups_v(const A (&v)[ents_per_thread<TB, KW>()][4],
+                                                     A* tbl, int ng, int64_t kp, int64_t kb_end,
+                                                     const uint32_t (&wd)[pw_of(TB)][KW],
+                                                     A* acc) {
   constexpr int PW = pw_of(TB);
   constexpr int gpp = kWaves * PW * 8 * KW;
   const int wv = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < TB * ng; e += kThreads) {
-    const int tok = e / ng, g = e - tok * ng;
-    A a[4];
-    act4(tok, g, a);
-    build_signed16<A>(a[0], a[1], a[2], a[3], tbl + (tok * gpp + g) * 16);
+#pragma unroll
+  for (int i = 0; i < ents_per_thread<TB, KW>(); ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    if (e < TB * ng) {
+      const int tok = e / ng, g = e - tok * ng;
+      build_signed16<A>(v[i][0], v[i][1], v[i][2], v[i][3], tbl + (tok * gpp + g) * 16);
+    }
   }
   __syncthreads();
   A acc2[TB];
@@ -154,6 +180,16 @@ __device__ __forceinline__ void tables_and_lookups(Act4 act4, A* tbl, int ng, in
 #pragma unroll
   for (int tok = 0; tok < TB; ++tok) acc[tok] += acc2[tok];
   __syncthreads();
+}
+
+template <typename A, int TB, int KW, typename Act4>
+__device__ __forceinline__ void tables_and_lookups(Act4 act4, A* tbl, int ng, int64_t kp,
+                                                   int64_t kb_end,
+                                                   const uint32_t (&wd)[pw_of(TB)][KW],
+                                                   A* acc) {
+  A v[ents_per_thread<TB, KW>()][4];
+  load_acts<A, TB, KW>(act4, ng, v);
+  tables_and_lookups_v<A, TB, KW>(v, tbl, ng, kp, kb_end, wd, acc);
 }
 
 // Sum of the 4 wave partials of each lane's row, in wave order; the result
@@ -185,18 +221,11 @@ struct Stage1 {
   int64_t nkb, kb_per_split, nrt;
   int ks;
   int ntb;        // token blocks (of TB tokens), one per workgroup
-  int inner;      // terms one workgroup runs over the same signs (shared
-                  // carriers: all L; otherwise 1)
   void* ws;       // partials [L][ks][T][rs]
   int64_t rs;
   int vec4;       // x rows allow 8-byte loads of four activations
 };
 
-// Stage-1 workgroup `bid` in [0, ntb * (L / inner) * nrt * ks): its token
-// block, row tile of B2, K-blocks [kb0, kb1) of its split (one or more
-// passes) and terms [term0, term0 + inner).  With shared carriers
-// (inner = L <= NI) every pass's sign words are loaded once and serve the
-// tables of all the terms.
 // Where stage 1 takes a term's B2, gamma and beta from: the term table of
 // the launch, or (OneTerm) a single term's pointers, e.g. the adapter of a
 // workgroup's token.
@@ -217,107 +246,103 @@ struct OneTerm {
   __device__ int n() const { return 1; }
 };
 
-template <typename A, int TB, int KW, int MODE, int NI = 1, class Src = TermSrc>
-__device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src, int bid, A* tbl,
-                                                A* red);
-
-template <typename A, int TB, int KW, int MODE, int NI = 1>
-__device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
-  stage1_role_src<A, TB, KW, MODE, NI>(p, TermSrc{p.t}, bid, tbl, red);
-}
-
-template <typename A, int TB, int KW, int MODE, int NI, class Src>
+// Stage-1 workgroup `bid` in [0, ntb * L * nrt * ks): its token block, term,
+// row tile of B2 and K-blocks [kb0, kb1) of its split (one or more passes).
+template <typename A, int TB, int KW, int MODE, class Src = TermSrc>
 __device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src, int bid, A* tbl,
                                                 A* red) {
   constexpr int PW = pw_of(TB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int inner = NI > 1 ? p.inner : 1;
-  const int per_tb = (src.n() / inner) * static_cast<int>(p.nrt) * p.ks;
+  const int per_term = static_cast<int>(p.nrt) * p.ks;
+  const int per_tb = src.n() * per_term;
   const int tblk = bid / per_tb;
   bid -= tblk * per_tb;
-  const int per_term = static_cast<int>(p.nrt) * p.ks;
-  const int term0 = (bid / per_term) * inner;
-  const int rem = bid - (term0 / inner) * per_term;
+  const int term = bid / per_term;
+  const int rem = bid - term * per_term;
   const int64_t rt = rem / p.ks;
   const int split = rem - static_cast<int>(rt) * p.ks;
   const int64_t kb0 = static_cast<int64_t>(split) * p.kb_per_split;
   const int64_t kb1 = min(p.nkb, kb0 + p.kb_per_split);
-  const uint32_t* bits = src.b2(term0);
+  const uint32_t* bits = src.b2(term);
+  const uint16_t* gam = src.gamma(term);
   const int64_t row = rt * 64 + lane;
+  const int64_t tok0 = static_cast<int64_t>(tblk) * TB;
 
+  // beta of the rows this workgroup stores, read first: an input, and a
+  // wave's loads return in order.  Every lane loads (row clamped), so no
+  // branch holds the load, and the value is converted only where it is used.
+  uint16_t bet = 0;
+  if constexpr (MODE == MODE_F) bet = src.beta(term)[row < p.R ? row : p.R - 1];
   uint32_t wd[PW][KW];
-  load_pass_bits<TB, KW>(bits, rt, p.nkb, kb0, kb1, wd);
-  bool have_bits = true;
-  {
-    const int64_t tok0 = static_cast<int64_t>(tblk) * TB;
-    A acc[NI][TB];
+  A acc[TB];
 #pragma unroll
-    for (int q = 0; q < NI; ++q)
+  for (int i = 0; i < TB; ++i) acc[i] = A(0);
+  for (int64_t kp = kb0; kp < kb1; kp += kWaves * PW) {
+    const int64_t kb_end = min(kb1, kp + kWaves * PW);
+    const int64_t k0 = kp * 32 * KW;
+    const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
+    auto act4 = [&](int tok, int g, A* a) {
+      const int64_t tt = tok0 + tok, k = k0 + 4 * g;
+      if constexpr (MODE == MODE_F) {
+        if (p.vec4) {
+          // M % 4 == 0: a group is wholly in or out.  Both loads are issued
+          // by every lane (indices clamped), out-of-range groups give zeros.
+          const bool in = tt < p.T && k < p.M;
+          const int64_t tc = in ? tt : 0, kc = in ? k : 0;
+          const uint2 xv = *reinterpret_cast<const uint2*>(
+              static_cast<const uint16_t*>(p.x) + tc * p.ldx + kc);
+          const uint2 gv = *reinterpret_cast<const uint2*>(gam + kc);
+          const uint16_t xs[4] = {uint16_t(xv.x), uint16_t(xv.x >> 16), uint16_t(xv.y),
+                                  uint16_t(xv.y >> 16)};
+          const uint16_t gs[4] = {uint16_t(gv.x), uint16_t(gv.x >> 16), uint16_t(gv.y),
+                                  uint16_t(gv.y >> 16)};
 #pragma unroll
-      for (int i = 0; i < TB; ++i) acc[q][i] = A(0);
-    for (int64_t kp = kb0; kp < kb1; kp += kWaves * PW) {
-      if (!have_bits) load_pass_bits<TB, KW>(bits, rt, p.nkb, kp, kb1, wd);
-      have_bits = false;
-      const int64_t kb_end = min(kb1, kp + kWaves * PW);
-      const int64_t k0 = kp * 32 * KW;
-      const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
-#pragma unroll
-      for (int q = 0; q < NI; ++q) {
-      if (q >= inner) break;
-      const uint16_t* gam = src.gamma(term0 + q);
-      auto act4 = [&](int tok, int g, A* a) {
-        const int64_t tt = tok0 + tok, k = k0 + 4 * g;
-        if constexpr (MODE == MODE_F) {
-          if (tt < p.T && k + 4 <= p.M && p.vec4) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(
-                static_cast<const uint16_t*>(p.x) + tt * p.ldx + k);
-            const uint2 gv = *reinterpret_cast<const uint2*>(gam + k);
-            const uint16_t xs[4] = {uint16_t(xv.x), uint16_t(xv.x >> 16), uint16_t(xv.y),
-                                    uint16_t(xv.y >> 16)};
-            const uint16_t gs[4] = {uint16_t(gv.x), uint16_t(gv.x >> 16), uint16_t(gv.y),
-                                    uint16_t(gv.y >> 16)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              a[j] = f16_bits_to_f32(gs[j]) * (p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xs[j])
-                                                                      : f16_bits_to_f32(xs[j]));
-            return;
+          for (int j = 0; j < 4; ++j) {
+            const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xs[j]) : f16_bits_to_f32(xs[j]);
+            a[j] = in ? f16_bits_to_f32(gs[j]) * xf : 0.f;
           }
+          return;
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          A v = A(0);
-          if (tt < p.T && k + j < p.M) {
-            if constexpr (MODE == MODE_F)
-              v = f16_bits_to_f32(gam[k + j]) * load_act(p.x, p.x_dtype, tt * p.ldx + k + j);
-            else
-              v = static_cast<const int8_t*>(p.x)[tt * p.ldx + k + j];
-          }
-          a[j] = v;
-        }
-      };
-      tables_and_lookups<A, TB, KW>(act4, tbl, ng, kp, kb_end, wd, acc[q]);
       }
-    }
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      if (q >= inner) break;
-      const int term = term0 + q;
-      reduce_waves<A, TB>(red, acc[q]);
-      if (wv == 0 && row < p.R) {
-#pragma unroll
-        for (int tok = 0; tok < TB; ++tok) {
-          const int64_t tt = tok0 + tok;
-          if (tt < p.T) {
-            const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
-            if constexpr (MODE == MODE_F)
-              store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(src.beta(term)[row]) * acc[q][tok]);
-            else
-              store_shared(static_cast<int32_t*>(p.ws) + o, static_cast<int32_t>(acc[q][tok]));
-          }
+      for (int j = 0; j < 4; ++j) {
+        A v = A(0);
+        if (tt < p.T && k + j < p.M) {
+          if constexpr (MODE == MODE_F)
+            v = f16_bits_to_f32(gam[k + j]) * load_act(p.x, p.x_dtype, tt * p.ldx + k + j);
+          else
+            v = static_cast<const int8_t*>(p.x)[tt * p.ldx + k + j];
         }
+        a[j] = v;
+      }
+    };
+    // the pass's sign words, then its activations, all in flight together
+    // (the activations are converted as they arrive, so loads issued after
+    // them would wait for them)
+    load_pass_bits<TB, KW>(bits, rt, p.nkb, kp, kb1, wd);
+    A v[ents_per_thread<TB, KW>()][4];
+    load_acts<A, TB, KW>(act4, ng, v);
+    tables_and_lookups_v<A, TB, KW>(v, tbl, ng, kp, kb_end, wd, acc);
+  }
+  reduce_waves<A, TB>(red, acc);
+  if (wv == 0 && row < p.R) {
+#pragma unroll
+    for (int tok = 0; tok < TB; ++tok) {
+      const int64_t tt = tok0 + tok;
+      if (tt < p.T) {
+        const int64_t o = ((static_cast<int64_t>(term) * p.ks + split) * p.T + tt) * p.rs + row;
+        if constexpr (MODE == MODE_F)
+          store_shared(static_cast<float*>(p.ws) + o, f16_bits_to_f32(bet) * acc[tok]);
+        else
+          store_shared(static_cast<int32_t*>(p.ws) + o, static_cast<int32_t>(acc[tok]));
       }
     }
   }
+}
+
+template <typename A, int TB, int KW, int MODE>
+__device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
+  stage1_role_src<A, TB, KW, MODE>(p, TermSrc{p.t}, bid, tbl, red);
 }
 
 // ---- handoff between the two roles of a launch ---------------------------
@@ -328,9 +353,9 @@ __device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src,
 // Consumers poll the counters with loads that bypass the caches (lane l of
 // wave 0 reads counter l).  A consumer that reads the results only with
 // load_shared4 needs nothing more; one that reads them with ordinary loads
-// invalidates its caches first (agent-scope acquire).  ctr[0] counts
-// consumers past their wait; ctr[2] is set if a wait gave up (read by
-// dbf_workspace_check).
+// invalidates its caches first (agent-scope acquire).  ctr[0] counts the
+// tickets consumers took after their wait; ctr[2] is set if a wait gave up
+// (read by dbf_workspace_check).
 struct Sync {
   unsigned* ctr;
   unsigned* slots;
@@ -360,11 +385,9 @@ __device__ __forceinline__ void publish(const Sync& s, unsigned pid) {
 // count, then acquires (an agent-scope invalidation of L1 and L2, about a
 // microsecond; a consumer that reads the results only with load_shared4
 // passes acquire = false); the workgroup barrier orders the other waves
-// after it.  Thread 0 then takes a ticket (the consumers' arrival order);
-// its value is only needed by consumer_done at the end.
-__device__ __forceinline__ unsigned wait_producers(const Sync& s, bool acquire = true) {
+// after it.
+__device__ __forceinline__ void wait_producers(const Sync& s, bool acquire = true) {
   static_assert(kSyncSlots <= 64, "one counter per lane");
-  unsigned ticket = 0;
   if (threadIdx.x < 64) {
     const unsigned lane = threadIdx.x;
     const unsigned ns = static_cast<unsigned>(kSyncSlots);
@@ -386,16 +409,26 @@ __device__ __forceinline__ unsigned wait_producers(const Sync& s, bool acquire =
     if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  // after the barrier, which would otherwise wait for the ticket's return;
-  // the loads that follow overlap with it
+  // loads issued before the wait (prefetched inputs) are complete by now;
+  // waiting for them here costs nothing and lets the compiler's later waits
+  // count only loads issued after this point
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Consumer, once past wait_producers: thread 0 takes a ticket (the order in
+// which consumers got here), which only consumer_done reads.  A wave's loads
+// return in order, so a consumer takes it after issuing its first loads of
+// the producers' results; its round trip then overlaps the work on them.
+__device__ __forceinline__ unsigned take_ticket(const Sync& s) {
+  unsigned ticket = 0;
   if (threadIdx.x == 0)
     ticket = __hip_atomic_fetch_add(s.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   return ticket;
 }
 
-// Consumer, at its end, with the ticket of its wait: the last consumer to
-// pass its wait (every producer has published and every consumer has
-// waited by then) clears the counters for the next call.
+// Consumer, at its end, with its ticket: the last consumer to take one
+// (every producer has published and every consumer has passed its wait by
+// then) clears the counters for the next call.
 __device__ __forceinline__ void consumer_done(const Sync& s, unsigned ticket) {
   if (threadIdx.x < 64) {
     // thread 0 holds the ticket; the lanes of wave 0 clear one counter each
@@ -453,11 +486,8 @@ inline int pick_ks(int64_t nrt, int n_terms, int64_t nkb, int64_t want_wg,
 // stage 1 has enough workgroups when `split`, else as few splits as the
 // partial buffer allows); *n1 = its number of workgroups.  ws is the
 // caller's workspace (counters first).
-// allow_shared: the caller's kernel folds the terms of shared carriers
-// into one workgroup (stage1_role with NI > 1); other kernels must pass
-// false.
 lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x,
                         int x_dtype, int64_t T, int64_t ldx, void* ws, bool split,
-                        int* n1, bool allow_shared = false);
+                        int* n1);
 
 }  // namespace dbf

@@ -169,9 +169,9 @@ int dbf_workspace_check(void *ws, void *stream);
  *   accumulate       0: y = result; 1: y = y + result (in fp32).
  *   ws, ws_bytes     workspace of dbf_workspace_bytes(..., path) bytes.
  *   path             DBF_PATH_AUTO picks the decode path while T <= 4 or
- *                    n_terms * ceil(T / 4) <= 5, and the MFMA path above;
- *                    the others force one (both are correct for every
- *                    T >= 1).
+ *                    n_terms * ceil(T / 4) * R * (N + M) <= 1.5e8, and the
+ *                    MFMA path above; the others force one (both are
+ *                    correct for every T >= 1).
  * Accumulation is fp32; the decode path keeps every intermediate in fp32,
  * the MFMA path rounds gamma*x and the scaled rank-R intermediate to fp16
  * (with an exact power-of-two scale per token).

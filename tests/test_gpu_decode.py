@@ -163,8 +163,8 @@ def _shared_terms(layer, share_b2=True):
                                        (1000, 4096, 512, 4, 3), (1000, 4096, 512, 4, 16), (130, 300, 70, 5, 2),
                                        (512, 2048, 256, 2, 20)])
 def test_shared_carriers(N, M, R, L, T):
-    # up to 4 terms and 4 tokens one workgroup runs all terms over one load
-    # of the signs; five terms, or more tokens, take the per-term path
+    # terms that alias one B1 and one B2 run as separate terms; the sums
+    # are exact to the tolerance and bitwise reproducible
     print("shared carriers", N, M, R, L, T, flush=True)
     layer, x = _shared_layer(N, M, R, L, T, seed=L + N)
     terms = _shared_terms(layer)
@@ -178,7 +178,7 @@ def test_shared_carriers(N, M, R, L, T):
 
 
 def test_partly_shared_carriers():
-    # B1 shared, B2 not: the per-term path
+    # B1 shared, B2 not
     layer, x = _shared_layer(200, 700, 64, 3, 4, seed=77, share_b2=False)
     terms = _shared_terms(layer, share_b2=False)
     y = D.dbf_linear_forward(terms, 200, 700, 64, x_dev(x), path=PATH)

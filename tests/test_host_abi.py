@@ -57,18 +57,27 @@ def test_workspace_bytes():
     assert D.dbf_workspace_bytes(512, 512, 256, 1, 1, D.DBF_PATH_MFMA) > 0
 
 
-@pytest.mark.parametrize("T,L,path", [(1, 1, "decode"), (20, 1, "decode"), (21, 1, "mfma"),
-                                      (4, 3, "decode"), (5, 3, "mfma"), (8, 2, "decode"),
-                                      (9, 2, "mfma"), (1, 8, "decode"), (4, 8, "decode"),
-                                      (5, 8, "mfma"), (4096, 1, "mfma")])
-def test_auto_path_rule(T, L, path):
-    # automatic choice: the decode kernel while T <= 4 or
-    # n_terms * ceil(T / 4) <= 5
+# (N, M, R, terms, tokens, path): decode while T <= 4 or the sign work
+# terms * ceil(T / 4) * R * (N + M) is at most 1.5e8
+AUTO_CASES = [(4096, 4096, 2048, 1, 1, "decode"), (4096, 4096, 2048, 1, 32, "decode"),
+              (4096, 4096, 2048, 1, 33, "mfma"), (4096, 4096, 2048, 2, 16, "decode"),
+              (4096, 4096, 2048, 2, 17, "mfma"), (11008, 4096, 2048, 3, 4, "decode"),
+              (11008, 4096, 2048, 3, 5, "mfma"), (8192, 8192, 6144, 1, 4, "decode"),
+              (8192, 8192, 6144, 1, 5, "mfma"), (512, 512, 256, 1, 64, "decode"),
+              (512, 512, 256, 8, 64, "decode"), (16384, 16384, 8192, 8, 1, "decode"),
+              (4096, 4096, 2048, 1, 4096, "mfma")]
+
+
+@pytest.mark.parametrize("N,M,R,L,T,path", AUTO_CASES)
+def test_auto_path_rule(N, M, R, L, T, path):
     want = D.DBF_PATH_DECODE if path == "decode" else D.DBF_PATH_MFMA
-    auto = D.dbf_workspace_bytes(4096, 4096, 2048, L, T, D.DBF_PATH_AUTO)
-    assert auto == D.dbf_workspace_bytes(4096, 4096, 2048, L, T, want)
+    # the rule itself, written out
+    work = L * -(-T // 4) * R * (N + M)
+    assert (T <= 4 or work <= 1.5e8) == (path == "decode")
+    auto = D.dbf_workspace_bytes(N, M, R, L, T, D.DBF_PATH_AUTO)
+    assert auto == D.dbf_workspace_bytes(N, M, R, L, T, want)
     other = D.DBF_PATH_MFMA if want == D.DBF_PATH_DECODE else D.DBF_PATH_DECODE
-    assert auto != D.dbf_workspace_bytes(4096, 4096, 2048, L, T, other)
+    assert auto != D.dbf_workspace_bytes(N, M, R, L, T, other)
 
 
 L = D.library()
