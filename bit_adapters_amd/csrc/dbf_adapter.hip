@@ -437,17 +437,26 @@ __global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
     floatx4 wacc[Group<L, QR>::NQ];
 #pragma unroll
     for (int q = 0; q < Group<L, QR>::NQ; ++q) wacc[q] = acc;
-    {
+    // The stream runs one group ahead.  Each path either loads the next
+    // group and then computes the current one, or computes the last one:
+    // the loads in flight at every MFMA are then known to the compiler, which
+    // otherwise waits for all of them (a load under a condition makes the
+    // count unknown).  Two groups ahead (three buffers) measured no faster
+    // and runs out of registers above one rank tile.
+    if (ngroups > 0) {
       Group<L, QR> G0, G1;
-      if (ngroups > 0) load_group(G0, p, kbeg, wrow, xrow, lane, li, lq);
-      for (int64_t g = 0; g < ngroups; g += 2) {
-        if (g + 1 < ngroups)
-          load_group(G1, p, kbeg + (g + 1) * kGroup, wrow, xrow, lane, li, lq);
-        compute_group(G0, acc, wacc, mygam, lut, lane, lq);
-        if (g + 1 >= ngroups) break;
-        if (g + 2 < ngroups)
-          load_group(G0, p, kbeg + (g + 2) * kGroup, wrow, xrow, lane, li, lq);
-        compute_group(G1, acc, wacc, mygam, lut, lane, lq);
+      auto ld = [&](Group<L, QR>& G, int64_t g) {
+        load_group(G, p, kbeg + g * kGroup, wrow, xrow, lane, li, lq);
+      };
+      auto cp = [&](const Group<L, QR>& G) { compute_group(G, acc, wacc, mygam, lut, lane, lq); };
+      ld(G0, 0);
+      for (int64_t g = 0;; g += 2) {  // G0 holds group g
+        if (g + 1 >= ngroups) { cp(G0); break; }
+        ld(G1, g + 1);
+        cp(G0);
+        if (g + 2 >= ngroups) { cp(G1); break; }
+        ld(G0, g + 2);
+        cp(G1);
       }
     }
     for (int64_t k0 = kbeg + ngroups * kGroup; k0 < kend; k0 += 32) {
