@@ -70,8 +70,11 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p, int64_t k) {
   return *reinterpret_cast<const uint4*>(p + k);
 }
 
-constexpr int kMainWaves = lut::kWaves;
-constexpr int kMainThreads = lut::kThreads;
+// Eight waves: the row roles need more than the 128 registers per wave that
+// a 1024-thread workgroup leaves.  The stage-1 roles of these kernels run
+// with the same eight.
+constexpr int kMainWaves = 8;
+constexpr int kMainThreads = 64 * kMainWaves;
 
 // MULTI: each token has its own adapter (tab, idx; one term each) instead of
 // the terms p.t shared by every token.
@@ -206,8 +209,8 @@ __global__ void __launch_bounds__(kMainThreads) adapter_fused(lut::Stage1 s1, Ma
   extern __shared__ __align__(16) unsigned char smem[];
   if (static_cast<int>(blockIdx.x) < n1) {
     float* tbl = reinterpret_cast<float*>(smem);
-    float* red = tbl + lut::tbl_elems<TB, KW>();
-    lut::stage1_role<float, TB, KW, lut::MODE_F>(s1, blockIdx.x, tbl, red);
+    float* red = tbl + lut::tbl_elems<TB, KW, kMainWaves>();
+    lut::stage1_role<float, TB, KW, lut::MODE_F, kMainWaves>(s1, blockIdx.x, tbl, red);
     lut::publish(m.sync, blockIdx.x);
     return;
   }
@@ -231,8 +234,8 @@ __global__ void __launch_bounds__(kMainThreads) adapter_multi(lut::Stage1 s1, Ma
         lut::token_adapter(idx, bid / (static_cast<int>(s1.nrt) * s1.ks), tab, m.sync, true));
     if (a >= 0) {
       float* tbl = reinterpret_cast<float*>(smem);
-      float* red = tbl + lut::tbl_elems<1, KW>();
-      lut::stage1_role_src<float, 1, KW, lut::MODE_F>(
+      float* red = tbl + lut::tbl_elems<1, KW, kMainWaves>();
+      lut::stage1_role_src<float, 1, KW, lut::MODE_F, kMainWaves>(
           s1, lut::OneTerm{tab.b2[a], tab.gamma[a], tab.beta[a]}, bid, tbl, red);
     }
     lut::publish(m.sync, static_cast<unsigned>(bid));
@@ -556,12 +559,12 @@ hipError_t launch_multi_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs*
   m.nmain = static_cast<unsigned>((N + 15) / 16);
   // stage 1 in one-token blocks (each token its own adapter)
   int n1 = 0;
-  lut::Stage1 a = make_stage1(adapters[0], M, R, x, DBF_BF16, T, ldx, ws, true, &n1);
+  lut::Stage1 a = make_stage1(adapters[0], M, R, x, DBF_BF16, T, ldx, ws, true, &n1, kMainWaves);
   int64_t per = 0;
   a.ntb = static_cast<int>(T);
   for (int q = 0; q < n_adapters; ++q)  // 8-byte gamma loads for every adapter
     if (reinterpret_cast<uintptr_t>(adapters[q].gamma[0]) % 8 != 0) a.vec4 = 0;
-  a.ks = lut::pick_ks(a.nrt * T, 1, a.nkb, 512, &per);
+  a.ks = lut::pick_ks(a.nrt * T, 1, a.nkb, 512, &per, kMainWaves);
   a.kb_per_split = per;
   n1 = static_cast<int>(a.nrt * a.ks * T);
   m.ws = static_cast<const float*>(a.ws);
@@ -573,7 +576,7 @@ hipError_t launch_multi_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs*
   const int kw = static_cast<int>(layout_kw(M));
   const dim3 grid(static_cast<unsigned>(n1) + m.nmain);
 #define DBF_MA(KW_) \
-  adapter_multi<KW_><<<grid, kMainThreads, std::max(main_lds, lut::lds_bytes<float, 1, KW_>()), s>>>(a, m, tab, idx, n1)
+  adapter_multi<KW_><<<grid, kMainThreads, std::max(main_lds, lut::lds_bytes<float, 1, KW_, kMainWaves>()), s>>>(a, m, tab, idx, n1)
   switch (kw) {
     case 1: DBF_MA(1); break;
     case 2: DBF_MA(2); break;
@@ -624,7 +627,7 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
   }
   const size_t main_lds = sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk);
   int n1 = 0;
-  const lut::Stage1 a = make_stage1(t, M, R, x, DBF_BF16, T, ldx, ws, true, &n1);
+  const lut::Stage1 a = make_stage1(t, M, R, x, DBF_BF16, T, ldx, ws, true, &n1, kMainWaves);
   m.ws = static_cast<const float*>(a.ws);
   m.ks = a.ks;
   m.rs = a.rs;
@@ -632,7 +635,7 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
   const int tb = lut::pick_tb(T), kw = static_cast<int>(layout_kw(M));
   const dim3 grid(static_cast<unsigned>(n1) + m.nmain);
 #define DBF_AD(TB_, KW_)                                                                 \
-  adapter_fused<TB_, KW_><<<grid, kMainThreads, std::max(main_lds, lut::lds_bytes<float, TB_, KW_>()), \
+  adapter_fused<TB_, KW_><<<grid, kMainThreads, std::max(main_lds, lut::lds_bytes<float, TB_, KW_, kMainWaves>()), \
                             s>>>(a, m, n1)
 #define DBF_AD_KW(TB_)              \
   switch (kw) {                     \

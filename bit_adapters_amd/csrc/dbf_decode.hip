@@ -95,15 +95,15 @@ __device__ __forceinline__ void w4(const Stage2& p, int term, int64_t tt, int64_
   }
 }
 
-template <typename A, int TB, int KW, int MODE>
+template <typename A, int TB, int KW, int MODE, int NW>
 __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tbl, A* red) {
   constexpr int PW = pw_of(TB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t tblk = bid2 / p.nrt;
   const int64_t rt = bid2 - tblk * p.nrt;
   const int64_t row = rt * 64 + lane;
-  constexpr int E = ents_per_thread<TB, KW>();
-  constexpr int64_t step = kWaves * PW;
+  constexpr int E = ents_per_thread<TB, KW, NW>();
+  constexpr int64_t step = NW * PW;
   // alpha of this lane's row for every term, two to a register (inputs:
   // read before the wait, which waits for them anyway, by every lane with
   // the row clamped; none means 1)
@@ -116,7 +116,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
     aln[q / 2] = lo | (hi << 16);
   }
   uint32_t wd[PW][KW], wdn[PW][KW];
-  load_pass_bits<TB, KW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
+  load_pass_bits<TB, KW, NW>(p.t.b1[0], rt, p.nkb, 0, p.nkb, wd);
   wait_producers(p.sync, false);  // partials via load_shared4
   unsigned ticket = 0;
   {
@@ -135,16 +135,16 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
         // group g of the pass: w[tok][k .. k + 4) of this term
         auto act4 = [&](int tok, int g, A* v) { w4<A, MODE>(p, term, tok0 + tok, kbase + 4 * g, rt, v); };
         A v[E][4];
-        load_acts<A, TB, KW>(act4, ng, v);
+        load_acts<A, TB, KW, NW>(act4, ng, v);
         // issued after the partials, so their round trips overlap the tables
         // and lookups: the ticket and the next pass's signs (this term's next
         // K-blocks or the next term's first)
         if (kp == 0 && term == 0) ticket = take_ticket(p.sync);
         const bool more = kp + step < p.nkb, next_term = !more && term + 1 < p.t.n;
         if (more || next_term)  // one call: the two cases load the same registers
-          load_pass_bits<TB, KW>(p.t.b1[more ? term : term + 1], rt, p.nkb, more ? kp + step : 0,
+          load_pass_bits<TB, KW, NW>(p.t.b1[more ? term : term + 1], rt, p.nkb, more ? kp + step : 0,
                                  p.nkb, wdn);
-        tables_and_lookups_v<A, TB, KW>(v, tbl, ng, kp, kb_end, wd, acc);
+        tables_and_lookups_v<A, TB, KW, NW>(v, tbl, ng, kp, kb_end, wd, acc);
         if (more || next_term) {
 #pragma unroll
           for (int j = 0; j < PW; ++j)
@@ -152,7 +152,7 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
             for (int w = 0; w < KW; ++w) wd[j][w] = wdn[j][w];
         }
       }
-      reduce_waves<A, TB>(red, acc);
+      reduce_waves<A, TB, NW>(red, acc);
       if (wv == 0 && row < p.N) {
         uint32_t a2 = aln[0];
 #pragma unroll
@@ -180,23 +180,45 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   consumer_done(p.sync, ticket);
 }
 
-template <typename A, int TB, int KW1, int KW2, int MODE>
-__global__ void __launch_bounds__(kThreads) decode_kernel(Stage1 s1, Stage2 s2, int n1,
-                                                          int run_stage2) {
+// NW waves per workgroup (16 or 8; the launcher picks, see pick_waves).
+template <typename A, int TB, int KW1, int KW2, int MODE, int NW>
+__global__ void __launch_bounds__(64 * NW) decode_kernel(Stage1 s1, Stage2 s2, int n1,
+                                                         int run_stage2) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int KWM = KW1 > KW2 ? KW1 : KW2;
   A* tbl = reinterpret_cast<A*>(smem);
-  A* red = tbl + tbl_elems<TB, KWM>();
+  A* red = tbl + tbl_elems<TB, KWM, NW>();
   const int bid = blockIdx.x;
   if (bid < n1) {
-    stage1_role<A, TB, KW1, MODE>(s1, bid, tbl, red);
+    stage1_role<A, TB, KW1, MODE, NW>(s1, bid, tbl, red);
     if (run_stage2) publish(s2.sync, static_cast<unsigned>(bid));
     return;
   }
-  stage2_role<A, TB, KW2, MODE>(s2, bid - n1, tbl, red);
+  stage2_role<A, TB, KW2, MODE, NW>(s2, bid - n1, tbl, red);
 }
 
-constexpr int64_t kStage1Wg = 512;
+// Stage 1 aims at about this many waves (512 workgroups of 8, 256 of 16).
+constexpr int64_t kStage1Waves = 4096;
+
+// Waves per decode workgroup for a launch whose 16-wave stage 1 is `a16`
+// with n1_16 workgroups.  Sixteen halve each lane's lookups per 64-row tile
+// and the partials, but a CU then holds one workgroup instead of three, so
+// they pay only while stage 1 still splits K and fits the 256 CUs at once,
+// or when R is large enough that stage 2 dominates (two_stage).  Measured,
+// 16 vs 8 waves (us): 4096^2 R 2048 at 4 / 16 tokens 11.6 / 18.7 vs 12.7 /
+// 21.0, at 32 tokens 31.4 vs 29.2; three terms of 11008 x 4096 at 1 / 4
+// tokens 14.5 / 31.1 vs 16.2 / 30.3; 8192^2 R 6144 at 4 / 8 tokens 27.0 /
+// 44.8 vs 29.6 / 52.7; boolean kernels 2 x 4096^2 at 1 / 8 tokens 8.7 / 18.1
+// vs 9.3 / 16.9, 3 x 11008 x 4096 at 1 token 16.4 vs 15.6.
+int pick_waves(const lut::Stage1& a16, int64_t n1_16, int64_t R, bool two_stage) {
+  // a launch with no stage 2 gains only the halved partials, and fewer than
+  // 128 workgroups would leave half the CUs idle (the backward's one-token
+  // products on 2048-row matrices: 39.1 vs 37.4 us per backward)
+  if (!two_stage && n1_16 < 128) return 8;
+  if (a16.ks >= 2 && n1_16 <= 256) return 16;
+  if (two_stage && R >= 4096) return 16;
+  return 8;
+}
 
 // ---- boolean kernels (Multi-Boolean form) -------------------------------
 // The stage-1 role alone computes s_out . (Wb (s_in . x)) for each kernel
@@ -252,27 +274,27 @@ __device__ __forceinline__ void sum_role(const SumArgs& p, int64_t bid2) {
   consumer_done(p.sync, ticket);
 }
 
-template <int TB, int KW>
-__global__ void __launch_bounds__(kThreads) bool_decode_kernel(Stage1 s1, SumArgs s2, int n1) {
+template <int TB, int KW, int NW>
+__global__ void __launch_bounds__(64 * NW) bool_decode_kernel(Stage1 s1, SumArgs s2, int n1) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* tbl = reinterpret_cast<float*>(smem);
-  float* red = tbl + tbl_elems<TB, KW>();
+  float* red = tbl + tbl_elems<TB, KW, NW>();
   const int bid = blockIdx.x;
   if (bid < n1) {
-    stage1_role<float, TB, KW, MODE_F>(s1, bid, tbl, red);
+    stage1_role<float, TB, KW, MODE_F, NW>(s1, bid, tbl, red);
     publish(s2.sync, static_cast<unsigned>(bid));
     return;
   }
   sum_role<TB>(s2, bid - n1);
 }
 
-template <typename A, int MODE>
+template <typename A, int MODE, int NW>
 hipError_t run(const Stage1& s1, const Stage2& s2, int n1, int n2, int run_stage2,
                int tb, int kw1, int kw2, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(n1 + (run_stage2 ? n2 : 0));
 #define DBF_LAUNCH(TB_, K1_, K2_)                                                        \
-  decode_kernel<A, TB_, K1_, K2_, MODE>                                                  \
-      <<<dim3(grid), kThreads, lds_bytes<A, TB_, (K1_ > K2_ ? K1_ : K2_)>(), s>>>(        \
+  decode_kernel<A, TB_, K1_, K2_, MODE, NW>                                              \
+      <<<dim3(grid), 64 * NW, lds_bytes<A, TB_, (K1_ > K2_ ? K1_ : K2_), NW>(), s>>>(     \
           s1, s2, n1, run_stage2)
 #define DBF_K2(TB_, K1_)                     \
   switch (kw2) {                             \
@@ -313,14 +335,14 @@ Stage2 make_stage2(const TermPtrs& t, const Stage1& s1, int64_t N, int64_t R, in
 }  // namespace
 
 lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, int x_dtype,
-                        int64_t T, int64_t ldx, void* ws, bool split, int* n1) {
+                        int64_t T, int64_t ldx, void* ws, bool split, int* n1, int nw) {
   lut::Stage1 a{};
   a.t = t; a.x = x; a.x_dtype = x_dtype; a.ldx = ldx; a.T = T; a.M = M; a.R = R;
   a.nkb = layout_nkb(M);
   a.nrt = layout_nrt(R);
   int64_t per = 0;
   a.ntb = static_cast<int>((T + lut::pick_tb(T) - 1) / lut::pick_tb(T));
-  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Wg : 1, &per);
+  a.ks = lut::pick_ks(a.nrt * a.ntb, t.n, a.nkb, split ? kStage1Waves / nw : 1, &per, nw);
   a.kb_per_split = per;
   a.rs = ws_rstride(R);
   // four 16-bit activations per 8-byte load (fp32 input takes the bounded path)
@@ -336,9 +358,13 @@ lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x, 
 size_t decode_ws_bytes(int64_t /*N*/, int64_t M, int64_t R, int n_terms, int64_t T) {
   int64_t per = 0;
   const int64_t ntb = (T + lut::pick_tb(T) - 1) / lut::pick_tb(T);
-  // the most splits any call of these sizes picks (split or not)
-  const int ks = std::max(lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Wg, &per),
-                          lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per));
+  // the most splits any call of these sizes picks: split or not, with the
+  // decode kernels' workgroups or the adapter kernels' 8-wave ones
+  int ks = 1;
+  for (const int nw : {lut::kWaves, 8})
+    ks = std::max({ks,
+                   lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), kStage1Waves / nw, &per, nw),
+                   lut::pick_ks(layout_nrt(R) * ntb, n_terms, layout_nkb(M), 1, &per, nw)});
   return kWsHeadBytes + static_cast<size_t>(n_terms) * ks * static_cast<size_t>(T) *
                                    static_cast<size_t>(ws_rstride(R)) * 4u;
 }
@@ -348,18 +374,24 @@ hipError_t launch_decode(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                          void* y, int y_dtype, int64_t ldy, int accumulate,
                          void* ws, hipStream_t s) {
   int n1 = 0;
-  const Stage1 a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1);
+  Stage1 a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1, 16);
+  const int nw = pick_waves(a, n1, R, true);
+  if (nw != 16) a = make_stage1(t, M, R, x, x_dtype, T, ldx, ws, true, &n1, nw);
   Stage2 b = make_stage2(t, a, N, R, T, ws, n1);
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
   const int kw1 = static_cast<int>(layout_kw(M)), kw2 = static_cast<int>(layout_kw(R));
-  return run<float, MODE_F>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1, kw2, s);
+  if (nw == 16)
+    return run<float, MODE_F, 16>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1, kw2, s);
+  return run<float, MODE_F, 8>(a, b, n1, static_cast<int>(b.n2), 1, pick_tb(T), kw1, kw2, s);
 }
 
 hipError_t launch_bool_decode(const TermPtrs& t, int64_t N, int64_t M, const void* x,
                               int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
                               int64_t ldy, int accumulate, void* ws, hipStream_t s) {
   int n1 = 0;
-  const Stage1 a = make_stage1(t, M, N, x, x_dtype, T, ldx, ws, true, &n1);
+  Stage1 a = make_stage1(t, M, N, x, x_dtype, T, ldx, ws, true, &n1, 16);
+  const int nw = pick_waves(a, n1, 0, false);
+  if (nw != 16) a = make_stage1(t, M, N, x, x_dtype, T, ldx, ws, true, &n1, nw);
   SumArgs b{};
   b.L = t.n; b.ks = a.ks; b.T = T; b.N = N; b.rs = a.rs;
   b.ws = static_cast<const float*>(a.ws);
@@ -369,20 +401,28 @@ hipError_t launch_bool_decode(const TermPtrs& t, int64_t N, int64_t M, const voi
   b.sync = make_sync(ws, n1, n2);
   const unsigned grid = static_cast<unsigned>(n1 + n2);
   const int tb = pick_tb(T), kw = static_cast<int>(layout_kw(M));
-#define DBF_BOOL(TB_, KW_) \
-  bool_decode_kernel<TB_, KW_><<<dim3(grid), kThreads, lds_bytes<float, TB_, KW_>(), s>>>(a, b, n1)
-#define DBF_BOOL_KW(TB_)          \
-  switch (kw) {                   \
-    case 1: DBF_BOOL(TB_, 1); break; \
-    case 2: DBF_BOOL(TB_, 2); break; \
-    case 3: DBF_BOOL(TB_, 3); break; \
-    default: DBF_BOOL(TB_, 4); break; \
+#define DBF_BOOL(TB_, KW_, NW_)                                                         \
+  bool_decode_kernel<TB_, KW_, NW_>                                                     \
+      <<<dim3(grid), 64 * NW_, lds_bytes<float, TB_, KW_, NW_>(), s>>>(a, b, n1)
+#define DBF_BOOL_KW(TB_, NW_)              \
+  switch (kw) {                            \
+    case 1: DBF_BOOL(TB_, 1, NW_); break;  \
+    case 2: DBF_BOOL(TB_, 2, NW_); break;  \
+    case 3: DBF_BOOL(TB_, 3, NW_); break;  \
+    default: DBF_BOOL(TB_, 4, NW_); break; \
   }
-  switch (tb) {
-    case 1: DBF_BOOL_KW(1); break;
-    case 2: DBF_BOOL_KW(2); break;
-    default: DBF_BOOL_KW(4); break;
+#define DBF_BOOL_TB(NW_)                \
+  switch (tb) {                         \
+    case 1: DBF_BOOL_KW(1, NW_); break; \
+    case 2: DBF_BOOL_KW(2, NW_); break; \
+    default: DBF_BOOL_KW(4, NW_); break; \
   }
+  if (nw == 16) {
+    DBF_BOOL_TB(16)
+  } else {
+    DBF_BOOL_TB(8)
+  }
+#undef DBF_BOOL_TB
 #undef DBF_BOOL_KW
 #undef DBF_BOOL
   return hipGetLastError();
@@ -393,7 +433,8 @@ hipError_t launch_decode_i8(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
                             int32_t* s1, int32_t* s2, void* y, int y_dtype,
                             int64_t ldy, void* ws, hipStream_t s) {
   int n1 = 0;
-  const Stage1 a = make_stage1(t, M, R, x, DBF_I8, T, ldx, ws, false, &n1);
+  // eight waves: the int8 variant is not timed against the float path
+  const Stage1 a = make_stage1(t, M, R, x, DBF_I8, T, ldx, ws, false, &n1, 8);
   Stage2 b = make_stage2(t, a, N, R, T, ws, n1);
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = 0; b.s2_out = s2;
   b.s1_out = s1;
@@ -401,8 +442,8 @@ hipError_t launch_decode_i8(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   const int tb = pick_tb(T), kw1 = static_cast<int>(layout_kw(M)),
             kw2 = static_cast<int>(layout_kw(R));
   if (t.beta[0] == nullptr)
-    return run<int32_t, MODE_I8>(a, b, n1, static_cast<int>(b.n2), run2, tb, kw1, kw2, s);
-  return run<float, MODE_I8_BETA>(a, b, n1, static_cast<int>(b.n2), run2, tb, kw1, kw2, s);
+    return run<int32_t, MODE_I8, 8>(a, b, n1, static_cast<int>(b.n2), run2, tb, kw1, kw2, s);
+  return run<float, MODE_I8_BETA, 8>(a, b, n1, static_cast<int>(b.n2), run2, tb, kw1, kw2, s);
 }
 
 }  // namespace dbf

@@ -11,10 +11,11 @@
 // (LoRDBA section 2, "Kernel de Inferencia": additions and subtractions in
 // place of multiplications in the inner products).
 //
-// A workgroup is 8 wavefronts over one 64-row tile; lane = row.  A pass
-// covers 8 * PW K-blocks; wave wv takes blocks kp + j * 8 + wv (j < PW), so
-// every wave reads whole contiguous tiles and all 64 lanes of a wave look up
-// the same group's 16 entries together (16 LDS banks, no conflicts).
+// A workgroup is NW wavefronts over one 64-row tile (16 in the decode
+// kernels, 8 in the adapter kernels); lane = row.  A pass covers NW * PW
+// K-blocks; wave wv takes blocks kp + j * NW + wv (j < PW), so every wave
+// reads whole contiguous tiles and all 64 lanes of a wave look up the same
+// group's 16 entries together (16 LDS banks, no conflicts).
 #pragma once
 
 #include "dbf_internal.h"
@@ -22,7 +23,11 @@
 namespace dbf {
 namespace lut {
 
-constexpr int kWaves = 8;
+// Waves per workgroup: the templates' default, 16.  The decode launchers
+// pick 16 or 8 per launch (pick_waves in dbf_decode.hip); the adapter
+// kernels use 8 (their row roles need more than the 128 registers a
+// 1024-thread workgroup leaves a wave).
+constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxKS = 8;
 constexpr unsigned kSpinLimit = 1u << 26;
@@ -35,13 +40,13 @@ inline int pick_tb(int64_t T) { return T <= 1 ? 1 : (T <= 4 ? 2 : 4); }
 
 // LDS (elements of type A): tables [TB][groups][16], wave partials
 // [4][TB][64].
-template <int TB, int KW>
-__host__ __device__ constexpr int tbl_elems() { return TB * kWaves * pw_of(TB) * 8 * KW * 16; }
-template <int TB>
-__host__ __device__ constexpr int red_elems() { return kWaves * TB * 64; }
-template <typename A, int TB, int KW>
+template <int TB, int KW, int NW = kWaves>
+__host__ __device__ constexpr int tbl_elems() { return TB * NW * pw_of(TB) * 8 * KW * 16; }
+template <int TB, int NW = kWaves>
+__host__ __device__ constexpr int red_elems() { return NW * TB * 64; }
+template <typename A, int TB, int KW, int NW = kWaves>
 __host__ __device__ constexpr size_t lds_bytes() {
-  return sizeof(A) * (tbl_elems<TB, KW>() + red_elems<TB>());
+  return sizeof(A) * (tbl_elems<TB, KW, NW>() + red_elems<TB, NW>());
 }
 
 // A result another workgroup of the launch will read: written through to
@@ -94,7 +99,7 @@ __device__ __forceinline__ void load_row_words(const uint32_t* p, uint32_t* wd) 
 }
 
 // This lane's words of the pass starting at K-block kp (zeros past kb_end).
-template <int TB, int KW>
+template <int TB, int KW, int NW = kWaves>
 __device__ __forceinline__ void load_pass_bits(const uint32_t* __restrict__ bits,
                                                int64_t rt, int64_t nkb, int64_t kp,
                                                int64_t kb_end,
@@ -102,7 +107,7 @@ __device__ __forceinline__ void load_pass_bits(const uint32_t* __restrict__ bits
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < pw_of(TB); ++j) {
-    const int64_t kb = kp + j * kWaves + wv;
+    const int64_t kb = kp + j * NW + wv;
 #pragma unroll
     for (int w = 0; w < KW; ++w) wd[j][w] = 0;
     if (kb < kb_end) load_row_words<KW>(bits + ((rt * nkb + kb) * 64 + lane) * KW, wd[j]);
@@ -111,9 +116,9 @@ __device__ __forceinline__ void load_pass_bits(const uint32_t* __restrict__ bits
 
 // Table entries of a pass, [TB][ng] (ng groups of four activations per
 // token), and how many of them one thread builds.
-template <int TB, int KW>
+template <int TB, int KW, int NW = kWaves>
 __host__ __device__ constexpr int ents_per_thread() {
-  return (TB * kWaves * pw_of(TB) * 8 * KW + kThreads - 1) / kThreads;
+  return (TB * NW * pw_of(TB) * 8 * KW + 64 * NW - 1) / (64 * NW);
 }
 
 // The four activations of each table entry this thread builds (entry
@@ -121,12 +126,12 @@ __host__ __device__ constexpr int ents_per_thread() {
 // Vector loads return in order within a wave, so a caller issues these loads
 // before loads whose data it needs later (the pass's sign words), and the
 // table build need not wait for those.
-template <typename A, int TB, int KW, typename Act4>
+template <typename A, int TB, int KW, int NW = kWaves, typename Act4>
 __device__ __forceinline__ void load_acts(Act4 act4, int ng,
-                                          A (&v)[ents_per_thread<TB, KW>()][4]) {
+                                          A (&v)[ents_per_thread<TB, KW, NW>()][4]) {
 #pragma unroll
-  for (int i = 0; i < ents_per_thread<TB, KW>(); ++i) {
-    const int e = threadIdx.x + i * kThreads;
+  for (int i = 0; i < ents_per_thread<TB, KW, NW>(); ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
     if (e < TB * ng) {
       const int tok = e / ng, g = e - tok * ng;
       act4(tok, g, v[i]);
@@ -139,17 +144,16 @@ __device__ __forceinline__ void load_acts(Act4 act4, int ng,
 // over the pass of S[row, k] * act[tok][k].  Two accumulators per token keep
 // the adds of consecutive nibbles independent, so many LDS reads are in
 // flight.  Ends with a barrier, so the tables may be overwritten afterwards.
-template <typename A, int TB, int KW>
-__device__ __forceinline__ void tables_and_lookups_v(const A (&v)[ents_per_thread<TB, KW>()][4],
-                                                     A* tbl, int ng, int64_t kp, int64_t kb_end,
-                                                     const uint32_t (&wd)[pw_of(TB)][KW],
-                                                     A* acc) {
+template <typename A, int TB, int KW, int NW = kWaves>
+__device__ __forceinline__ void tables_and_lookups_v(
+    const A (&v)[ents_per_thread<TB, KW, NW>()][4], A* tbl, int ng, int64_t kp, int64_t kb_end,
+    const uint32_t (&wd)[pw_of(TB)][KW], A* acc) {
   constexpr int PW = pw_of(TB);
-  constexpr int gpp = kWaves * PW * 8 * KW;
+  constexpr int gpp = NW * PW * 8 * KW;
   const int wv = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < ents_per_thread<TB, KW>(); ++i) {
-    const int e = threadIdx.x + i * kThreads;
+  for (int i = 0; i < ents_per_thread<TB, KW, NW>(); ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
     if (e < TB * ng) {
       const int tok = e / ng, g = e - tok * ng;
       build_signed16<A>(v[i][0], v[i][1], v[i][2], v[i][3], tbl + (tok * gpp + g) * 16);
@@ -161,8 +165,8 @@ __device__ __forceinline__ void tables_and_lookups_v(const A (&v)[ents_per_threa
   for (int tok = 0; tok < TB; ++tok) acc2[tok] = A(0);
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
-    if (kp + j * kWaves + wv >= kb_end) continue;  // wave-uniform
-    const A* tb = tbl + ((j * kWaves + wv) * 8 * KW) * 16;
+    if (kp + j * NW + wv >= kb_end) continue;  // wave-uniform
+    const A* tb = tbl + ((j * NW + wv) * 8 * KW) * 16;
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
 #pragma unroll
@@ -182,19 +186,19 @@ __device__ __forceinline__ void tables_and_lookups_v(const A (&v)[ents_per_threa
   __syncthreads();
 }
 
-template <typename A, int TB, int KW, typename Act4>
+template <typename A, int TB, int KW, int NW = kWaves, typename Act4>
 __device__ __forceinline__ void tables_and_lookups(Act4 act4, A* tbl, int ng, int64_t kp,
                                                    int64_t kb_end,
                                                    const uint32_t (&wd)[pw_of(TB)][KW],
                                                    A* acc) {
-  A v[ents_per_thread<TB, KW>()][4];
-  load_acts<A, TB, KW>(act4, ng, v);
-  tables_and_lookups_v<A, TB, KW>(v, tbl, ng, kp, kb_end, wd, acc);
+  A v[ents_per_thread<TB, KW, NW>()][4];
+  load_acts<A, TB, KW, NW>(act4, ng, v);
+  tables_and_lookups_v<A, TB, KW, NW>(v, tbl, ng, kp, kb_end, wd, acc);
 }
 
-// Sum of the 4 wave partials of each lane's row, in wave order; the result
+// Sum of the NW wave partials of each lane's row, in wave order; the result
 // is valid in wave 0.
-template <typename A, int TB>
+template <typename A, int TB, int NW = kWaves>
 __device__ __forceinline__ void reduce_waves(A* red, A* acc) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
@@ -205,7 +209,7 @@ __device__ __forceinline__ void reduce_waves(A* red, A* acc) {
     for (int tok = 0; tok < TB; ++tok) {
       A s = red[tok * 64 + lane];
 #pragma unroll
-      for (int v = 1; v < kWaves; ++v) s += red[(v * TB + tok) * 64 + lane];
+      for (int v = 1; v < NW; ++v) s += red[(v * TB + tok) * 64 + lane];
       acc[tok] = s;
     }
   }
@@ -248,7 +252,7 @@ struct OneTerm {
 
 // Stage-1 workgroup `bid` in [0, ntb * L * nrt * ks): its token block, term,
 // row tile of B2 and K-blocks [kb0, kb1) of its split (one or more passes).
-template <typename A, int TB, int KW, int MODE, class Src = TermSrc>
+template <typename A, int TB, int KW, int MODE, int NW = kWaves, class Src = TermSrc>
 __device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src, int bid, A* tbl,
                                                 A* red) {
   constexpr int PW = pw_of(TB);
@@ -277,8 +281,8 @@ __device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src,
   A acc[TB];
 #pragma unroll
   for (int i = 0; i < TB; ++i) acc[i] = A(0);
-  for (int64_t kp = kb0; kp < kb1; kp += kWaves * PW) {
-    const int64_t kb_end = min(kb1, kp + kWaves * PW);
+  for (int64_t kp = kb0; kp < kb1; kp += NW * PW) {
+    const int64_t kb_end = min(kb1, kp + NW * PW);
     const int64_t k0 = kp * 32 * KW;
     const int ng = static_cast<int>((kb_end - kp) * 8 * KW);
     auto act4 = [&](int tok, int g, A* a) {
@@ -319,12 +323,12 @@ __device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src,
     // the pass's sign words, then its activations, all in flight together
     // (the activations are converted as they arrive, so loads issued after
     // them would wait for them)
-    load_pass_bits<TB, KW>(bits, rt, p.nkb, kp, kb1, wd);
-    A v[ents_per_thread<TB, KW>()][4];
-    load_acts<A, TB, KW>(act4, ng, v);
-    tables_and_lookups_v<A, TB, KW>(v, tbl, ng, kp, kb_end, wd, acc);
+    load_pass_bits<TB, KW, NW>(bits, rt, p.nkb, kp, kb1, wd);
+    A v[ents_per_thread<TB, KW, NW>()][4];
+    load_acts<A, TB, KW, NW>(act4, ng, v);
+    tables_and_lookups_v<A, TB, KW, NW>(v, tbl, ng, kp, kb_end, wd, acc);
   }
-  reduce_waves<A, TB>(red, acc);
+  reduce_waves<A, TB, NW>(red, acc);
   if (wv == 0 && row < p.R) {
 #pragma unroll
     for (int tok = 0; tok < TB; ++tok) {
@@ -340,9 +344,9 @@ __device__ __forceinline__ void stage1_role_src(const Stage1& p, const Src& src,
   }
 }
 
-template <typename A, int TB, int KW, int MODE>
+template <typename A, int TB, int KW, int MODE, int NW = kWaves>
 __device__ __forceinline__ void stage1_role(const Stage1& p, int bid, A* tbl, A* red) {
-  stage1_role_src<A, TB, KW, MODE>(p, TermSrc{p.t}, bid, tbl, red);
+  stage1_role_src<A, TB, KW, MODE, NW>(p, TermSrc{p.t}, bid, tbl, red);
 }
 
 // ---- handoff between the two roles of a launch ---------------------------
@@ -466,15 +470,16 @@ __device__ __forceinline__ int token_adapter(const int32_t* idx, int64_t tok,
   return a;
 }
 
-// Splits of stage 1 along M (at most kMaxKS, whole K-block groups of 4)
-// so that stage 1 has about `want_wg` workgroups.
+// Splits of stage 1 along M (at most kMaxKS, each a whole number of passes'
+// worth of nw K-blocks) so that stage 1 has about `want_wg` workgroups of nw
+// waves.
 inline int pick_ks(int64_t nrt, int n_terms, int64_t nkb, int64_t want_wg,
-                   int64_t* kb_per_split) {
+                   int64_t* kb_per_split, int nw = kWaves) {
   const int64_t want = want_wg / std::max<int64_t>(1, nrt * n_terms);
-  const int64_t maxks = std::max<int64_t>(1, nkb / kWaves);
+  const int64_t maxks = std::max<int64_t>(1, nkb / nw);
   int64_t ks = std::max<int64_t>(1, std::min<int64_t>(std::min(want, maxks), kMaxKS));
   int64_t per = (nkb + ks - 1) / ks;
-  per = (per + kWaves - 1) / kWaves * kWaves;
+  per = (per + nw - 1) / nw * nw;
   ks = (nkb + per - 1) / per;
   *kb_per_split = per;
   return static_cast<int>(ks);
@@ -482,12 +487,12 @@ inline int pick_ks(int64_t nrt, int n_terms, int64_t nkb, int64_t want_wg,
 
 }  // namespace lut
 
-// Stage-1 parameters of the decode path for these sizes (K-split so that
-// stage 1 has enough workgroups when `split`, else as few splits as the
-// partial buffer allows); *n1 = its number of workgroups.  ws is the
-// caller's workspace (counters first).
+// Stage-1 parameters of the decode path for these sizes and workgroups of
+// nw waves (K-split so that stage 1 has enough waves when `split`, else as
+// few splits as the partial buffer allows); *n1 = its number of workgroups.
+// ws is the caller's workspace (counters first).
 lut::Stage1 make_stage1(const TermPtrs& t, int64_t M, int64_t R, const void* x,
                         int x_dtype, int64_t T, int64_t ldx, void* ws, bool split,
-                        int* n1);
+                        int* n1, int nw = lut::kWaves);
 
 }  // namespace dbf
