@@ -103,18 +103,37 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
     const uint16_t* xrow = p.x + (tok_ok ? tok : 0) * p.ldx;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     int64_t k0 = kbeg;
-    for (; k0 + kUnroll * 32 <= kend; k0 += kUnroll * 32) {
-      uint4 a[kUnroll], b[kUnroll];
+    // two loops rather than a choice per load: the bounded loads branch per
+    // lane, and a load under a branch makes the compiler wait for every
+    // load before the next (kUnroll round trips per step instead of one)
+    if (vec) {
+      for (; k0 + kUnroll * 32 <= kend; k0 += kUnroll * 32) {
+        uint4 a[kUnroll], b[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t k = k0 + u * 32 + lq * 8;
-        a[u] = vec ? load16(wrow, k) : load8(wrow, k, p.M, arow_ok, false);
-        b[u] = vec ? load16(xrow, k) : load8(xrow, k, p.M, tok_ok, false);
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t k = k0 + u * 32 + lq * 8;
+          a[u] = load16(wrow, k);
+          b[u] = load16(xrow, k);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
       }
+    } else {
+      for (; k0 + kUnroll * 32 <= kend; k0 += kUnroll * 32) {
+        uint4 a[kUnroll], b[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t k = k0 + u * 32 + lq * 8;
+          a[u] = load8(wrow, k, p.M, arow_ok, false);
+          b[u] = load8(xrow, k, p.M, tok_ok, false);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+      }
     }
     for (; k0 < kend; k0 += 32) {
       const int64_t k = k0 + lq * 8;
@@ -137,12 +156,33 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
     for (int q = 0; q < kMainWaves; ++q) v += red[q][i][j];
 
     if (MULTI || p.t.n > 0) {
-      if (!waited) {
-        lut::wait_producers(p.sync);
-        waited = true;
-      }
       const int64_t kw = layout_kw(p.R), nkb = layout_nkb(p.R);
       const int64_t rt = n >> 6, rin = n & 63;
+      bool active = owner && n < p.N && tt < p.T;
+      // The words of this owner's B1 row for one chunk of ranks, issued
+      // together (one at a time, each cost a round trip of its own).
+      constexpr int kWords = kRChunk / 32;
+      uint32_t wd[kWords];
+      auto load_words = [&](const uint32_t* b1, int64_t r0, int nr) {
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) {
+          wd[q] = 0u;
+          const int64_t r = r0 + 32 * q;
+          if (active && 32 * q < nr) {
+            const int64_t kb = r / (32 * kw), w = (r % (32 * kw)) / 32;
+            wd[q] = b1[((rt * nkb + kb) * 64 + rin) * kw + w];
+          }
+        }
+      };
+      // one adapter for every token: the first chunk's words before the
+      // wait, so their round trip overlaps it
+      if constexpr (!MULTI) load_words(p.t.b1[0], 0, static_cast<int>(min<int64_t>(kRChunk, p.R)));
+      if (!waited) {
+        // the partials are read with system-scope loads (written through by
+        // the producers), so no acquire (an L2 invalidation) is needed
+        lut::wait_producers(p.sync, false);
+        waited = true;
+      }
       // this owner's adapter (MULTI; -1: none)
       int am = -1;
       if constexpr (MULTI) {
@@ -150,12 +190,14 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
           am = idx[tt];
           if (am < -1 || am >= nad) am = -1;  // flagged by the stage-1 workgroups
         }
+        active = active && am >= 0;
       }
       const int nterms = MULTI ? 1 : p.t.n;
       for (int term = 0; term < nterms; ++term) {
         float z = 0.f;
         for (int64_t r0 = 0; r0 < p.R; r0 += kRChunk) {
           const int nr = static_cast<int>(min<int64_t>(kRChunk, p.R - r0));
+          if (!MULTI && (term > 0 || r0 > 0)) load_words(p.t.b1[term], r0, nr);
           // w[tok][r0 .. r0 + nr) summed over the K-split partials
           for (int e = tid; e < 16 * nr; e += kMainThreads) {
             const int jt = e / nr, rr = e - jt * nr;
@@ -166,7 +208,9 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
               float q[lut::kMaxKS];
 #pragma unroll
               for (int qq = 0; qq < lut::kMaxKS; ++qq)
-                if (qq < p.ks) q[qq] = src[qq * p.T * p.rs];
+                if (qq < p.ks)
+                  q[qq] = __hip_atomic_load(src + qq * p.T * p.rs, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
               s = q[0];
 #pragma unroll
               for (int qq = 1; qq < lut::kMaxKS; ++qq)
@@ -175,14 +219,15 @@ __device__ __forceinline__ void main_role(const Main& p, int64_t blk, float* lds
             wst[jt * kRChunk + rr] = s;
           }
           __syncthreads();
-          if (owner && n < p.N && tt < p.T && (!MULTI || am >= 0)) {
-            const uint32_t* b1 = MULTI ? static_cast<const uint32_t*>(ptrs[am]) : p.t.b1[term];
-            for (int r1 = 0; r1 < nr; r1 += 32) {
-              const int64_t r = r0 + r1;
-              const int64_t kb = r / (32 * kw), w = (r % (32 * kw)) / 32;
-              const uint32_t word = b1[((rt * nkb + kb) * 64 + rin) * kw + w];
-              const int rend = min(32, nr - r1);
-              const float* wr = wst + j * kRChunk + r1;
+          // a token's own adapter: its words once its index has arrived
+          if constexpr (MULTI) load_words(static_cast<const uint32_t*>(ptrs[am >= 0 ? am : 0]), r0, nr);
+          if (active) {
+#pragma unroll
+            for (int q = 0; q < kWords; ++q) {
+              if (32 * q >= nr) break;
+              const uint32_t word = wd[q];
+              const int rend = min(32, nr - 32 * q);
+              const float* wr = wst + j * kRChunk + 32 * q;
               for (int j2 = 0; j2 < rend; ++j2) z += ((word >> j2) & 1u) ? wr[j2] : -wr[j2];
             }
           }
