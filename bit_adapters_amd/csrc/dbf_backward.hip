@@ -21,6 +21,7 @@ namespace dbf {
 namespace {
 
 constexpr int64_t kTokChunk = 64;
+constexpr int kTokRound = 8;
 
 __global__ void __launch_bounds__(256) fill_ones_f16(uint16_t* p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -67,24 +68,40 @@ __global__ void __launch_bounds__(256) grad_partial4_kernel(PartArgs p) {
   auto fma4 = [&](const float4 a, const float4 b) {
     acc.x += a.x * b.x; acc.y += a.y * b.y; acc.z += a.z * b.z; acc.w += a.w * b.w;
   };
+  // kTokRound tokens a round: their loads are issued together, then added
+  // in token order (one round trip per round instead of per token)
+  auto run = [&](auto ld_a, auto ld_b) {
+    int64_t t = t0;
+    for (; t + kTokRound <= t1; t += kTokRound) {
+      float4 a[kTokRound], b[kTokRound];
+#pragma unroll
+      for (int u = 0; u < kTokRound; ++u) {
+        a[u] = ld_a(t + u);
+        b[u] = ld_b(t + u);
+      }
+#pragma unroll
+      for (int u = 0; u < kTokRound; ++u) fma4(a[u], b[u]);
+    }
+    for (; t < t1; ++t) fma4(ld_a(t), ld_b(t));
+  };
   int64_t c = col;
   if (c < p.L * p.N) {  // dalpha: dy . z
     const int64_t i = c / p.N, n = c - i * p.N;
     const float* z = p.z + i * p.T * p.N + n;
-    for (int64_t t = t0; t < t1; ++t)
-      fma4(load4_act(p.dy, p.dy_dtype, t * p.lddy + n), *reinterpret_cast<const float4*>(z + t * p.N));
+    run([&](int64_t t) { return load4_act(p.dy, p.dy_dtype, t * p.lddy + n); },
+        [&](int64_t t) { return *reinterpret_cast<const float4*>(z + t * p.N); });
   } else if ((c -= p.L * p.N) < p.L * p.R) {  // dbeta: s . g
     const int64_t i = c / p.R, r = c - i * p.R;
     const float* s = p.s + i * p.T * p.R + r;
     const float* g = p.g + i * p.T * p.R + r;
-    for (int64_t t = t0; t < t1; ++t)
-      fma4(*reinterpret_cast<const float4*>(s + t * p.R), *reinterpret_cast<const float4*>(g + t * p.R));
+    run([&](int64_t t) { return *reinterpret_cast<const float4*>(s + t * p.R); },
+        [&](int64_t t) { return *reinterpret_cast<const float4*>(g + t * p.R); });
   } else {  // dgamma: x . h
     c -= p.L * p.R;
     const int64_t i = c / p.M, m = c - i * p.M;
     const float* h = p.h + i * p.T * p.M + m;
-    for (int64_t t = t0; t < t1; ++t)
-      fma4(load4_act(p.x, p.x_dtype, t * p.ldx + m), *reinterpret_cast<const float4*>(h + t * p.M));
+    run([&](int64_t t) { return load4_act(p.x, p.x_dtype, t * p.ldx + m); },
+        [&](int64_t t) { return *reinterpret_cast<const float4*>(h + t * p.M); });
   }
   *reinterpret_cast<float4*>(p.part + static_cast<int64_t>(blockIdx.y) * ncol + col) = acc;
 }
@@ -124,8 +141,17 @@ __global__ void __launch_bounds__(256) grad_final_kernel(const float* part, int6
                                                           float* dbeta, float* dgamma) {
   const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (col >= ncol) return;
+  // eight chunks' loads in flight at a time, added in chunk order
   float acc = 0.f;
-  for (int q = 0; q < nchunks; ++q) acc += part[q * ncol + col];
+  int q = 0;
+  for (; q + 8 <= nchunks; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(q + u) * ncol + col];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; q < nchunks; ++q) acc += part[q * ncol + col];
   int64_t c = col;
   if (c < L * N) {
     if (dalpha) dalpha[c] = acc;
