@@ -80,6 +80,7 @@ struct PrepArgs {
 };
 
 constexpr int kPrepSeg = 8192;  // features of a row staged in LDS at a time
+constexpr int kPrepRound = 4;   // 16-byte chunks a thread loads at once
 
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   __shared__ float red[4];
@@ -100,7 +101,65 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
     // 2 j + 1 hold features j and j + 16 of a 32-feature group)
     for (int64_t seg = 0; seg < p.mpad; seg += kPrepSeg) {
       const int64_t segn = min<int64_t>(kPrepSeg, p.mpad - seg);
-      for (int64_t c = tid; c < segn / 8; c += 256) {
+      // chunk c's 8 values as fp16 pairs into LDS; acc gets their |u|
+      auto put = [&](int64_t c, const float* a) {
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const _Float16 lo = static_cast<_Float16>(a[2 * j]), hi = static_cast<_Float16>(a[2 * j + 1]);
+          acc += fabsf(static_cast<float>(lo)) + fabsf(static_cast<float>(hi));
+          o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+        }
+        reinterpret_cast<uint4*>(useg)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+      };
+      int64_t cstart = tid;
+      if (p.vec != 0 && seg + segn <= p.M) {
+        // the whole segment lies inside the row: kPrepRound chunks a thread
+        // per round, their loads issued together (addresses clamped to the
+        // last chunk, so no load sits under a branch), then converted in
+        // chunk order
+        const int64_t nch = segn / 8;
+        for (; cstart < nch; cstart += kPrepRound * 256) {
+          uint4 xv[kPrepRound][2], gv[kPrepRound];
+#pragma unroll
+          for (int j = 0; j < kPrepRound; ++j) {
+            const int64_t k0 = seg + 8 * min(cstart + 256 * j, nch - 1);
+            if (p.vec == 2) {
+              const float* xf32 = static_cast<const float*>(p.x) + tok * p.ldx + k0;
+              xv[j][0] = *reinterpret_cast<const uint4*>(xf32);
+              xv[j][1] = *reinterpret_cast<const uint4*>(xf32 + 4);
+            } else {
+              xv[j][0] = *reinterpret_cast<const uint4*>(xr + k0);
+            }
+            gv[j] = *reinterpret_cast<const uint4*>(g + k0);
+          }
+#pragma unroll
+          for (int j = 0; j < kPrepRound; ++j) {
+            if (cstart + 256 * j >= nch) break;
+            const uint32_t gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+            float a[8];
+            if (p.vec == 2) {
+              const uint32_t xw[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                                      xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                a[i] = f16_bits_to_f32(static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)))) * __uint_as_float(xw[i]);
+            } else {
+              const uint32_t xw[4] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w};
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
+                const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
+                const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
+                a[i] = f16_bits_to_f32(gb) * xf;
+              }
+            }
+            put(cstart + 256 * j, a);
+          }
+        }
+      }
+      for (int64_t c = cstart; c < segn / 8; c += 256) {
         const int64_t k0 = seg + 8 * c;
         float a[8];
         if (p.vec == 2 && k0 + 8 <= p.M) {
@@ -131,15 +190,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
             a[i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
           }
         }
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const _Float16 lo = static_cast<_Float16>(a[2 * j]), hi = static_cast<_Float16>(a[2 * j + 1]);
-          acc += fabsf(static_cast<float>(lo)) + fabsf(static_cast<float>(hi));
-          o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-        }
-        reinterpret_cast<uint4*>(useg)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        put(c, a);
       }
       __syncthreads();
       // output chunk c: group c / 4, pairs 4 (c % 4) .. + 3 = features
