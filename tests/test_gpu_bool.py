@@ -53,7 +53,7 @@ def test_configs(config, T, path):
 # kernels; on the MFMA path the few-tile shapes split K
 ODD = [(1, 1, 1, 1), (65, 33, 3, 1), (130, 300, 2, 5), (300, 129, 3, 20),
        (77, 1000, 2, 40), (513, 64, 1, 17), (40, 4100, 1, 33), (700, 3000, 4, 9),
-       (2000, 2048, 2, 130)]
+       (2000, 2048, 2, 130), (77, 9000, 2, 40)]
 
 
 @pytest.mark.parametrize("N,M,K,T", ODD)

@@ -29,7 +29,9 @@ def run(layer, x, path=MF, **kw):
 
 ODD = [(1, 1, 1, 1, 1), (65, 33, 17, 2, 3), (130, 300, 70, 3, 5),
        (300, 129, 257, 1, 130), (256, 256, 256, 1, 128), (77, 1000, 96, 2, 200),
-       (513, 64, 600, 1, 17), (40, 4100, 130, 1, 33)]
+       (513, 64, 600, 1, 17), (40, 4100, 130, 1, 33),
+       # a row of one full 8192-feature prep segment and a ragged one
+       (40, 9000, 130, 1, 33)]
 
 
 @pytest.mark.parametrize("N,M,R,L,T", ODD)
