@@ -62,6 +62,18 @@ def test_config2_forced_mfma():
     assert_close(y, ref)
 
 
+def test_config2_short_product_tiles():
+    # 250 tokens of the 4096 x 4096, R 2048 layer: stage 2 (16 K steps)
+    # runs on 32-row tiles, the last one ragged
+    print("mfma config 2 T 250", flush=True)
+    layer = S.make_layer(2)
+    x = S.make_x(2, 250)
+    y = to_np(run(layer, x))
+    toks = np.array([0, 31, 32, 128, 223, 224, 249])
+    ref = O.default().forward(O.terms64(layer), x64(x[toks]))
+    assert_close(y[toks], ref)
+
+
 def test_config5_sampled_tokens():
     print("mfma config 5", flush=True)
     layer = S.make_layer(5)
