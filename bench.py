@@ -110,8 +110,8 @@ def auto_path(T, L, blocks):
 def auto_dbf_path(N, M, R, L, T):
     # the library's automatic choice for the double-binary forward
     # (dbf_abi.hip, resolve_dbf_path): decode while T <= 4 or the sign work
-    # of the 4-token blocks is at most 1.5e8 lookups
-    return "decode" if T <= 4 or L * ((T + 3) // 4) * R * (N + M) <= 1.5e8 else "mfma"
+    # of the 4-token blocks is at most 1.0e8 lookups
+    return "decode" if T <= 4 or L * ((T + 3) // 4) * R * (N + M) <= 1.0e8 else "mfma"
 
 
 def main():

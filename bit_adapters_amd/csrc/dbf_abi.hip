@@ -27,18 +27,20 @@ bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0
 // 4-token block runs both products of every term), is at most
 // kAutoDecodeWork; else the MFMA products, whose cost at these token counts
 // is nearly flat.  Measured, decode vs MFMA, each path forced:
-//   512 x 512, R 256: decode faster through 64 tokens (10.8 vs 22.0 us);
-//   4096 x 4096, R 2048: faster through 32 tokens (29.2 vs 31.0 us), slower
-//     from 36 (41.2 vs 31.7 us: stage 1 then runs unsplit);
-//   11008 x 4096, R 2048, three terms: faster at 4 tokens (30.3 vs 42.3 us),
-//     slower from 5 (44.7 vs 42.2 us);
-//   8192 x 8192, R 6144: faster at 4 tokens (29.6 vs 46.5 us), slower at 8
-//     (52.7 vs 46.8 us).
+//   512 x 512, R 256: decode faster through 64 tokens (10.9 vs 17.8 us);
+//   4096 x 4096, R 2048: faster through 20 tokens (25.9 vs 27.4 us), even at
+//     28 (28.5 vs 28.7 us), slower at 24 by 3% (27.0 vs 27.8 us, the one
+//     measured point the rule gets wrong) and from 30 (29.7 vs 28.7 us);
+//   the same with two terms: slower from 12 tokens (34.1 vs 28.8 us);
+//   11008 x 4096, R 2048, three terms: faster at 4 tokens (30.8 vs 40.8 us),
+//     slower from 5 (44.9 vs 41.2 us);
+//   8192 x 8192, R 6144: faster at 4 tokens (29.6 vs 46.5 us); at 8 the
+//     16-wave decode edges ahead (45.2 vs 46.7 us) while the rule picks MFMA.
 // The boolean kernels (one product each, over a full N x M sign matrix):
 // decode while T <= 4 or K * ceil(T / 4) <= 4 (two 4096 x 4096 kernels:
 // decode faster at 8 tokens, 16.9 vs 18.5 us, slower at 16; three 11008 x
 // 4096 kernels: faster at 4 tokens, slower at 5).
-constexpr double kAutoDecodeWork = 1.5e8;
+constexpr double kAutoDecodeWork = 1.0e8;
 constexpr int64_t kAutoBoolDecodeBlocks = 4;
 
 int resolve_path(int path, int64_t T, int n_terms, int64_t blocks) {

@@ -703,15 +703,16 @@ __global__ void __launch_bounds__(256) reduce2_kernel(Reduce2Args p) {
 }
 
 // Tile shape and K-split of one product: the largest of 128 x 256,
-// 128 x 128, 64 x 128 that still gives >= 256 workgroups; a short product
-// (at most kShortSteps K steps) that 64 x 128 tiles leave below that takes
-// 32 x 128 tiles when they reach it; with fewer tiles than that, K is split
-// (each split >= 2 steps, at most kMaxSplit) towards kSplitTarget
-// workgroups.  (Measured on MI355X for 16 to 256 tokens: a target of 256
-// beat 512 and 1024; the split partials' traffic grows with the split
-// count.  32-row tiles beat a 2-way split of 64-row ones on products of 16
-// and 32 steps, 4096 x 4096 R 2048 at 256 tokens 42.3 -> 37.7 us, and lost
-// on one of 64, 40.7 -> 46.0 us: one MFMA per sign unpack instead of two.)
+// 128 x 128, 64 x 128 that still gives >= 256 workgroups, where a short
+// product (at most kShortSteps K steps) takes 32 x 128 tiles instead of
+// 64 x 128 ones; with fewer tiles than that, K is split (each split >= 2
+// steps, at most kMaxSplit) towards kSplitTarget workgroups.  (Measured on
+// MI355X for 16 to 256 tokens: a target of 256 beat 512 and 1024; the split
+// partials' traffic grows with the split count.  32-row tiles, which halve
+// the split, beat 64-row ones on products of 16 and 32 steps: 4096 x 4096
+// R 2048 at 64 tokens 33.2 -> 28.4 us, at 256 tokens 42.3 -> 37.7 us; on
+// products of 48 and 64 steps they lost, 51.6 -> 53.5 us and 40.7 -> 46.0
+// us, each sign unpack serving one MFMA instead of two.)
 
 struct Tiling {
   int bm, bn, ntt, ntc, nsplit;
@@ -722,7 +723,7 @@ Tiling choose_tiling(int64_t T, int64_t cols, int terms_in_grid, int64_t steps) 
   Tiling t{128, 256, 0, 0, 1};
   if (wgs(128, 256) < 256) t.bn = 128;
   if (wgs(128, 128) < 256) t.bm = 64;
-  if (wgs(64, 128) < 256 && wgs(32, 128) >= 256 && steps <= kShortSteps) t.bm = 32;
+  if (wgs(64, 128) < 256 && steps <= kShortSteps) t.bm = 32;
   t.ntt = static_cast<int>(cdiv(T, t.bm));
   t.ntc = static_cast<int>(cdiv(cols, t.bn));
   const int64_t tiles = wgs(t.bm, t.bn);

@@ -169,7 +169,7 @@ int dbf_workspace_check(void *ws, void *stream);
  *   accumulate       0: y = result; 1: y = y + result (in fp32).
  *   ws, ws_bytes     workspace of dbf_workspace_bytes(..., path) bytes.
  *   path             DBF_PATH_AUTO picks the decode path while T <= 4 or
- *                    n_terms * ceil(T / 4) * R * (N + M) <= 1.5e8, and the
+ *                    n_terms * ceil(T / 4) * R * (N + M) <= 1.0e8, and the
  *                    MFMA path above; the others force one (both are
  *                    correct for every T >= 1).
  * Accumulation is fp32; the decode path keeps every intermediate in fp32,

@@ -58,10 +58,11 @@ def test_workspace_bytes():
 
 
 # (N, M, R, terms, tokens, path): decode while T <= 4 or the sign work
-# terms * ceil(T / 4) * R * (N + M) is at most 1.5e8
-AUTO_CASES = [(4096, 4096, 2048, 1, 1, "decode"), (4096, 4096, 2048, 1, 32, "decode"),
-              (4096, 4096, 2048, 1, 33, "mfma"), (4096, 4096, 2048, 2, 16, "decode"),
-              (4096, 4096, 2048, 2, 17, "mfma"), (11008, 4096, 2048, 3, 4, "decode"),
+# terms * ceil(T / 4) * R * (N + M) is at most 1.0e8
+AUTO_CASES = [(4096, 4096, 2048, 1, 1, "decode"), (4096, 4096, 2048, 1, 20, "decode"),
+              (4096, 4096, 2048, 1, 21, "mfma"), (4096, 4096, 2048, 1, 32, "mfma"),
+              (4096, 4096, 2048, 2, 8, "decode"), (4096, 4096, 2048, 2, 9, "mfma"),
+              (4096, 4096, 2048, 2, 16, "mfma"), (11008, 4096, 2048, 3, 4, "decode"),
               (11008, 4096, 2048, 3, 5, "mfma"), (8192, 8192, 6144, 1, 4, "decode"),
               (8192, 8192, 6144, 1, 5, "mfma"), (512, 512, 256, 1, 64, "decode"),
               (512, 512, 256, 8, 64, "decode"), (16384, 16384, 8192, 8, 1, "decode"),
@@ -73,7 +74,7 @@ def test_auto_path_rule(N, M, R, L, T, path):
     want = D.DBF_PATH_DECODE if path == "decode" else D.DBF_PATH_MFMA
     # the rule itself, written out
     work = L * -(-T // 4) * R * (N + M)
-    assert (T <= 4 or work <= 1.5e8) == (path == "decode")
+    assert (T <= 4 or work <= 1.0e8) == (path == "decode")
     auto = D.dbf_workspace_bytes(N, M, R, L, T, D.DBF_PATH_AUTO)
     assert auto == D.dbf_workspace_bytes(N, M, R, L, T, want)
     other = D.DBF_PATH_MFMA if want == D.DBF_PATH_DECODE else D.DBF_PATH_DECODE
