@@ -706,9 +706,13 @@ __global__ void __launch_bounds__(256) reduce2_kernel(Reduce2Args p) {
 // 128 x 128, 64 x 128 that still gives >= 256 workgroups, where a short
 // product (at most kShortSteps K steps) takes 32 x 128 tiles instead of
 // 64 x 128 ones; with fewer tiles than that, K is split (each split >= 2
-// steps, at most kMaxSplit) towards kSplitTarget workgroups.  (Measured on
-// MI355X for 16 to 256 tokens: a target of 256 beat 512 and 1024; the split
-// partials' traffic grows with the split count.  32-row tiles, which halve
+// steps, at most kMaxSplit) towards kSplitTarget workgroups, taking among
+// up to twice the fewest such splits the count whose workgroups fill their
+// last round of 256 best.  (Measured on MI355X for 16 to 256 tokens: a
+// target of 256 beat 512 and 1024, the split partials' traffic growing with
+// the split count; but 86 tiles split 3 ways are 258 workgroups, two past a
+// round, and 5 ways (430) ran 11008 x 4096 products 4-20% faster, three
+// boolean kernels at 8 tokens 40.2 -> 32.3 us.  32-row tiles, which halve
 // the split, beat 64-row ones on products of 16 and 32 steps: 4096 x 4096
 // R 2048 at 64 tokens 33.2 -> 28.4 us, at 256 tokens 42.3 -> 37.7 us; on
 // products of 48 and 64 steps they lost, 51.6 -> 53.5 us and 40.7 -> 46.0
@@ -728,10 +732,21 @@ Tiling choose_tiling(int64_t T, int64_t cols, int terms_in_grid, int64_t steps) 
   t.ntc = static_cast<int>(cdiv(cols, t.bn));
   const int64_t tiles = wgs(t.bm, t.bn);
   if (tiles < 256) {
-    int64_t sp = cdiv(kSplitTarget, tiles);
-    sp = std::min<int64_t>(sp, steps / 2);
-    sp = std::min<int64_t>(sp, kMaxSplit);
-    t.nsplit = static_cast<int>(std::max<int64_t>(sp, 1));
+    // from the fewest splits that reach kSplitTarget workgroups up to twice
+    // as many, the count whose last round of 256 workgroups is fullest
+    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(steps / 2, kMaxSplit));
+    const int64_t sp0 = std::min<int64_t>(cdiv(kSplitTarget, tiles), cap);
+    int64_t best = sp0;
+    double best_fill = 0.0;
+    for (int64_t sp = sp0; sp <= std::min<int64_t>(2 * sp0, cap); ++sp) {
+      const int64_t n = tiles * sp;
+      const double fill = static_cast<double>(n) / (256.0 * static_cast<double>(cdiv(n, 256)));
+      if (fill > best_fill + 1e-9) {
+        best_fill = fill;
+        best = sp;
+      }
+    }
+    t.nsplit = static_cast<int>(std::max<int64_t>(best, 1));
   }
   return t;
 }
