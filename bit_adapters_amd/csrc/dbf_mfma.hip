@@ -704,7 +704,8 @@ __global__ void __launch_bounds__(256) reduce2_kernel(Reduce2Args p) {
 
 // Tile shape and K-split of one product: the largest of 128 x 256,
 // 128 x 128, 64 x 128 that still gives >= 256 workgroups, where a short
-// product (at most kShortSteps K steps) takes 32 x 128 tiles instead of
+// product (at most kShortSteps K steps), or one of at most 32 tokens (one
+// token tile either way, less padding), takes 32 x 128 tiles instead of
 // 64 x 128 ones; with fewer tiles than that, K is split (each split >= 2
 // steps, at most kMaxSplit) towards kSplitTarget workgroups, taking among
 // up to twice the fewest such splits the count whose workgroups fill their
@@ -727,7 +728,7 @@ Tiling choose_tiling(int64_t T, int64_t cols, int terms_in_grid, int64_t steps) 
   Tiling t{128, 256, 0, 0, 1};
   if (wgs(128, 256) < 256) t.bn = 128;
   if (wgs(128, 128) < 256) t.bm = 64;
-  if (wgs(64, 128) < 256 && steps <= kShortSteps) t.bm = 32;
+  if (wgs(64, 128) < 256 && (steps <= kShortSteps || T <= 32)) t.bm = 32;
   t.ntt = static_cast<int>(cdiv(T, t.bm));
   t.ntc = static_cast<int>(cdiv(cols, t.bn));
   const int64_t tiles = wgs(t.bm, t.bn);
