@@ -107,6 +107,15 @@ def auto_path(T, L, blocks):
     return "decode" if T <= 4 or L * ((T + 3) // 4) <= blocks else "mfma"
 
 
+def auto_bool_path(T, K):
+    # the library's automatic choice for the boolean kernels (dbf_abi.hip,
+    # resolve_bool_path): decode while its launch has one token block or
+    # K times its token blocks is at most 4
+    tb = 1 if T <= 1 else (2 if T <= 4 else 4)
+    blocks = (T + tb - 1) // tb
+    return "decode" if blocks == 1 or K * blocks <= 4 else "mfma"
+
+
 def auto_dbf_path(N, M, R, L, T):
     # the library's automatic choice for the double-binary forward
     # (dbf_abi.hip, resolve_dbf_path): decode while T <= 4 or the sign work
@@ -287,7 +296,7 @@ def main():
         path = {1: "decode", 2: "mfma"}.get(args.path) or auto_path(T, 1, 4)
     else:
         path = "adapter" if base else ({1: "decode", 2: "mfma"}.get(args.path)
-                                       or (auto_path(T, L, 4) if boolk
+                                       or (auto_bool_path(T, L) if boolk
                                            else auto_dbf_path(N, M, R, L, T)))
     # achieved = algorithmic bytes (flops) per step / HIP-event time per step;
     # decode and adapter steps are one kernel launch each, the MFMA step is

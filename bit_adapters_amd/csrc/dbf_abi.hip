@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "dbf_internal.h"
+#include "dbf_lut.h"
 
 namespace {
 
@@ -37,9 +38,12 @@ bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0
 //   8192 x 8192, R 6144: faster at 4 tokens (29.6 vs 46.5 us); at 8 the
 //     16-wave decode edges ahead (45.2 vs 46.7 us) while the rule picks MFMA.
 // The boolean kernels (one product each, over a full N x M sign matrix):
-// decode while T <= 4 or K * ceil(T / 4) <= 4 (two 4096 x 4096 kernels:
-// decode faster at 8 tokens, 16.9 vs 18.5 us, slower at 16; three 11008 x
-// 4096 kernels: faster at 4 tokens, slower at 5).
+// decode while its launch has one token block (up to 2 tokens) or K times
+// its token blocks (of 1, 2 or 4 tokens) is at most 4.  Measured: two
+// 4096 x 4096 kernels, decode faster through 4 tokens (13.7 vs 16.8 us),
+// within 3% at 6 and 8, slower from 12 (27.1 vs 17.3 us); three 11008 x
+// 4096 kernels, faster through 2 tokens (22.4 vs 26.5 us), slower from 3
+// (33.4 vs 26.7 us).
 constexpr double kAutoDecodeWork = 1.0e8;
 constexpr int64_t kAutoBoolDecodeBlocks = 4;
 
@@ -47,6 +51,14 @@ int resolve_path(int path, int64_t T, int n_terms, int64_t blocks) {
   if (path != DBF_PATH_AUTO) return path;
   const bool decode = T <= 4 || n_terms * ((T + 3) / 4) <= blocks;
   return decode ? DBF_PATH_DECODE : DBF_PATH_MFMA;
+}
+
+int resolve_bool_path(int path, int64_t T, int n_kernels) {
+  if (path != DBF_PATH_AUTO) return path;
+  const int64_t tb = dbf::lut::pick_tb(T);
+  const int64_t blocks = (T + tb - 1) / tb;
+  return blocks == 1 || n_kernels * blocks <= kAutoBoolDecodeBlocks ? DBF_PATH_DECODE
+                                                                    : DBF_PATH_MFMA;
 }
 
 int resolve_dbf_path(int path, int64_t N, int64_t M, int64_t R, int64_t T, int n_terms) {
@@ -337,7 +349,7 @@ int lordba_multi_adapter_forward(const void* w0, int64_t ldw, const dbf_term* ad
 
 size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T, int path) {
   if (N <= 0 || M <= 0 || n_kernels <= 0 || T <= 0) return 0;
-  if (resolve_path(path, T, n_kernels, kAutoBoolDecodeBlocks) == DBF_PATH_MFMA)
+  if (resolve_bool_path(path, T, n_kernels) == DBF_PATH_MFMA)
     return dbf::mfma_bool_ws_bytes(N, M, n_kernels, T);
   return dbf::decode_ws_bytes(N, M, N, n_kernels, T);
 }
@@ -369,7 +381,7 @@ int dbf_bool_forward(const dbf_bool_kernel* kernels, int n_kernels, int64_t N, i
   if (ldx < M) return fail(DBF_EINVAL, "ldx %lld < M %lld", (long long)ldx, (long long)M);
   if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
   if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
-  const int p = resolve_path(path, T, n_kernels, kAutoBoolDecodeBlocks);
+  const int p = resolve_bool_path(path, T, n_kernels);
   int e = check_ws(ws, ws_bytes, dbf_bool_workspace_bytes(N, M, n_kernels, T, p));
   if (e != DBF_OK) return e;
   e = check_device();

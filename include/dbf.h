@@ -254,8 +254,10 @@ size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T,
  *   y                [T x N], y_dtype DBF_F32, DBF_BF16 or DBF_F16, ldy.
  *   accumulate       0: y = result; 1: y = y + result (in fp32).
  *   ws, ws_bytes     workspace of dbf_bool_workspace_bytes(..., path) bytes.
- *   path             DBF_PATH_AUTO picks the decode path while T <= 4 or
- *                    n_kernels * ceil(T / 4) <= 4, and the MFMA path above;
+ *   path             DBF_PATH_AUTO picks the decode path while T <= 2 or
+ *                    n_kernels * b <= 4, b the decode's token blocks
+ *                    (ceil(T / 2) for T <= 4, ceil(T / 4) above), and the
+ *                    MFMA path otherwise;
  *                    the others force one.
  * The decode path keeps everything in fp32; the MFMA path rounds s_in . x
  * to fp16 once, with fp32 accumulation.  x, y 16-byte aligned.  T = 0 is

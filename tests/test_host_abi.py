@@ -220,11 +220,14 @@ def test_bool_workspace_bytes():
     assert (D.dbf_bool_workspace_bytes(4096, 4096, 2, 1) == dec)
 
 
-@pytest.mark.parametrize("T,K,path", [(1, 2, "decode"), (4, 3, "decode"), (8, 2, "decode"),
+@pytest.mark.parametrize("T,K,path", [(1, 2, "decode"), (2, 8, "decode"), (4, 2, "decode"),
+                                      (3, 3, "mfma"), (4, 3, "mfma"), (8, 2, "decode"),
                                       (9, 2, "mfma"), (5, 3, "mfma"), (16, 1, "decode"),
-                                      (17, 1, "mfma"), (4, 8, "decode")])
+                                      (17, 1, "mfma"), (4, 8, "mfma")])
 def test_bool_auto_path_rule(T, K, path):
-    # decode while T <= 4 or n_kernels * ceil(T / 4) <= 4
+    # decode while the decode launch has one token block (T <= 2) or
+    # n_kernels times its blocks (ceil(T / 2) to 4 tokens, ceil(T / 4)
+    # above) is at most 4
     want = D.DBF_PATH_DECODE if path == "decode" else D.DBF_PATH_MFMA
     auto = D.dbf_bool_workspace_bytes(4096, 4096, K, T, D.DBF_PATH_AUTO)
     assert auto == D.dbf_bool_workspace_bytes(4096, 4096, K, T, want)
