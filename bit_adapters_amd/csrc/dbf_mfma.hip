@@ -4,18 +4,22 @@
 // with the +-1 signs unpacked from the packed bits straight into MFMA
 // operand registers (exact in fp16).
 //
-//   prep:     u_i = fp16(gamma_i . x) for every term, and per token
-//             l_i[t] = sum_m |u_i[t, m]|; bmax_i = max_r |beta_i[r]|
+//   prep:     u_i = fp16(sigma_t gamma_i . x) for every term, sigma_t the
+//             power of two that puts the token's largest |gamma_i . x| (over
+//             every term) in [2^14, 2^15); per token l_i[t] = sum_m
+//             |u_i[t, m]| / sigma_t; bmax_i = max_r |beta_i[r]|
 //   scale:    s_t = 2^e, the largest power of two with
 //             s_t * max_i(bmax_i * l_i[t]) * (1 + 2^-8) <= 2^14; since
 //             |w_i[t, r]| <= bmax_i * l_i[t], every s_t * w fits fp16
-//   stage 1:  v_i[t, r] = fp16(s_t * beta_i[r] * sum_m S2_i[r, m] u_i[t, m])
+//   stage 1:  v_i[t, r] = fp16(s_t / sigma_t * beta_i[r] * sum_m S2_i[r, m] u_i[t, m])
 //   stage 2:  y[t, n] = (1 / s_t) sum_i sum_r (+-alpha_i[n]) v_i[t, r]
 //             (one term: alpha_1[n] / s_t * sum_r (+-1) v_1[t, r], alpha
 //             applied in the epilogue)
 //
 // Rounding: u and v are each rounded to fp16 once (relative 2^-11), all
-// sums are fp32; alpha, beta and the +-1 signs are exact in fp16.
+// sums are fp32; alpha, beta and the +-1 signs are exact in fp16.  Both
+// fp16 intermediates carry a per-token power of two, so any finite input
+// that gives a finite output stays inside the fp16 range.
 //
 // Operand order.  The MFMA sums over k, so any k order works as long as A
 // and B agree.  u and v are stored with each 32 features reordered as pairs
@@ -57,15 +61,33 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t kpad(int64_t K) { return (K + BK - 1) / BK * BK; }
 
 // Power-of-two scale of the fp16 intermediate from the bound b = max_i
-// bmax_i * l_i[t]: s * b * (1 + 2^-8) <= 2^14.
+// bmax_i * l_i[t]: s * b * (1 + 2^-8) <= 2^14.  The exponent is clamped so
+// that s and 1 / s stay finite fp32 normals.
 __device__ __forceinline__ float scale_from_bound(float b) {
   if (!(b > 0.f)) return 1.f;
   int e = 0;
   frexpf(b * (1.f + 1.f / 256.f), &e);  // b' = f * 2^e, f in [0.5, 1)
-  return ldexpf(1.f, 14 - e);
+  return ldexpf(1.f, max(-100, min(100, 14 - e)));
 }
 
-// ---- prep: u = fp16(gamma . x) in pair order, l1 norms, max |beta| --------
+// Power of two that brings a token's largest |scale_in . x| into
+// [2^14, 2^15), so that fp16(sigma . scale_in . x) neither overflows nor
+// leaves the normal range where it matters (the products of scale_in and x
+// are exact in fp32, and a power of two commutes with the fp16 rounding
+// wherever the result is normal).  1 for an all-zero (or non-finite) row.
+__device__ __forceinline__ float act_scale(float amax) {
+  if (!(amax > 0.f) || !(amax <= 3.0e38f)) return 1.f;
+  int e = 0;
+  frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1)
+  return ldexpf(1.f, max(-100, min(100, 15 - e)));
+}
+
+// ---- prep: u = fp16(sigma_t gamma . x) in pair order, l1 norms, max |beta|
+//
+// sigma_t (act_scale of the token's largest |gamma_i . x| over every term) is
+// common to the terms of a token, so their products still add in one
+// accumulator; it is written to sig[t] and divided out after the products.
+// l1[i][t] is sum_m |u_i[t, m]| / sigma_t, the norm at the true scale.
 struct PrepArgs {
   const void* x;
   int x_dtype;
@@ -76,11 +98,92 @@ struct PrepArgs {
   _Float16* u;  // [L][T][mpad]
   float* l1;    // [L][T]
   float* bmax;  // [L]
+  float* sig;   // [T]
   int vec;      // 16-byte loads of x and gamma allowed (2: x is fp32)
 };
 
 constexpr int kPrepSeg = 8192;  // features of a row staged in LDS at a time
 constexpr int kPrepRound = 4;   // 16-byte chunks a thread loads at once
+
+// gamma . x of the chunks cs + 256 j (j < kPrepRound) of 8 features each
+// (chunk c holds features 8 c .. 8 c + 7 of the row), zeros past M.  The
+// vector loads of whole chunks are issued together with their addresses
+// clamped to the last whole chunk, so no load sits under a branch; the one
+// chunk that straddles M is read element by element.
+__device__ __forceinline__ void prep_round(const PrepArgs& p, int term, int64_t tok, int64_t cs,
+                                           float (&a)[kPrepRound][8]) {
+  const uint16_t* g = p.gamma[term];
+  const int64_t nfull = p.M / 8;
+  if (p.vec != 0 && nfull > 0) {
+    uint4 xv[kPrepRound][2], gv[kPrepRound];
+#pragma unroll
+    for (int j = 0; j < kPrepRound; ++j) {
+      const int64_t k0 = 8 * min(cs + 256 * j, nfull - 1);
+      if (p.vec == 2) {
+        const float* xf32 = static_cast<const float*>(p.x) + tok * p.ldx + k0;
+        xv[j][0] = *reinterpret_cast<const uint4*>(xf32);
+        xv[j][1] = *reinterpret_cast<const uint4*>(xf32 + 4);
+      } else {
+        xv[j][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + tok * p.ldx + k0);
+      }
+      gv[j] = *reinterpret_cast<const uint4*>(g + k0);
+    }
+#pragma unroll
+    for (int j = 0; j < kPrepRound; ++j) {
+      const int64_t c = cs + 256 * j;
+      if (c < nfull) {
+        const uint32_t gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+        if (p.vec == 2) {
+          const uint32_t xw[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                                  xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            a[j][i] = f16_bits_to_f32(static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)))) *
+                      __uint_as_float(xw[i]);
+        } else {
+          const uint32_t xw[4] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
+            const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
+            const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
+            a[j][i] = f16_bits_to_f32(gb) * xf;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int64_t k = 8 * c + i;
+          a[j][i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < kPrepRound; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t k = 8 * (cs + 256 * j) + i;
+      a[j][i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
+    }
+}
+
+// Sum (or max) of v over the 256 threads, returned to every thread.
+__device__ __forceinline__ float block_reduce(float v, bool sum, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = sum ? v + o : fmaxf(v, o);
+  }
+  __syncthreads();  // red may still be read from an earlier call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) r = sum ? r + red[w] : fmaxf(r, red[w]);
+  return r;
+}
 
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   __shared__ float red[4];
@@ -88,147 +191,82 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x;
   const int64_t nrow = static_cast<int64_t>(p.L) * p.T;
+  if (blk >= nrow) {
+    const int term = static_cast<int>(blk - nrow);
+    float m = 0.f;
+    for (int64_t r = tid; r < p.R; r += 256) m = fmaxf(m, fabsf(f16_bits_to_f32(p.beta[term][r])));
+    m = block_reduce(m, false, red);
+    if (tid == 0) p.bmax[term] = m;
+    return;
+  }
+  const int term = static_cast<int>(blk / p.T);
+  const int64_t tok = blk - static_cast<int64_t>(term) * p.T;
+  const int64_t nch = p.mpad / 8;  // chunks of the padded row
+  constexpr int64_t kRoundCh = 256 * kPrepRound;
+  // one round covers this thread's whole row: its values stay in registers
+  // from the max pass to the conversion
+  const bool single = p.L == 1 && nch <= kRoundCh && p.mpad <= kPrepSeg;
+  float keep[kPrepRound][8];
+
+  // pass 1: the token's largest |gamma_i . x| over every term
+  float amx = 0.f;
+  for (int i = 0; i < p.L; ++i)
+    for (int64_t cs = tid; cs < nch; cs += kRoundCh) {
+      prep_round(p, i, tok, cs, keep);
+#pragma unroll
+      for (int j = 0; j < kPrepRound; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amx = fmaxf(amx, fabsf(keep[j][e]));
+    }
+  const float sig = act_scale(block_reduce(amx, false, red));
+  if (term == 0 && tid == 0) p.sig[tok] = sig;
+
+  // pass 2: u = fp16(sigma . gamma . x) in natural order into LDS, a segment
+  // of kPrepSeg features at a time, then each thread writes one 16-byte
+  // chunk of the pair order (positions 2 j and 2 j + 1 hold features j and
+  // j + 16 of a 32-feature group)
   float acc = 0.f;
-  if (blk < nrow) {
-    const int term = static_cast<int>(blk / p.T);
-    const int64_t tok = blk - static_cast<int64_t>(term) * p.T;
-    const uint16_t* g = p.gamma[term];
-    _Float16* out = p.u + blk * p.mpad;
-    const uint16_t* xr = static_cast<const uint16_t*>(p.x) + tok * p.ldx;
-    // the row in segments of kPrepSeg features: u in natural order into LDS
-    // (coalesced 16-byte loads, 8 features per thread and chunk), then each
-    // thread writes one 16-byte chunk of the pair order (positions 2 j and
-    // 2 j + 1 hold features j and j + 16 of a 32-feature group)
-    for (int64_t seg = 0; seg < p.mpad; seg += kPrepSeg) {
-      const int64_t segn = min<int64_t>(kPrepSeg, p.mpad - seg);
-      // chunk c's 8 values as fp16 pairs into LDS; acc gets their |u|
-      auto put = [&](int64_t c, const float* a) {
+  _Float16* out = p.u + blk * p.mpad;
+  for (int64_t seg = 0; seg < p.mpad; seg += kPrepSeg) {
+    const int64_t segn = min<int64_t>(kPrepSeg, p.mpad - seg);
+    const int64_t c0 = seg / 8, c1 = c0 + segn / 8;
+    for (int64_t cs = c0 + tid; cs < c1; cs += kRoundCh) {
+      if (!single) prep_round(p, term, tok, cs, keep);
+#pragma unroll
+      for (int j = 0; j < kPrepRound; ++j) {
+        const int64_t c = cs + 256 * j;
+        if (c >= c1) break;
         uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const _Float16 lo = static_cast<_Float16>(a[2 * j]), hi = static_cast<_Float16>(a[2 * j + 1]);
+        for (int q = 0; q < 4; ++q) {
+          const _Float16 lo = static_cast<_Float16>(sig * keep[j][2 * q]);
+          const _Float16 hi = static_cast<_Float16>(sig * keep[j][2 * q + 1]);
           acc += fabsf(static_cast<float>(lo)) + fabsf(static_cast<float>(hi));
-          o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+          o[q] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        reinterpret_cast<uint4*>(useg)[c] = make_uint4(o[0], o[1], o[2], o[3]);
-      };
-      int64_t cstart = tid;
-      if (p.vec != 0 && seg + segn <= p.M) {
-        // the whole segment lies inside the row: kPrepRound chunks a thread
-        // per round, their loads issued together (addresses clamped to the
-        // last chunk, so no load sits under a branch), then converted in
-        // chunk order
-        const int64_t nch = segn / 8;
-        for (; cstart < nch; cstart += kPrepRound * 256) {
-          uint4 xv[kPrepRound][2], gv[kPrepRound];
-#pragma unroll
-          for (int j = 0; j < kPrepRound; ++j) {
-            const int64_t k0 = seg + 8 * min(cstart + 256 * j, nch - 1);
-            if (p.vec == 2) {
-              const float* xf32 = static_cast<const float*>(p.x) + tok * p.ldx + k0;
-              xv[j][0] = *reinterpret_cast<const uint4*>(xf32);
-              xv[j][1] = *reinterpret_cast<const uint4*>(xf32 + 4);
-            } else {
-              xv[j][0] = *reinterpret_cast<const uint4*>(xr + k0);
-            }
-            gv[j] = *reinterpret_cast<const uint4*>(g + k0);
-          }
-#pragma unroll
-          for (int j = 0; j < kPrepRound; ++j) {
-            if (cstart + 256 * j >= nch) break;
-            const uint32_t gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
-            float a[8];
-            if (p.vec == 2) {
-              const uint32_t xw[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
-                                      xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
-#pragma unroll
-              for (int i = 0; i < 8; ++i)
-                a[i] = f16_bits_to_f32(static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)))) * __uint_as_float(xw[i]);
-            } else {
-              const uint32_t xw[4] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w};
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
-                const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
-                const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
-                a[i] = f16_bits_to_f32(gb) * xf;
-              }
-            }
-            put(cstart + 256 * j, a);
-          }
-        }
+        reinterpret_cast<uint4*>(useg)[c - c0] = make_uint4(o[0], o[1], o[2], o[3]);
       }
-      for (int64_t c = cstart; c < segn / 8; c += 256) {
-        const int64_t k0 = seg + 8 * c;
-        float a[8];
-        if (p.vec == 2 && k0 + 8 <= p.M) {
-          const float* xf32 = static_cast<const float*>(p.x) + tok * p.ldx + k0;
-          const float4 x0 = *reinterpret_cast<const float4*>(xf32);
-          const float4 x1 = *reinterpret_cast<const float4*>(xf32 + 4);
-          const uint4 gv = *reinterpret_cast<const uint4*>(g + k0);
-          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            a[i] = f16_bits_to_f32(static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)))) * xs[i];
-        } else if (p.vec == 1 && k0 + 8 <= p.M) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xr + k0);
-          const uint4 gv = *reinterpret_cast<const uint4*>(g + k0);
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint16_t xb = static_cast<uint16_t>(xw[i >> 1] >> (16 * (i & 1)));
-            const uint16_t gb = static_cast<uint16_t>(gw[i >> 1] >> (16 * (i & 1)));
-            const float xf = p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(xb) : f16_bits_to_f32(xb);
-            a[i] = f16_bits_to_f32(gb) * xf;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int64_t k = k0 + i;
-            a[i] = k < p.M ? f16_bits_to_f32(g[k]) * load_act(p.x, p.x_dtype, tok * p.ldx + k) : 0.f;
-          }
-        }
-        put(c, a);
-      }
-      __syncthreads();
-      // output chunk c: group c / 4, pairs 4 (c % 4) .. + 3 = features
-      // 4 (c % 4) .. + 3 (low halves) and 16 + 4 (c % 4) .. + 3 (high halves)
-      for (int64_t c = tid; c < segn / 8; c += 256) {
-        const int64_t grp = c >> 2, q4 = c & 3;
-        const uint2 lo = reinterpret_cast<const uint2*>(useg)[grp * 8 + q4];      // features 4 q4 ..
-        const uint2 hi = reinterpret_cast<const uint2*>(useg)[grp * 8 + 4 + q4];  // 16 + 4 q4 ..
-        uint4 w;
-        w.x = (lo.x & 0xFFFFu) | (hi.x << 16);
-        w.y = (lo.x >> 16) | (hi.x & 0xFFFF0000u);
-        w.z = (lo.y & 0xFFFFu) | (hi.y << 16);
-        w.w = (lo.y >> 16) | (hi.y & 0xFFFF0000u);
-        reinterpret_cast<uint4*>(out + seg)[c] = w;
-      }
-      __syncthreads();
     }
-  } else {
-    const int term = static_cast<int>(blk - nrow);
-    for (int64_t r = tid; r < p.R; r += 256)
-      acc = fmaxf(acc, fabsf(f16_bits_to_f32(p.beta[term][r])));
+    __syncthreads();
+    // output chunk c: group c / 4, pairs 4 (c % 4) .. + 3 = features
+    // 4 (c % 4) .. + 3 (low halves) and 16 + 4 (c % 4) .. + 3 (high halves)
+    for (int64_t c = tid; c < segn / 8; c += 256) {
+      const int64_t grp = c >> 2, q4 = c & 3;
+      const uint2 lo = reinterpret_cast<const uint2*>(useg)[grp * 8 + q4];      // features 4 q4 ..
+      const uint2 hi = reinterpret_cast<const uint2*>(useg)[grp * 8 + 4 + q4];  // 16 + 4 q4 ..
+      uint4 w;
+      w.x = (lo.x & 0xFFFFu) | (hi.x << 16);
+      w.y = (lo.x >> 16) | (hi.x & 0xFFFF0000u);
+      w.z = (lo.y & 0xFFFFu) | (hi.y << 16);
+      w.w = (lo.y >> 16) | (hi.y & 0xFFFF0000u);
+      reinterpret_cast<uint4*>(out + seg)[c] = w;
+    }
+    __syncthreads();
   }
-  // sum (or max) over the workgroup: within each wave, then over the 4 waves
-  const bool sum = blk < nrow;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(acc, off);
-    acc = sum ? acc + o : fmaxf(acc, o);
-  }
-  if ((tid & 63) == 0) red[tid >> 6] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) r = sum ? r + red[w] : fmaxf(r, red[w]);
-    if (sum) p.l1[blk] = r;
-    else p.bmax[blk - nrow] = r;
-  }
+  // sum_m |u| at the true scale (sigma is a power of two: exact)
+  acc = block_reduce(acc, true, red);
+  if (tid == 0) p.l1[blk] = acc / sig;
 }
 
 // ---- the two products -------------------------------------------------
@@ -244,6 +282,8 @@ struct GemmArgs {
   const _Float16* a;        // A operand [L][T][kp] in pair order
   const float* l1;          // [L][T]
   const float* bmax;        // [L]
+  const float* sig;         // [T] prep's per-token power of two
+  int sig_div;              // stage 2 reads u itself (boolean kernels): divide by sig too
   int nsplit;               // K-splits (grid z); > 1: fp32 partials to `part`
   float* part;              // [nsplit][terms in grid][T][ldp]
   int64_t ldp;
@@ -342,12 +382,19 @@ gemm_kernel(GemmArgs p) {
   const int term_end = STAGE == 1 ? term_first + 1 : p.L;
 
   if (tid < BM) {
+    // stage 1: the factor s_t / sigma_t of v; stage 2: the divisor s_t of y
+    // (s_t sigma_t when the A operand is u itself)
     const int64_t tok = tok0 + tid;
-    float bnd = 0.f;
-    if (tok < p.T)
+    float ts = 1.f;
+    if (tok < p.T) {
+      float bnd = 0.f;
       for (int i = 0; i < p.L; ++i)
         bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
-    tokscale[tid] = scale_from_bound(bnd);
+      ts = scale_from_bound(bnd);
+      if (STAGE == 1) ts /= p.sig[tok];
+      else if (p.sig_div) ts *= p.sig[tok];
+    }
+    tokscale[tid] = ts;
   }
 
   const int spt = static_cast<int>(p.kp / BK);  // K steps per term
@@ -608,6 +655,7 @@ struct Reduce1Args {
   const uint16_t* beta[DBF_MAX_TERMS];
   const float* l1;
   const float* bmax;
+  const float* sig;
   _Float16* v;
 };
 
@@ -621,7 +669,7 @@ __global__ void __launch_bounds__(256) reduce1_kernel(Reduce1Args p) {
   const int64_t tok = row - static_cast<int64_t>(term) * p.T;
   float bnd = 0.f;
   for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
-  const float sc = scale_from_bound(bnd);
+  const float sc = scale_from_bound(bnd) / p.sig[tok];
   const int64_t r0[2] = {32 * (c >> 2) + 4 * (c & 3), 32 * (c >> 2) + 16 + 4 * (c & 3)};
   const int64_t sstride = static_cast<int64_t>(p.L) * p.T * p.ldp;
   // all splits' loads in flight at once, then the sums in split order
@@ -667,6 +715,8 @@ struct Reduce2Args {
   const uint16_t* alpha;
   const float* l1;
   const float* bmax;
+  const float* sig;
+  int sig_div;
   void* y;
   int y_dtype;
   int64_t ldy;
@@ -681,7 +731,7 @@ __global__ void __launch_bounds__(256) reduce2_kernel(Reduce2Args p) {
   const int64_t n0 = 4 * (idx - tok * nch);
   float bnd = 0.f;
   for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
-  const float sc = scale_from_bound(bnd);
+  const float sc = scale_from_bound(bnd) * (p.sig_div ? p.sig[tok] : 1.f);
   float4 q[kMaxSplit];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplit; ++sp)
@@ -803,7 +853,7 @@ Plan make_plan(int64_t N, int64_t M, int64_t R, int L, int64_t T) {
 }
 
 struct WsLayout {
-  size_t u, v, l1, bmax, part, total;
+  size_t u, v, l1, bmax, sig, part, total;
 };
 
 WsLayout ws_layout(int64_t N, int64_t M, int64_t R, int L, int64_t T) {
@@ -815,6 +865,7 @@ WsLayout ws_layout(int64_t N, int64_t M, int64_t R, int L, int64_t T) {
   w.v = off; off += al(static_cast<size_t>(L) * T * kpad(R) * 2);
   w.l1 = off; off += al(static_cast<size_t>(L) * T * 4);
   w.bmax = off; off += al(static_cast<size_t>(L) * 4);
+  w.sig = off; off += al(static_cast<size_t>(T) * 4);
   // split partials: stage 1's are consumed before stage 2 writes its own
   size_t part = 0;
   if (pl.t1.nsplit > 1) part = static_cast<size_t>(pl.t1.nsplit) * L * T * round4(R) * 4;
@@ -835,7 +886,7 @@ namespace {
 // Boolean kernels: u_k [L][T][kpad(M)], per-token sums, max|s| slots (zero),
 // then the split partials of the one product.
 struct BoolLayout {
-  size_t u, l1, bmax, part, total;
+  size_t u, l1, bmax, sig, part, total;
   Tiling tl;
 };
 
@@ -847,6 +898,7 @@ BoolLayout bool_layout(int64_t N, int64_t M, int L, int64_t T) {
   w.u = off; off += al(static_cast<size_t>(L) * T * kpad(M) * 2);
   w.l1 = off; off += al(static_cast<size_t>(L) * T * 4);
   w.bmax = off; off += al(static_cast<size_t>(L) * 4);
+  w.sig = off; off += al(static_cast<size_t>(T) * 4);
   w.part = off;
   if (w.tl.nsplit > 1) off += al(static_cast<size_t>(w.tl.nsplit) * T * round4(N) * 4);
   w.total = off;
@@ -859,10 +911,10 @@ size_t mfma_bool_ws_bytes(int64_t N, int64_t M, int n_kernels, int64_t T) {
   return bool_layout(N, M, n_kernels, T).total;
 }
 
-// y = sum_k s_out_k . (Wb_k u_k), u_k = fp16(s_in_k . x): prep, then the
-// stage-2 product with the sign matrices in the place of B1 and u in the
-// place of v.  prep sees no beta (R = 0), so max|beta| is 0 and the token
-// scale is exactly 1: u is used as rounded, with no further scaling.
+// y = sum_k s_out_k . (Wb_k u_k) / sigma_t, u_k = fp16(sigma_t s_in_k . x):
+// prep, then the stage-2 product with the sign matrices in the place of B1
+// and u in the place of v.  prep sees no beta (R = 0), so max|beta| is 0 and
+// s_t is exactly 1: the product divides by sigma_t alone.
 hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void* x,
                             int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
                             int64_t ldy, int accumulate, void* ws, hipStream_t s) {
@@ -871,11 +923,12 @@ hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void*
   _Float16* u = reinterpret_cast<_Float16*>(base + lay.u);
   float* l1 = reinterpret_cast<float*>(base + lay.l1);
   float* bmax = reinterpret_cast<float*>(base + lay.bmax);
+  float* sig = reinterpret_cast<float*>(base + lay.sig);
   float* part = reinterpret_cast<float*>(base + lay.part);
 
   PrepArgs pa{};
   pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
-  pa.R = 0; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
+  pa.R = 0; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax; pa.sig = sig;
   // eight 16-bit activations per 16-byte load, or eight fp32 ones per two
   pa.vec = reinterpret_cast<uintptr_t>(x) % 16 != 0 ? 0
            : x_dtype == DBF_F32                    ? (ldx % 4 == 0 ? 2 : 0)
@@ -896,14 +949,14 @@ hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void*
     b.bits[i] = t.b1[i];
     b.colscale[i] = t.alpha[i];
   }
-  b.a = u; b.l1 = l1; b.bmax = bmax;
+  b.a = u; b.l1 = l1; b.bmax = bmax; b.sig = sig; b.sig_div = 1;
   b.y = y; b.y_dtype = y_dtype; b.ldy = ldy; b.accumulate = accumulate;
   b.part = part; b.ldp = round4(N);
   e = launch_stage<2>(b, lay.tl, 1, s);
   if (e != hipSuccess || lay.tl.nsplit == 1) return e;
   Reduce2Args r{};
   r.part = part; r.ldp = b.ldp; r.T = T; r.N = N; r.L = t.n; r.nsplit = lay.tl.nsplit;
-  r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax;
+  r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax; r.sig = sig; r.sig_div = 1;
   r.y = y; r.y_dtype = y_dtype; r.ldy = ldy; r.accumulate = accumulate;
   reduce2_kernel<<<dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), 256, 0, s>>>(r);
   return hipGetLastError();
@@ -921,10 +974,11 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   _Float16* v = reinterpret_cast<_Float16*>(base + lay.v);
   float* l1 = reinterpret_cast<float*>(base + lay.l1);
   float* bmax = reinterpret_cast<float*>(base + lay.bmax);
+  float* sig = reinterpret_cast<float*>(base + lay.sig);
 
   PrepArgs pa{};
   pa.x = x; pa.x_dtype = x_dtype; pa.ldx = ldx; pa.T = T; pa.M = M; pa.mpad = kpad(M);
-  pa.R = R; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax;
+  pa.R = R; pa.L = t.n; pa.u = u; pa.l1 = l1; pa.bmax = bmax; pa.sig = sig;
   pa.vec = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   for (int i = 0; i < t.n; ++i)
     if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) pa.vec = 0;
@@ -943,14 +997,14 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
     a.bits[i] = t.b2[i];
     a.colscale[i] = t.beta[i];
   }
-  a.a = u; a.l1 = l1; a.bmax = bmax; a.v = v; a.vp = kpad(R);
+  a.a = u; a.l1 = l1; a.bmax = bmax; a.sig = sig; a.sig_div = 0; a.v = v; a.vp = kpad(R);
   a.part = part; a.ldp = round4(R);
   e = launch_stage<1>(a, pl.t1, t.n, s);
   if (e != hipSuccess) return e;
   if (pl.t1.nsplit > 1) {
     Reduce1Args r{};
     r.part = part; r.ldp = a.ldp; r.T = T; r.R = R; r.vp = a.vp; r.L = t.n;
-    r.nsplit = pl.t1.nsplit; r.l1 = l1; r.bmax = bmax; r.v = v;
+    r.nsplit = pl.t1.nsplit; r.l1 = l1; r.bmax = bmax; r.sig = sig; r.v = v;
     for (int i = 0; i < t.n; ++i) r.beta[i] = t.beta[i];
     const int64_t n = t.n * T * (a.vp / 8);
     reduce1_kernel<<<dim3(static_cast<unsigned>(cdiv(n, 256))), 256, 0, s>>>(r);
@@ -972,7 +1026,7 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   if (e != hipSuccess || pl.t2.nsplit == 1) return e;
   Reduce2Args r{};
   r.part = part; r.ldp = b.ldp; r.T = T; r.N = N; r.L = t.n; r.nsplit = pl.t2.nsplit;
-  r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax;
+  r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax; r.sig = sig; r.sig_div = 0;
   r.y = y; r.y_dtype = y_dtype; r.ldy = ldy; r.accumulate = accumulate;
   reduce2_kernel<<<dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), 256, 0, s>>>(r);
   return hipGetLastError();

@@ -173,8 +173,10 @@ int dbf_workspace_check(void *ws, void *stream);
  *                    MFMA path above; the others force one (both are
  *                    correct for every T >= 1).
  * Accumulation is fp32; the decode path keeps every intermediate in fp32,
- * the MFMA path rounds gamma*x and the scaled rank-R intermediate to fp16
- * (with an exact power-of-two scale per token).
+ * the MFMA path rounds gamma*x and the rank-R intermediate to fp16 once
+ * each, both multiplied by exact powers of two per token that keep them
+ * inside the fp16 range (so any finite x with a finite result works at any
+ * magnitude).
  * T = 0 is valid and does nothing.  Results are bitwise reproducible run
  * to run (no floating-point atomics).
  */
@@ -187,7 +189,10 @@ int dbf_linear_forward(const dbf_term *terms, int n_terms, int64_t N,
 /*
  * Integer-activation variant: x is int8 [T x M] with gamma folded into it
  * upstream (terms[i].gamma must be NULL, since gamma sits on the summed
- * index and cannot be applied to integer sums).
+ * index and cannot be applied to integer sums).  The two sign-accumulate
+ * products of LoRDBA section 2 ("Kernel de Inferencia") need only additions
+ * and subtractions, so with integer activations they are exact integer sums
+ * (the int32 S1 and S2 below); the per-channel scales then enter in fp32.
  *   s1 (optional, int32 [n_terms x T x R]):  S1_i = B2_i x, exact.
  *   s2 (optional, int32 [n_terms x T x N]):  S2_i = B1_i S1_i, exact;
  *       needs every beta == NULL (beta = 1).
@@ -260,7 +265,8 @@ size_t dbf_bool_workspace_bytes(int64_t N, int64_t M, int n_kernels, int64_t T,
  *                    MFMA path otherwise;
  *                    the others force one.
  * The decode path keeps everything in fp32; the MFMA path rounds s_in . x
- * to fp16 once, with fp32 accumulation.  x, y 16-byte aligned.  T = 0 is
+ * to fp16 once (times an exact power of two per token that keeps it inside
+ * the fp16 range), with fp32 accumulation.  x, y 16-byte aligned.  T = 0 is
  * valid and does nothing.  Results are bitwise reproducible run to run.
  */
 int dbf_bool_forward(const dbf_bool_kernel *kernels, int n_kernels, int64_t N,
@@ -309,7 +315,9 @@ size_t dbf_backward_workspace_bytes(int64_t N, int64_t M, int64_t R, int n_terms
  *   path             DBF_PATH_AUTO: decode products while T <= 16, MFMA
  *                    products above; or forced.
  * The products keep fp32 intermediates; on the MFMA path each product rounds
- * its scaled input to fp16 once (fp32 sums).  Token sums run in fixed order,
+ * its scaled input to fp16 once, times an exact power of two per token that
+ * keeps it inside the fp16 range (fp32 sums), so small gradients keep their
+ * precision.  Token sums run in fixed order,
  * so results are bitwise reproducible.  T = 0 is valid and does nothing.
  */
 int dbf_linear_backward(const dbf_term *terms, const dbf_term_t *tterms, int n_terms,
