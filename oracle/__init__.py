@@ -95,6 +95,8 @@ class Oracle:
             ctypes.POINTER(_dp), ctypes.POINTER(_dp), ctypes.POINTER(_dp),
             _dp, _dp, _dp, _dp, _dp, _dp]
         lib.dbf_oracle_threads.restype = ctypes.c_int
+        lib.dbf_oracle_set_threads.restype = None
+        lib.dbf_oracle_set_threads.argtypes = [ctypes.c_int]
         self.lib = lib
         self.path = path
 
@@ -266,6 +268,11 @@ class Oracle:
 
     def threads(self) -> int:
         return int(self.lib.dbf_oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads of the parallel loops from now on (results do not depend
+        on it)."""
+        self.lib.dbf_oracle_set_threads(int(n))
 
 
 # -- successive SVID (numpy) ---------------------------------------------

@@ -54,6 +54,18 @@ int dbf_oracle_threads(void)
 #endif
 }
 
+/* Threads the parallel loops use from now on (n >= 1); the results do not
+ * depend on it (every output element is summed by one thread in order). */
+void dbf_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* One term, one token:  y_t += diag(a) B1 diag(be) B2 diag(g) x_t.
  * u, v are scratch of length M and R. */
 static void term_one_token(int64_t N, int64_t M, int64_t R,

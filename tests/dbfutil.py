@@ -76,6 +76,23 @@ def round_bf16(a):
     return O.widen_bf16(f32_to_bf16_bits(np.asarray(a, dtype=np.float32)))
 
 
+def assert_close_bf16(y, ref, what=""):
+    """A bf16 output against the oracle rounded the same way (RNE to bf16),
+    at the float tolerance: the rounding of the output itself is then not
+    charged to the kernel.  Where the kernel's fp32 result and the oracle lie
+    on either side of a rounding boundary the two differ by one bf16 step, so
+    additionally every element must be within one step (2^-7 relative, the
+    spacing at the bottom of a binade) of the exact oracle value, or within
+    1e-3 max|ref| for values near zero."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert_close(y, round_bf16(ref), what=what + " (bf16 output)")
+    lim = np.abs(ref) * 2.0 ** -7 + 1e-3 * np.abs(ref).max()
+    bad = np.abs(y - ref) > lim
+    assert not bad.any(), "%s: %d elements more than one bf16 step from the oracle" % (
+        what, int(bad.sum()))
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     t = t.detach()
     if t.dtype == torch.bfloat16:

@@ -9,7 +9,7 @@ import torch
 import bit_adapters_amd as D
 import oracle as O
 from bit_adapters_amd import synth as S
-from dbfutil import (DEV, assert_close, bf16_dev, device_terms, to_np, x64,
+from dbfutil import (DEV, assert_close, assert_close_bf16, bf16_dev, device_terms, to_np, x64,
                      x_dev)
 
 pytestmark = pytest.mark.gpu
@@ -76,7 +76,7 @@ def test_strided_x_and_bf16_output():
     y = D.lordba_adapter_forward(bf16_dev(layer["w0"]), terms, 96, 200, 32,
                                  xd[:, :200], y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    assert_close(to_np(y), ref, rel_l2=4e-3)
+    assert_close_bf16(to_np(y), ref)
 
 
 def test_unaligned_activation_rows():

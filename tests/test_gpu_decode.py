@@ -6,7 +6,7 @@ import torch
 import bit_adapters_amd as D
 import oracle as O
 from bit_adapters_amd import synth as S
-from dbfutil import (DEV, assert_close, bf16_dev, device_terms, round_bf16, to_np, x64,
+from dbfutil import (DEV, assert_close, assert_close_bf16, bf16_dev, device_terms, to_np, x64,
                      x_dev)
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +71,7 @@ def test_output_dtypes_accumulate_and_strides():
     # bf16 and fp16 outputs, compared with the oracle rounded the same way
     yb = D.dbf_linear_forward(terms, 96, 200, 40, xs, y_dtype=torch.bfloat16, path=PATH)
     torch.cuda.synchronize()
-    assert_close(to_np(yb), round_bf16(ref), rel_l2=4e-3)
+    assert_close_bf16(to_np(yb), ref)
     yh = D.dbf_linear_forward(terms, 96, 200, 40, xs, y_dtype=torch.float16, path=PATH)
     torch.cuda.synchronize()
     assert_close(to_np(yh), ref.astype(np.float16).astype(np.float64))
@@ -183,4 +183,30 @@ def test_partly_shared_carriers():
     terms = _shared_terms(layer, share_b2=False)
     y = D.dbf_linear_forward(terms, 200, 700, 64, x_dev(x), path=PATH)
     torch.cuda.synchronize()
+    assert_close(to_np(y), O.default().forward(O.terms64(layer), x64(x)))
+
+
+@pytest.mark.parametrize("slot,code", [(2, D.DBF_ESTALLED), (3, D.DBF_EINVAL)])
+def test_workspace_check_reports_and_clears(slot, code):
+    # A handoff wait that gave up (slot 2) or an adapter index out of range
+    # (slot 3) is a flag in the workspace head.  The flag is set here from
+    # the host, so no kernel has to stall: dbf_workspace_check must report
+    # it, clear the whole head, and leave the buffer usable.
+    layer, x = S.make_custom(130, 300, 70, 1, 2, seed=21)
+    nb = D.dbf_workspace_bytes(130, 300, 70, 1, 2, D.DBF_PATH_DECODE)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    head = ws[:D.DBF_WS_HEAD_BYTES].view(torch.int32)
+    head[slot] = 1
+    head[0] = 5   # a consumer ticket
+    head[64] = 7  # a producer counter
+    torch.cuda.synchronize()
+    with pytest.raises(D.DbfError) as e:
+        D.dbf_workspace_check(ws)
+    assert e.value.code == code
+    assert not ws[:D.DBF_WS_HEAD_BYTES].any()
+    D.dbf_workspace_check(ws)  # clean now
+    y = D.dbf_linear_forward(device_terms(layer), 130, 300, 70, x_dev(x), ws=ws,
+                             path=D.DBF_PATH_DECODE)
+    D.dbf_workspace_check(ws)
+    assert not ws[:D.DBF_WS_HEAD_BYTES].any()
     assert_close(to_np(y), O.default().forward(O.terms64(layer), x64(x)))
