@@ -30,10 +30,11 @@ DBF_PATH_AUTO, DBF_PATH_DECODE, DBF_PATH_MFMA = 0, 1, 2
 DBF_MAX_TERMS = 8
 DBF_WS_HEAD_BYTES = 16640
 DBF_MAX_ADAPTERS = 32
+DBF_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
            "dbf_packed_bytes", "dbf_pack", "dbf_unpack", "dbf_workspace_bytes",
-           "dbf_linear_forward", "dbf_linear_forward_i8",
+           "dbf_linear_forward", "dbf_linear_forward_noalloc", "dbf_linear_forward_i8",
            "lordba_adapter_forward", "dbf_workspace_check",
            "dbf_bool_workspace_bytes", "dbf_bool_forward", "dbf_transpose_packed",
            "dbf_backward_workspace_bytes", "dbf_linear_backward",
@@ -73,6 +74,10 @@ def library() -> ctypes.CDLL:
     lib.dbf_linear_forward.argtypes = [
         ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _int, _i64, _i64,
         _vp, _int, _i64, _int, _vp, _sz, _int, _vp]
+    lib.dbf_linear_forward_noalloc.restype = _int
+    lib.dbf_linear_forward_noalloc.argtypes = [
+        ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _int, _i64, _i64,
+        _vp, _int, _i64, _int, _int, _vp]
     lib.dbf_linear_forward_i8.restype = _int
     lib.dbf_linear_forward_i8.argtypes = [
         ctypes.POINTER(_CTerm), _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp,
@@ -350,6 +355,23 @@ def dbf_linear_forward(terms: Sequence[DbfTerm], N: int, M: int, R: int,
         _terms(terms), len(terms), N, M, R, _ptr(x), _DT.get(x.dtype, -1), T,
         _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), int(accumulate),
         _ptr(ws), wsb, path, _stream(stream)))
+    return y
+
+
+def dbf_linear_forward_noalloc(terms: Sequence[DbfTerm], N: int, M: int, R: int,
+                               x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                               y_dtype: torch.dtype = torch.float32,
+                               accumulate: bool = False, path: int = DBF_PATH_AUTO,
+                               stream=None) -> torch.Tensor:
+    """dbf_linear_forward with the library's own scratch as workspace (no
+    workspace argument; calls on one device must not overlap)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=y_dtype, device=x.device)
+    _check(library().dbf_linear_forward_noalloc(
+        _terms(terms), len(terms), N, M, R, _ptr(x), _DT.get(x.dtype, -1), T,
+        _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), int(accumulate), path,
+        _stream(stream)))
     return y
 
 

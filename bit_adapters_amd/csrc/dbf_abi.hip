@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dbf_internal.h"
 #include "dbf_lut.h"
@@ -140,6 +141,59 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
   return DBF_OK;
 }
 
+int linear_forward(const dbf_term* terms, int n_terms, int64_t N, int64_t M, int64_t R,
+                   const void* x, int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
+                   int64_t ldy, int accumulate, void* ws, size_t ws_bytes, bool noalloc, int path,
+                   void* stream);
+
+}  // namespace
+
+// ---- scratch of dbf_linear_forward_noalloc --------------------------------
+// The workspace of the allocation-free entry point: a fixed array in the
+// library's code object, so each device that loads the library holds its own
+// copy until the process ends.  Its first DBF_WS_HEAD_BYTES are the decode
+// path's handoff counters: zero at load, cleared once more at set-up, and
+// left zero by every call.
+static __device__ __align__(256) unsigned char scratch[DBF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device
+
+// The current device's address of `scratch`, looked up (hipGetSymbolAddress)
+// and its head cleared on the first call on that device.  In host code the
+// array's name is only a stand-in for the symbol; kernels get this address.
+int scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(DBF_EDEVICE, "no HIP device is current");
+  if (dev >= kMaxDevices) return fail(DBF_EDEVICE, "device %d is past the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DBF_ELAUNCH, "looking up the scratch array on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+    // a fill kernel rather than a memset node, so a first call under graph
+    // capture records nothing that replays differently
+    constexpr int64_t kHeadWords = DBF_WS_HEAD_BYTES / 4;
+    zero_words_kernel<<<dim3(static_cast<unsigned>((kHeadWords + 255) / 256)), 256, 0, s>>>(
+        static_cast<uint32_t*>(ptr), kHeadWords);
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess)
+      return fail(DBF_ELAUNCH, "clearing the scratch head failed: %s", hipGetErrorString(le));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return DBF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,6 +269,28 @@ int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
                        int64_t T, int64_t ldx, void* y, int y_dtype,
                        int64_t ldy, int accumulate, void* ws, size_t ws_bytes,
                        int path, void* stream) {
+  return linear_forward(terms, n_terms, N, M, R, x, x_dtype, T, ldx, y, y_dtype, ldy, accumulate,
+                        ws, ws_bytes, false, path, stream);
+}
+
+int dbf_linear_forward_noalloc(const dbf_term* terms, int n_terms, int64_t N, int64_t M,
+                               int64_t R, const void* x, int x_dtype, int64_t T, int64_t ldx,
+                               void* y, int y_dtype, int64_t ldy, int accumulate, int path,
+                               void* stream) {
+  return linear_forward(terms, n_terms, N, M, R, x, x_dtype, T, ldx, y, y_dtype, ldy, accumulate,
+                        nullptr, 0, true, path, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// dbf_linear_forward and dbf_linear_forward_noalloc: the same validation and
+// kernels; the second takes its workspace from the library's scratch array.
+int linear_forward(const dbf_term* terms, int n_terms, int64_t N, int64_t M, int64_t R,
+                   const void* x, int x_dtype, int64_t T, int64_t ldx, void* y, int y_dtype,
+                   int64_t ldy, int accumulate, void* ws, size_t ws_bytes, bool noalloc, int path,
+                   void* stream) {
   int e = check_terms(terms, n_terms, true, true);
   if (e != DBF_OK) return e;
   if (N < 1 || M < 1 || R < 1) return fail(DBF_EINVAL, "N, M, R must be >= 1");
@@ -231,18 +307,35 @@ int dbf_linear_forward(const dbf_term* terms, int n_terms, int64_t N,
   if (ldy < N) return fail(DBF_EINVAL, "ldy %lld < N %lld", (long long)ldy, (long long)N);
   if (!aligned16(x) || !aligned16(y)) return fail(DBF_EALIGN, "x or y not 16-byte aligned");
   const int p = resolve_dbf_path(path, N, M, R, T, n_terms);
-  e = check_ws(ws, ws_bytes, dbf_workspace_bytes(N, M, R, n_terms, T, p));
-  if (e != DBF_OK) return e;
-  e = check_device();
-  if (e != DBF_OK) return e;
-  const dbf::TermPtrs tp = to_ptrs(terms, n_terms);
+  const size_t need = dbf_workspace_bytes(N, M, R, n_terms, T, p);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (noalloc) {
+    if (need > DBF_NOALLOC_SCRATCH_BYTES)
+      return fail(DBF_EWORKSPACE,
+                  "this call needs %zu bytes of workspace, more than the %zu of the "
+                  "library's scratch; use dbf_linear_forward with a workspace",
+                  need, static_cast<size_t>(DBF_NOALLOC_SCRATCH_BYTES));
+    e = check_device();
+    if (e != DBF_OK) return e;
+    e = scratch_address(s, &ws);
+    if (e != DBF_OK) return e;
+  } else {
+    e = check_ws(ws, ws_bytes, need);
+    if (e != DBF_OK) return e;
+    e = check_device();
+    if (e != DBF_OK) return e;
+  }
+  const dbf::TermPtrs tp = to_ptrs(terms, n_terms);
   if (p == DBF_PATH_MFMA)
     return launched(dbf::launch_mfma(tp, N, M, R, x, x_dtype, T, ldx, y, y_dtype,
                                      ldy, accumulate, ws, s));
   return launched(dbf::launch_decode(tp, N, M, R, x, x_dtype, T, ldx, y, y_dtype,
                                      ldy, accumulate, ws, s));
 }
+
+}  // namespace
+
+extern "C" {
 
 int dbf_transpose_packed(const uint32_t* packed, int64_t rows, int64_t k, uint32_t* out,
                          void* stream) {

@@ -187,6 +187,27 @@ int dbf_linear_forward(const dbf_term *terms, int n_terms, int64_t N,
                        int path, void *stream);
 
 /*
+ * dbf_linear_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a fixed scratch array of
+ * DBF_NOALLOC_SCRATCH_BYTES inside the library, one per device (each device
+ * that loads the library holds it until the process ends).  The call
+ * allocates nothing.
+ *   Arguments, paths and results as dbf_linear_forward (the same kernels).
+ *   A call whose dbf_workspace_bytes(N, M, R, n_terms, T, path) exceeds
+ *   DBF_NOALLOC_SCRATCH_BYTES returns DBF_EWORKSPACE before any HIP call.
+ *   Every call on a device shares that device's array: calls that overlap on
+ *   one device (different streams or threads at the same time) race; order
+ *   them on one stream.
+ */
+#define DBF_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dbf_linear_forward_noalloc(const dbf_term *terms, int n_terms, int64_t N,
+                               int64_t M, int64_t R, const void *x, int x_dtype,
+                               int64_t T, int64_t ldx, void *y, int y_dtype,
+                               int64_t ldy, int accumulate, int path,
+                               void *stream);
+
+/*
  * Integer-activation variant: x is int8 [T x M] with gamma folded into it
  * upstream (terms[i].gamma must be NULL, since gamma sits on the summed
  * index and cannot be applied to integer sums).  The two sign-accumulate

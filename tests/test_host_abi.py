@@ -122,6 +122,37 @@ def test_forward_validation(kw, code):
     assert D.dbf_last_error()
 
 
+def fwd_noalloc(terms=None, n=1, N=8, M=8, R=8, x=FAKE, xdt=D.DBF_BF16, T=1, ldx=8,
+                y=FAKE, ydt=D.DBF_F32, ldy=8, acc=0, path=0):
+    if terms is None:
+        terms = _terms(n)
+    return L.dbf_linear_forward_noalloc(terms, n, N, M, R, x, xdt, T, ldx, y, ydt, ldy, acc,
+                                        path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), D.DBF_EINVAL), (dict(terms=_terms(1, b2=MIS)), D.DBF_EALIGN),
+    (dict(N=0), D.DBF_EINVAL), (dict(T=-1), D.DBF_EINVAL),
+    (dict(xdt=D.DBF_F32), D.DBF_EDTYPE), (dict(ydt=D.DBF_I8), D.DBF_EDTYPE),
+    (dict(acc=2), D.DBF_EINVAL), (dict(path=7), D.DBF_EINVAL),
+    (dict(ldx=7), D.DBF_EINVAL), (dict(x=None), D.DBF_EINVAL), (dict(y=MIS), D.DBF_EALIGN),
+    # the 8192 x 8192, R 6144 layer at 4096 tokens needs more workspace than
+    # the library's scratch: refused before any HIP call
+    (dict(N=8192, M=8192, R=6144, T=4096, ldx=8192, ldy=8192), D.DBF_EWORKSPACE),
+])
+def test_forward_noalloc_validation(kw, code):
+    assert fwd_noalloc(**kw) == code
+    assert D.dbf_last_error()
+
+
+def test_forward_noalloc_limit():
+    # the limit is the scratch size: sizes just above it are refused, and the
+    # workspace of the one-token 4096 x 4096 layer fits
+    assert L.dbf_workspace_bytes(8192, 8192, 6144, 1, 4096, 0) > D.DBF_NOALLOC_SCRATCH_BYTES
+    assert L.dbf_workspace_bytes(4096, 4096, 2048, 1, 1, 0) <= D.DBF_NOALLOC_SCRATCH_BYTES
+    assert fwd_noalloc(T=0, x=None, y=None) == D.DBF_OK
+
+
 def test_forward_zero_tokens_is_a_noop():
     assert fwd(T=0, x=None, y=None, ws=None) == D.DBF_OK
 
