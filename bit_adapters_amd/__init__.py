@@ -38,7 +38,7 @@ EXPORTS = ("dbf_abi_version", "dbf_layout_version", "dbf_last_error",
            "lordba_adapter_forward", "dbf_workspace_check",
            "dbf_bool_workspace_bytes", "dbf_bool_forward", "dbf_transpose_packed",
            "dbf_backward_workspace_bytes", "dbf_linear_backward",
-           "lordba_multi_adapter_forward")
+           "lordba_multi_adapter_forward", "dbf_svid_workspace_bytes", "dbf_svid_extract")
 
 
 class _CTerm(ctypes.Structure):
@@ -107,6 +107,11 @@ def library() -> ctypes.CDLL:
     lib.dbf_bool_forward.argtypes = [
         ctypes.POINTER(_CBool), _int, _i64, _i64, _vp, _int, _i64, _i64, _vp,
         _int, _i64, _int, _vp, _sz, _int, _vp]
+    lib.dbf_svid_workspace_bytes.restype = _sz
+    lib.dbf_svid_workspace_bytes.argtypes = [_i64, _i64]
+    lib.dbf_svid_extract.restype = _int
+    lib.dbf_svid_extract.argtypes = [
+        _vp, _int, _i64, _i64, _i64, _int, ctypes.POINTER(_CBoolOut), _int, _vp, _vp, _sz, _vp]
     _lib_handle = lib
     return lib
 
@@ -175,6 +180,10 @@ class _CBool(ctypes.Structure):
     _fields_ = [("w", _vp), ("s_in", _vp), ("s_out", _vp)]
 
 
+class _CBoolOut(ctypes.Structure):
+    _fields_ = [("w", _vp), ("s_in", _vp), ("s_out", _vp)]
+
+
 def _bool_kernels(kernels: Sequence[DbfBoolKernel]):
     arr = (_CBool * max(1, len(kernels)))()
     for i, k in enumerate(kernels):
@@ -232,6 +241,36 @@ def dbf_bool_forward(kernels: Sequence[DbfBoolKernel], N: int, M: int,
         T, _ld(x), _ptr(y), _DT.get(y.dtype, -1), _ld(y), int(accumulate),
         _ptr(ws), wsb, path, _stream(stream)))
     return y
+
+
+def dbf_svid_workspace_bytes(N: int, M: int) -> int:
+    return int(library().dbf_svid_workspace_bytes(N, M))
+
+
+def dbf_svid_extract(w: torch.Tensor, n_kernels: int, iters: int = 32,
+                     ws: Optional[torch.Tensor] = None, residual: bool = False,
+                     stream=None):
+    """Successive SVID of w [N x M] (f32, bf16 or f16, device) into n_kernels
+    boolean kernels.  Returns a list of DbfBoolKernel (packed signs, fp16
+    s_in, fp16 s_out), plus the float [n_kernels] squared residual norms if
+    residual is set."""
+    N, M = w.shape
+    dev = w.device
+    outs = [DbfBoolKernel(torch.empty(dbf_packed_bytes(N, M) // 4, dtype=torch.int32, device=dev),
+                          torch.empty(M, dtype=torch.float16, device=dev),
+                          torch.empty(N, dtype=torch.float16, device=dev))
+            for _ in range(n_kernels)]
+    arr = (_CBoolOut * n_kernels)()
+    for i, k in enumerate(outs):
+        arr[i] = _CBoolOut(_ptr(k.w), _ptr(k.s_in), _ptr(k.s_out))
+    res = torch.empty(n_kernels, dtype=torch.float32, device=dev) if residual else None
+    nb = dbf_svid_workspace_bytes(N, M)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check(library().dbf_svid_extract(_ptr(w), _DT.get(w.dtype, -1), N, M, _ld(w), n_kernels,
+                                       arr, iters, _ptr(res), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+    return (outs, res) if residual else outs
 
 
 def dbf_transpose_packed(packed: torch.Tensor, rows: int, k: int,

@@ -337,6 +337,48 @@ int linear_forward(const dbf_term* terms, int n_terms, int64_t N, int64_t M, int
 
 extern "C" {
 
+size_t dbf_svid_workspace_bytes(int64_t N, int64_t M) {
+  if (N <= 0 || M <= 0) return 0;
+  return dbf::svid_ws_bytes(N, M);
+}
+
+int dbf_svid_extract(const void* w, int w_dtype, int64_t N, int64_t M, int64_t ldw, int n_kernels,
+                     const dbf_bool_kernel_out* kernels, int iters, float* residual_sq, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (N < 1 || M < 1) return fail(DBF_EINVAL, "N, M must be >= 1");
+  if (w_dtype != DBF_F32 && w_dtype != DBF_BF16 && w_dtype != DBF_F16)
+    return fail(DBF_EDTYPE, "w dtype %d unsupported (f32, bf16 or f16)", w_dtype);
+  if (!w) return fail(DBF_EINVAL, "w is NULL");
+  if (ldw < M) return fail(DBF_EINVAL, "ldw %lld < M %lld", (long long)ldw, (long long)M);
+  if (reinterpret_cast<uintptr_t>(w) % (w_dtype == DBF_F32 ? 4u : 2u) != 0)
+    return fail(DBF_EALIGN, "w not aligned to its element");
+  if (!kernels) return fail(DBF_EINVAL, "kernels is NULL");
+  if (n_kernels < 1 || n_kernels > DBF_MAX_TERMS)
+    return fail(DBF_EINVAL, "n_kernels %d outside 1..%d", n_kernels, DBF_MAX_TERMS);
+  if (iters < 1 || iters > 1000) return fail(DBF_EINVAL, "iters %d outside 1..1000", iters);
+  uint32_t* wb[DBF_MAX_TERMS];
+  uint16_t* sin[DBF_MAX_TERMS];
+  uint16_t* sout[DBF_MAX_TERMS];
+  for (int k = 0; k < n_kernels; ++k) {
+    const dbf_bool_kernel_out& o = kernels[k];
+    if (!o.w || !o.s_in || !o.s_out) return fail(DBF_EINVAL, "kernel %d: an output is NULL", k);
+    if (!aligned16(o.w)) return fail(DBF_EALIGN, "kernel %d: packed signs not 16-byte aligned", k);
+    if (!aligned2(o.s_in) || !aligned2(o.s_out))
+      return fail(DBF_EALIGN, "kernel %d: a scale vector is not 2-byte aligned", k);
+    wb[k] = o.w;
+    sin[k] = static_cast<uint16_t*>(o.s_in);
+    sout[k] = static_cast<uint16_t*>(o.s_out);
+  }
+  if (residual_sq && (reinterpret_cast<uintptr_t>(residual_sq) & 3u))
+    return fail(DBF_EALIGN, "residual_sq not 4-byte aligned");
+  int e = check_ws(ws, ws_bytes, dbf_svid_workspace_bytes(N, M));
+  if (e != DBF_OK) return e;
+  e = check_device();
+  if (e != DBF_OK) return e;
+  return launched(dbf::launch_svid(w, w_dtype, N, M, ldw, n_kernels, wb, sin, sout, iters,
+                                   residual_sq, ws, static_cast<hipStream_t>(stream)));
+}
+
 int dbf_transpose_packed(const uint32_t* packed, int64_t rows, int64_t k, uint32_t* out,
                          void* stream) {
   if (rows < 0 || k < 0) return fail(DBF_EINVAL, "negative size");

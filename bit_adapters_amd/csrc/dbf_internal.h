@@ -137,6 +137,15 @@ hipError_t launch_backward(const TermPtrs& t, const uint32_t* const* b1t,
                            int64_t lddx, float* dalpha, float* dbeta, float* dgamma,
                            int path, void* ws, hipStream_t s);
 
+// Successive SVID extraction (dbf_svid.hip): n_kernels boolean kernels of
+// the real N x M matrix w (dtype w_dtype, row stride ldw) into the packed
+// signs wb[k], fp16 s_in[k] [M] and s_out[k] [N]; residual_sq[k] (optional)
+// = ||W - sum_{j <= k} kernel_j||_F^2; ws of svid_ws_bytes(N, M) bytes.
+size_t svid_ws_bytes(int64_t N, int64_t M);
+hipError_t launch_svid(const void* w, int w_dtype, int64_t N, int64_t M, int64_t ldw, int n_kernels,
+                       uint32_t* const* wb, uint16_t* const* s_in, uint16_t* const* s_out, int iters,
+                       float* residual_sq, void* ws, hipStream_t s);
+
 // Several adapters, one per token (idx[t] in [-1, n_adapters), -1 = base
 // only), in one launch: one-token stage-1 workgroups each run their
 // token's adapter, the row workgroups stream the base once for every token

@@ -256,9 +256,8 @@ int lordba_adapter_forward(const void *w0, int64_t ldw, const dbf_term *terms,
  *   y = sum_{k=1..K} s_out_k . (Wb_k (s_in_k . x)),   Wb_k in {+-1}^{N x M},
  *
  * one sign-accumulate product per kernel over a full N x M sign matrix (the
- * double-binary layer's stage S3 at R = M).  Extraction of the kernels from
- * a real weight (successive SVID, item 3) is offline model conversion and
- * not part of this library.
+ * double-binary layer's stage S3 at R = M).  dbf_svid_extract (below)
+ * extracts such kernels from a real weight.
  */
 typedef struct {
     const uint32_t *w;  /* Wb_k, dbf_pack(rows = N, k = M) layout; 16-byte aligned */
@@ -294,6 +293,44 @@ int dbf_bool_forward(const dbf_bool_kernel *kernels, int n_kernels, int64_t N,
                      int64_t M, const void *x, int x_dtype, int64_t T,
                      int64_t ldx, void *y, int y_dtype, int64_t ldy,
                      int accumulate, void *ws, size_t ws_bytes, int path,
+                     void *stream);
+
+/*
+ * Successive SVID extraction of boolean kernels from a real weight, the
+ * conversion the same section describes: item 1 takes a kernel as the signs
+ * of the matrix with a rank-one scale, W ~ sign(W) . (s_out s_in^T); item 3
+ * extracts each later kernel the same way from the residual the earlier
+ * ones leave.  The page leaves the rank-one fit open; here it is the
+ * leading singular pair (sigma, u, v) of |r| (r the current residual),
+ * which |r| >= 0 makes nonnegative, split evenly: s_out = fp16(sqrt(sigma)
+ * u), s_in = fp16(sqrt(sigma) v), found by `iters` power iterations from
+ * the all-ones direction in fp32; the residual is then r - sign(r) .
+ * (s_out s_in^T) with the rounded scales.  sign(0) = +1 (the pack rule).
+ *   w               N x M, w_dtype DBF_F32, DBF_BF16 or DBF_F16, row stride
+ *                   ldw >= M (element-aligned).
+ *   kernels         host array of n_kernels (1..DBF_MAX_TERMS) outputs:
+ *                   w the packed signs (dbf_packed_bytes(N, M) bytes,
+ *                   16-byte aligned), s_in fp16 [M], s_out fp16 [N]
+ *                   (2-byte aligned); all written.  They feed
+ *                   dbf_bool_forward as they are.
+ *   iters           power iterations per kernel, 1..1000.
+ *   residual_sq     optional device float [n_kernels]: ||W - sum_{j <= k}
+ *                   kernel_j||_F^2 after kernel k.
+ *   ws, ws_bytes    dbf_svid_workspace_bytes(N, M) bytes, 16-byte aligned
+ *                   (scratch; holds the fp32 residual).
+ * Every sum runs in a fixed order, so results are bitwise reproducible.
+ */
+typedef struct {
+    uint32_t *w;  /* packed signs, written */
+    void *s_in;   /* fp16 [M], written */
+    void *s_out;  /* fp16 [N], written */
+} dbf_bool_kernel_out;
+
+size_t dbf_svid_workspace_bytes(int64_t N, int64_t M);
+int dbf_svid_extract(const void *w, int w_dtype, int64_t N, int64_t M,
+                     int64_t ldw, int n_kernels,
+                     const dbf_bool_kernel_out *kernels, int iters,
+                     float *residual_sq, void *ws, size_t ws_bytes,
                      void *stream);
 
 /*

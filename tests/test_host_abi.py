@@ -400,3 +400,40 @@ def test_pack_validation():
 def test_valid_call_without_device_reports_edevice():
     assert fwd() == D.DBF_EDEVICE
     assert "device" in D.dbf_last_error()
+
+
+def svid(w=FAKE, dt=D.DBF_F32, N=8, M=8, ldw=8, n=1, outs=None, iters=8, res=None, ws=FAKE,
+         wsb=1 << 30):
+    if outs is None:
+        outs = (D._CBoolOut * max(n, 1))()
+        for i in range(n):
+            outs[i] = D._CBoolOut(FAKE, FAKE, FAKE)
+    return L.dbf_svid_extract(w, dt, N, M, ldw, n, outs, iters, res, ws, wsb, None)
+
+
+def _souts(**over):
+    a = (D._CBoolOut * 1)()
+    f = dict(w=FAKE, s_in=FAKE, s_out=FAKE)
+    f.update(over)
+    a[0] = D._CBoolOut(**f)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), D.DBF_EINVAL), (dict(dt=D.DBF_I8), D.DBF_EDTYPE), (dict(w=None), D.DBF_EINVAL),
+    (dict(ldw=7), D.DBF_EINVAL), (dict(w=FAKE + 2), D.DBF_EALIGN),
+    (dict(n=0), D.DBF_EINVAL), (dict(n=9), D.DBF_EINVAL),
+    (dict(iters=0), D.DBF_EINVAL), (dict(iters=1001), D.DBF_EINVAL),
+    (dict(outs=_souts(w=None)), D.DBF_EINVAL), (dict(outs=_souts(w=MIS)), D.DBF_EALIGN),
+    (dict(outs=_souts(s_in=FAKE + 1)), D.DBF_EALIGN), (dict(res=FAKE + 2), D.DBF_EALIGN),
+    (dict(ws=None), D.DBF_EWORKSPACE), (dict(wsb=16), D.DBF_EWORKSPACE),
+])
+def test_svid_validation(kw, code):
+    assert svid(**kw) == code
+    assert D.dbf_last_error()
+
+
+def test_svid_workspace_bytes():
+    # the fp32 residual dominates: at least N * M * 4 bytes
+    assert L.dbf_svid_workspace_bytes(0, 8) == 0
+    assert L.dbf_svid_workspace_bytes(300, 1000) >= 300 * 1000 * 4
