@@ -180,8 +180,239 @@ __device__ __forceinline__ void stage2_role(const Stage2& p, int64_t bid2, A* tb
   consumer_done(p.sync, ticket);
 }
 
+// ---- float consumers, wave by wave ----------------------------------------
+// Wave wv of a stage-2 workgroup owns the K-blocks kb = wv, wv + NW, ... of
+// B1 (ranks 32 KW kb ..).  Instead of the whole workgroup waiting for every
+// producer, each wave waits only for the producers of its own ranks (their
+// counter slots), then fetches its partials, builds its own tables and makes
+// its lookups while other waves are still waiting.  Each wave accumulates
+// only its own K-blocks, alpha of its row applied per term, and the waves
+// are added in wave order at the end (reduce_waves), so the result does not
+// depend on which wave finished first.
+//
+// Producer pid = ((tblk L + term) nrt2 + rt2) ks + split adds to counter
+// slot pid % kSyncSlots; a wave waits until each slot of its producers
+// holds that slot's full count (a superset of what it needs when several
+// producers share a slot).  The reset rule of consumer_done needs every
+// wait of the launch to be over before the last ticket: here the last wave
+// of a workgroup to pass its final wait (counted in LDS) takes the
+// workgroup's ticket.
+
+// Wait until every producer of (tblk, term) whose rows fall in ranks
+// [r0, r1) has published.  All lanes of the wave call it; bounded like
+// wait_producers.
+__device__ __forceinline__ void wait_ranks(const Sync& s, int tblk, int term, int L, int nrt2,
+                                           int ks, int r0, int r1) {
+  const int lane = threadIdx.x & 63;
+  const int rt_lo = r0 / 64, rt_hi = min(nrt2, (r1 + 63) / 64);
+  const int npid = (rt_hi - rt_lo) * ks;
+  const unsigned ns = static_cast<unsigned>(kSyncSlots);
+  const unsigned base = static_cast<unsigned>((tblk * L + term) * nrt2 + rt_lo) * ks;
+  unsigned spins = 0;
+  for (int j0 = 0; j0 < npid; j0 += 64) {
+    const int j = j0 + lane;
+    unsigned slot = 0, want = 0;
+    if (j < npid) {
+      // pids of consecutive (row tile, split) are consecutive
+      slot = (base + static_cast<unsigned>(j)) % ns;
+      want = s.n_prod / ns + (slot < s.n_prod % ns ? 1u : 0u);
+    }
+    unsigned have = 0;
+    while (true) {
+      if (have < want)
+        have = __hip_atomic_load(s.slots + slot * kSyncStride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_SYSTEM);
+      if (__all(have >= want)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        if (lane == 0)
+          __hip_atomic_fetch_or(s.ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        break;
+      }
+    }
+  }
+}
+
+// LDS operations of one wave are done in order; this keeps the compiler
+// from moving them across the point and waits for this wave's own.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Splits of the first product the wave-by-wave consumers take (their
+// partial loads are issued one item ahead, so they are held in registers).
+constexpr int kWavesMaxKS = 2;
+
+template <int TB, int KW, int NW>
+__device__ __forceinline__ void stage2_role_waves(const Stage2& p, int64_t bid2, float* tbl,
+                                                  float* red, unsigned* wg_ctr) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t tblk = bid2 / p.nrt;
+  const int64_t rt = bid2 - tblk * p.nrt;
+  const int64_t row = rt * 64 + lane;
+  const int64_t nrt2 = layout_nrt(p.R);
+  constexpr int G = 8 * KW;                       // groups of four ranks in a K-block
+  constexpr int NE = (TB * G + 63) / 64;           // tables a lane builds
+  float* wtbl = tbl + wv * (TB * G * 16);          // this wave's tables [TB][G][16]
+  // this wave's items: (term, K-block wv + i NW) for every term, i < nmine
+  const int nmine = wv < p.nkb ? static_cast<int>((p.nkb - 1 - wv) / NW) + 1 : 0;
+  const int nitems = p.t.n * nmine;
+  const int64_t tok0 = tblk * TB;
+  // alpha of this lane's row for every term, two to a register (read before
+  // the wait, by every lane with the row clamped)
+  const int64_t arow = row < p.N ? row : p.N - 1;
+  uint32_t aln[DBF_MAX_TERMS / 2];
+#pragma unroll
+  for (int q = 0; q < DBF_MAX_TERMS; q += 2) {
+    const uint32_t lo = q < p.t.n ? p.t.alpha[q][arow] : 0x3C00u;
+    const uint32_t hi = q + 1 < p.t.n ? p.t.alpha[q + 1][arow] : 0x3C00u;
+    aln[q / 2] = lo | (hi << 16);
+  }
+  if (threadIdx.x == 0) wg_ctr[0] = 0u;
+  // the sign words of this lane's row for item it
+  auto words = [&](int it, uint32_t (&wd)[KW]) {
+#pragma unroll
+    for (int w = 0; w < KW; ++w) wd[w] = 0u;
+    if (it < nitems) {
+      const int term = it / nmine, i = it - term * nmine;
+      load_row_words<KW>(p.t.b1[term] + ((rt * p.nkb + wv + static_cast<int64_t>(i) * NW) * 64 + lane) * KW, wd);
+    }
+  };
+  uint32_t wd[KW];
+  words(0, wd);
+  __syncthreads();  // wg_ctr cleared
+  // wait for every producer of this wave's ranks, all terms
+  if (nmine > 0) {
+    const int r0 = wv * 32 * KW;
+    const int r1 = static_cast<int>(min(p.R, static_cast<int64_t>(wv + (nmine - 1) * NW + 1) * 32 * KW));
+    for (int term = 0; term < p.t.n; ++term)
+      wait_ranks(p.sync, static_cast<int>(tblk), term, p.t.n, static_cast<int>(nrt2), p.ks, r0, r1);
+  }
+  // the partials of item it, as raw system-scope loads (at most kWavesMaxKS
+  // splits), addresses clamped past R and T
+  struct Raw {
+    float4 q[NE][kWavesMaxKS];
+  };
+  auto issue = [&](int it, Raw& r) {
+    const int term = it < nitems ? it / nmine : 0, i = it < nitems ? it - term * nmine : 0;
+    const int64_t kbase = (wv + static_cast<int64_t>(i) * NW) * 32 * KW;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int ent = lane + 64 * e;
+      const int tok = ent / G, g = ent - tok * G;
+      const int64_t tt = tok0 + tok, k = kbase + 4 * g;
+      const bool in = it < nitems && ent < TB * G && tt < p.T && k < p.R;
+      const int64_t base = (static_cast<int64_t>(term) * p.ks * p.T + (in ? tt : 0)) * p.rs + (in ? k : 0);
+#pragma unroll
+      for (int sp = 0; sp < kWavesMaxKS; ++sp)
+        r.q[e][sp] = sp < p.ks ? load_shared4<float4>(static_cast<const float*>(p.ws) + base + sp * p.T * p.rs)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  Raw raw;
+  issue(0, raw);
+  if (lane == 0) {
+    // this wave's waits are over; the workgroup's last such wave takes the
+    // ticket, after its first partials' loads (a wave's loads return in
+    // order, so those need not wait for the ticket's round trip)
+    const unsigned done = __hip_atomic_fetch_add(wg_ctr, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (done == NW - 1) wg_ctr[1] = take_ticket_any(p.sync);
+  }
+  float yacc[TB], acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) yacc[t] = acc[t] = 0.f;
+  for (int it = 0; it < nitems; ++it) {
+    const int term = it / nmine, i = it - term * nmine;
+    const int64_t kbase = (wv + static_cast<int64_t>(i) * NW) * 32 * KW;
+    // this item's w (splits summed in order; zeros past R or T)
+    float v[NE][4];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float4 sm = raw.q[e][0];
+#pragma unroll
+      for (int sp = 1; sp < kWavesMaxKS; ++sp)
+        if (sp < p.ks) {
+          sm.x += raw.q[e][sp].x; sm.y += raw.q[e][sp].y; sm.z += raw.q[e][sp].z; sm.w += raw.q[e][sp].w;
+        }
+      const int ent = lane + 64 * e;
+      const int tok = ent / G, g = ent - tok * G;
+      const int64_t k = kbase + 4 * g;
+      const bool in = tok0 + tok < p.T;
+      v[e][0] = in && k < p.R ? sm.x : 0.f;
+      v[e][1] = in && k + 1 < p.R ? sm.y : 0.f;
+      v[e][2] = in && k + 2 < p.R ? sm.z : 0.f;
+      v[e][3] = in && k + 3 < p.R ? sm.w : 0.f;
+    }
+    // the next item's partials and sign words, before this item's lookups
+    // (none past the last item: loads still in flight would hold the wave)
+    uint32_t wdn[KW];
+#pragma unroll
+    for (int w = 0; w < KW; ++w) wdn[w] = 0u;
+    if (it + 1 < nitems) {
+      issue(it + 1, raw);
+      words(it + 1, wdn);
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int ent = lane + 64 * e;
+      if (ent < TB * G) {
+        const int tok = ent / G, g = ent - tok * G;
+        build_signed16<float>(v[e][0], v[e][1], v[e][2], v[e][3], wtbl + (tok * G + g) * 16);
+      }
+    }
+    wave_lds_sync();
+    float acc2[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc2[t] = 0.f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+#pragma unroll
+      for (int c = 0; c < 8; c += 2) {
+        const int n0 = (wd[w] >> (4 * c)) & 15, n1 = (wd[w] >> (4 * c + 4)) & 15;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          acc[t] += wtbl[(t * G + w * 8 + c) * 16 + n0];
+          acc2[t] += wtbl[(t * G + w * 8 + c + 1) * 16 + n1];
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] += acc2[t];
+    wave_lds_sync();  // lookups done before the tables are rebuilt
+#pragma unroll
+    for (int w = 0; w < KW; ++w) wd[w] = wdn[w];
+    if (i == nmine - 1) {
+      // the term's last K-block of this wave: alpha of the row, then on
+      uint32_t a2 = aln[0];
+#pragma unroll
+      for (int q = 1; q < DBF_MAX_TERMS / 2; ++q)
+        if (q == term / 2) a2 = aln[q];
+      const float al = f16_bits_to_f32(static_cast<uint16_t>(term & 1 ? a2 >> 16 : a2));
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        yacc[t] += al * acc[t];
+        acc[t] = 0.f;
+      }
+    }
+  }
+  reduce_waves<float, TB, NW>(red, yacc);
+  if (wv == 0 && row < p.N && p.y) {
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int64_t tt = tok0 + t;
+      if (tt < p.T) store_out(p.y, p.y_dtype, tt * p.ldy + row, yacc[t], p.accumulate);
+    }
+  }
+  consumer_done(p.sync, wg_ctr[1]);
+}
+
 // NW waves per workgroup (16 or 8; the launcher picks, see pick_waves).
-template <typename A, int TB, int KW1, int KW2, int MODE, int NW>
+// CW: float consumers wave by wave (stage2_role_waves).
+template <typename A, int TB, int KW1, int KW2, int MODE, int NW, bool CW = false>
 __global__ void __launch_bounds__(64 * NW) decode_kernel(Stage1 s1, Stage2 s2, int n1,
                                                          int run_stage2) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -194,7 +425,15 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(Stage1 s1, Stage2 s2, i
     if (run_stage2) publish(s2.sync, static_cast<unsigned>(bid));
     return;
   }
-  stage2_role<A, TB, KW2, MODE, NW>(s2, bid - n1, tbl, red);
+  if constexpr (CW) {
+    static_assert(MODE == MODE_F && TB <= 2, "wave-by-wave consumers: float, up to two tokens");
+    // two words after the tables and wave partials: the workgroup's count of
+    // waves past their last wait, and its ticket
+    unsigned* wg_ctr = reinterpret_cast<unsigned*>(red + red_elems<TB, NW>());
+    stage2_role_waves<TB, KW2, NW>(s2, bid - n1, tbl, red, wg_ctr);
+  } else {
+    stage2_role<A, TB, KW2, MODE, NW>(s2, bid - n1, tbl, red);
+  }
 }
 
 // Stage 1 aims at about this many waves (512 workgroups of 8, 256 of 16).
@@ -292,6 +531,19 @@ template <typename A, int MODE, int NW>
 hipError_t run(const Stage1& s1, const Stage2& s2, int n1, int n2, int run_stage2,
                int tb, int kw1, int kw2, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(n1 + (run_stage2 ? n2 : 0));
+  // Float consumers wave by wave for one or two tokens of layers with whole
+  // 128-feature K-blocks (stage2_role_waves).
+  if constexpr (MODE == MODE_F) {
+    if (run_stage2 && tb <= 2 && kw1 == 4 && kw2 == 4 && s2.ks <= kWavesMaxKS &&
+        s2.t.n == 1 && s2.nkb <= NW) {
+      const size_t lds = (tb == 1 ? lds_bytes<A, 1, 4, NW>() : lds_bytes<A, 2, 4, NW>()) + 16;
+      if (tb == 1)
+        decode_kernel<A, 1, 4, 4, MODE, NW, true><<<dim3(grid), 64 * NW, lds, s>>>(s1, s2, n1, run_stage2);
+      else
+        decode_kernel<A, 2, 4, 4, MODE, NW, true><<<dim3(grid), 64 * NW, lds, s>>>(s1, s2, n1, run_stage2);
+      return hipGetLastError();
+    }
+  }
 #define DBF_LAUNCH(TB_, K1_, K2_)                                                        \
   decode_kernel<A, TB_, K1_, K2_, MODE, NW>                                              \
       <<<dim3(grid), 64 * NW, lds_bytes<A, TB_, (K1_ > K2_ ? K1_ : K2_), NW>(), s>>>(     \

@@ -430,6 +430,11 @@ __device__ __forceinline__ unsigned take_ticket(const Sync& s) {
   return ticket;
 }
 
+// The same ticket, taken by the calling lane (one lane of any wave).
+__device__ __forceinline__ unsigned take_ticket_any(const Sync& s) {
+  return __hip_atomic_fetch_add(s.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Consumer, at its end, with its ticket: the last consumer to take one
 // (every producer has published and every consumer has passed its wait by
 // then) clears the counters for the next call.
