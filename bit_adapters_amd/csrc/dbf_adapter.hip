@@ -16,7 +16,9 @@
 // bf16 values, the signs flipped by the packed B2 bits, so every product is
 // exact and the sums are fp32.  That adds at most 8 MFMAs per 32 features to
 // the base's one, needs no other workgroup, no workspace and no wait, and the
-// wavefronts load one group of features ahead of their MFMAs.
+// wavefronts load one group of features ahead of their MFMAs.  One token
+// (decode) has a kernel of its own, adapter_tok1: stream waves copy W0 into
+// LDS by DMA while rank waves derive w beside them (see there).
 //
 // Larger adapters: workgroups [0, n1) run the decode path's stage 1
 // (dbf_lut.h) for B2 and publish w; the row workgroups stream the base, then
@@ -28,6 +30,7 @@ namespace dbf {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnroll = 8;  // W0 loads in flight per lane
@@ -307,6 +310,7 @@ constexpr int kSmallTiles = 4;  // 16-rank MFMA tiles, summed over the terms
 constexpr int kSmallTerms = 2;  // more terms run out of registers
 constexpr int kSteps = 4;       // 32-feature MFMA steps per group
 constexpr int kGroup = kSteps * 32;  // one K-block of packed bits (kw = 4)
+constexpr size_t kMaxLds = 160 * 1024;  // LDS of one workgroup
 
 struct Small {
   const uint16_t* w0;
@@ -578,6 +582,303 @@ __global__ void __launch_bounds__(kMainThreads) adapter_small(Small p) {
   }
 }
 
+// ---- small ranks, one token: stream waves and rank waves -----------------
+
+// One-token decode is a stream of W0 (here 99.8% of the bytes) with a small
+// matrix-core job beside it.  The two run in separate waves of the row
+// workgroup so neither holds the other up:
+// - 8 stream waves copy their share of the 16 W0 rows and of x global -> LDS
+//   by DMA into a ring of S 128-feature groups each (no registers held by
+//   loads in flight; a wave refills a slot as soon as it has read it) and
+//   feed them to the base MFMA;
+// - 4 rank waves copy x, gamma and the B2 words of a quarter of the
+//   features into LDS first thing (a few tens of KiB, the same for every
+//   workgroup, so L2 hits), split gamma exactly, and derive their quarter of
+//   the unscaled w with adapter_small's arithmetic (exact split of gamma,
+//   sign-mask table, fp32 MFMA sums) while the stream runs.
+// The CU's memory pipeline serves its requests in order, so anything a wave
+// loads while the stream is in flight waits behind several microseconds of
+// W0; the rank inputs are therefore issued before the ring fills up, and
+// nothing else is loaded until the stream ends.
+constexpr int kRankWaves = 8;
+constexpr int kTok1Threads = 64 * (kMainWaves + kRankWaves);
+
+// Stream ring slot: the W0 fragments of a group [16 rows][16 chunks of
+// 16 B] (16-byte position q of row r holds chunk q ^ r, so that the
+// fragment reads of 16 rows hit 16 different bank groups) and x of the
+// group (128 features).
+constexpr int kTok1Slot = kSteps * 1024 + 256;
+constexpr int kTok1Copies = kSteps + 1;  // DMA instructions per group
+
+// The rank inputs are copied in chunks of 4 groups (1 KiB of x, of gamma,
+// and of the B2 words of each rank tile); chunk c goes to rank wave c % 8.
+constexpr int kChunkGroups = 4;
+__host__ __device__ inline int64_t tok1_padded_groups(int64_t M) {
+  return (M / kGroup + kChunkGroups - 1) / kChunkGroups * kChunkGroups;
+}
+
+// LDS of adapter_tok1: sign-mask table [256][16 B] | stream ring [8][S]
+// [slot] | base partials [8][16] | rank inputs, over Gp = the groups
+// rounded up to whole chunks: x [Gp * 128] (bf16, then the rank wave's
+// scaled fp16), gamma [L][Gp * 128], B2 words [NQ][Gp][64] | rank partials
+// [8][NQ * 16] | w [NQ * 16].
+template <int L, int QR>
+size_t tok1_lds_bytes(int S, int64_t M) {
+  constexpr int NQ = L * QR;
+  const int64_t Gp = tok1_padded_groups(M);
+  return 4096 + size_t(kMainWaves) * S * kTok1Slot + size_t(kMainWaves) * 16 * 4 +
+         size_t(Gp) * 256 + size_t(L) * Gp * 256 + size_t(NQ) * Gp * 256 +
+         size_t(kRankWaves) * NQ * 16 * 4 + size_t(NQ) * 16 * 4;
+}
+// DMA instructions of one rank wave (at most 63 may be outstanding).
+inline int64_t tok1_rank_copies(int L, int QR, int64_t M) {
+  const int64_t nc = tok1_padded_groups(M) / kChunkGroups;
+  return (nc + kRankWaves - 1) / kRankWaves * (1 + L + L * QR);
+}
+
+// Wait until every copy issued before the last `after` groups' copies (C
+// per group) has landed: copies complete in issue order.
+template <int C>
+__device__ __forceinline__ void wait_groups(int after) {
+  static_assert(2 * C < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C));
+  else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// T = 1, M a multiple of kGroup, 16-byte W0 / x / B2 and 4-byte gamma
+// addresses, 1 or 2 terms and at most 4 rank tiles; LDS as tok1_lds_bytes.
+template <int L, int QR, int S>
+__global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
+  constexpr int NQ = L * QR;
+  constexpr int C = kTok1Copies;
+  static_assert(L >= 1 && S >= 1 && S <= 3, "terms, ring depth");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t M = p.M, G = M / kGroup, Gp = tok1_padded_groups(M);
+  const int64_t MP = Gp * kGroup;  // features of the padded rank inputs
+  uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
+  unsigned char* ring = smem + 4096;
+  float* red = reinterpret_cast<float*>(ring + size_t(kMainWaves) * S * kTok1Slot);  // [8][16]
+  unsigned char* rx = reinterpret_cast<unsigned char*>(red + kMainWaves * 16);       // x
+  unsigned char* rg = rx + 2 * MP;                                                   // gamma
+  uint32_t* rb = reinterpret_cast<uint32_t*>(rg + size_t(L) * 2 * MP);               // B2 words
+  float* pr = reinterpret_cast<float*>(rb + size_t(NQ) * Gp * 64);                   // [8][NQ*16]
+  float* wfin = pr + kRankWaves * NQ * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 15, lq = lane >> 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t kwR = layout_kw(p.R);
+
+  // the epilogue's operands, loaded by every wave before its copies (so
+  // the waits for those cover them), unconditionally from in-bounds
+  // addresses and masked where used: a load under a branch is waited for
+  // at the branch's end
+  const int oi = tid >> 4, oj = tid & 15;  // owners: row oi, rank lane oj
+  const bool owner = tid < 256;
+  const int64_t on = n0 + oi;
+  const int64_t onc = min(on, p.N - 1);
+  uint32_t b1w[L][2];
+  uint16_t al[L];
+#pragma unroll
+  for (int term = 0; term < L; ++term) {
+    const uint32_t* b1 = p.t.b1[term] + ((onc >> 6) * 64 + (onc & 63)) * kwR;
+    b1w[term][0] = b1[0];
+    b1w[term][1] = b1[kwR - 1];  // used only for ranks >= 32, where kw = 2
+    al[term] = p.t.alpha[term][onc];
+  }
+  const int bq = min(tid >> 4, NQ - 1);
+  const int64_t br = 16 * (bq % QR) + (tid & 15);
+  const uint16_t bt = p.t.beta[bq / QR][min(br, p.R - 1)];
+
+  // the rank waves' inputs go first, ahead of the W0 stream in the CU's
+  // memory pipeline (the stream waves issue nothing before the barrier)
+  const int64_t nchunk = Gp / kChunkGroups;
+  if (wv >= kMainWaves) {
+    const unsigned rx0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(rx));
+    const unsigned rg0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(rg));
+    const unsigned rb0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(rb));
+    // lane l copies 16 bytes of group 4c + l / 16 (past the last group it
+    // reads the last group again, into the padding)
+    for (int64_t c = wv - kMainWaves; c < nchunk; c += kRankWaves) {
+      const int64_t gl = min(kChunkGroups * c + lane / 16, G - 1);
+      const int64_t k = gl * kGroup + 8 * (lane & 15);
+      const unsigned off = static_cast<unsigned>(c * kChunkGroups * 256);
+      copy16_to_lds(p.x + k, rx0 + off);
+#pragma unroll
+      for (int term = 0; term < L; ++term)
+        copy16_to_lds(p.t.gamma[term] + k, rg0 + static_cast<unsigned>(2 * MP * term) + off);
+      // the 256 bytes of B2 words of ranks 16 (q % QR) .. + 15, per group
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        copy16_to_lds(p.t.b2[q / QR] + (gl * 64 + 16 * (q % QR)) * 4 + 4 * (lane & 15),
+                      rb0 + static_cast<unsigned>(256 * q * Gp) + off);
+    }
+  }
+  // the sign-mask table of adapter_small
+  for (int e = tid; e < 1024; e += kTok1Threads) {
+    const uint32_t nb = ~static_cast<uint32_t>(e >> 2);
+    const int d = e & 3;
+    lut[e] = (((nb >> (2 * d)) & 1u) << 15) | (((nb >> (2 * d + 1)) & 1u) << 31);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  if (wv >= kMainWaves) {
+    const int r = wv - kMainWaves;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // x of the wave's chunks in fp16, scaled by sigma = a power of two that
+    // puts their largest |x| in [2^14, 2^15): exact wherever the scaled
+    // value is at least 2^-17 (x has 8 significant bits), so below 2^-31 of
+    // the largest only; every product with gamma (fp16) is then exact in the
+    // fp32 accumulator, and 1 / sigma is applied to the wave's partial
+    float amax = 0.f;
+    for (int64_t c = r; c < nchunk; c += kRankWaves) {
+      const uint4 v = reinterpret_cast<const uint4*>(rx + c * kChunkGroups * 256)[lane];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w4[h] << 16)),
+                                 fabsf(__uint_as_float(w4[h] & 0xFFFF0000u))));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sig = act_scale(amax);
+    for (int64_t c = r; c < nchunk; c += kRankWaves) {
+      uint4* vp = reinterpret_cast<uint4*>(rx + c * kChunkGroups * 256) + lane;
+      const uint4 v = *vp;
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o[h] = f32_to_f16_bits(sig * __uint_as_float(w4[h] << 16)) |
+               (static_cast<uint32_t>(f32_to_f16_bits(sig * __uint_as_float(w4[h] & 0xFFFF0000u))) << 16);
+      *vp = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    floatx4 wacc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) wacc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t c = r; c < nchunk; c += kRankWaves)
+    for (int64_t g = c * kChunkGroups; g < min(G, (c + 1) * kChunkGroups); ++g) {
+      uint32_t bw[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) bw[q] = rb[(q * Gp + g) * 64 + 4 * li + lq];
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const int64_t k = g * kGroup + lq * 32 + u * 8;
+        const uint4 xb = *reinterpret_cast<const uint4*>(rx + 2 * k);
+#pragma unroll
+        for (int term = 0; term < L; ++term) {
+          const uint4 g4 = *reinterpret_cast<const uint4*>(rg + 2 * MP * term + 2 * k);
+#pragma unroll
+          for (int qr = 0; qr < QR; ++qr) {
+            // 16 ranks x 16 tokens of (+-gamma) . x': the lane's eight B2 bits
+            // pick sign masks from the table, which flip its eight gammas
+            const int q = term * QR + qr;
+            const uint4 m = *reinterpret_cast<const uint4*>(lut + 4 * ((bw[q] >> (8 * u)) & 0xFFu));
+            const uint4 a = make_uint4(g4.x ^ m.x, g4.y ^ m.y, g4.z ^ m.z, g4.w ^ m.w);
+            wacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                             __builtin_bit_cast(f16x8, xb), wacc[q], 0, 0, 0);
+          }
+        }
+      }
+    }
+    const float isig = 1.f / sig;  // exact: sig is a power of two
+    // D[i][j]: rank i = 4 * (lane / 16) + r, token j = lane % 16; the token
+    // is column 0
+    if (li == 0) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) pr[(r * NQ + q) * 16 + 4 * lq + rr] = wacc[q][rr] * isig;
+    }
+  } else {
+    // ---- stream role: the wave's share of W0 through the ring ----------
+    const int64_t kbeg = static_cast<int64_t>(wv) * p.kq;
+    const int64_t kend = min(M, kbeg + p.kq);
+    const int ng = kend > kbeg ? static_cast<int>((kend - kbeg) / kGroup) : 0;
+    const uint16_t* wj[kSteps];  // W0 row 4j + lane / 16 (rows past N read row 0)
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int64_t rw = n0 + 4 * j + (lane >> 4);
+      wj[j] = p.w0 + (rw < p.N ? rw : 0) * p.ldw + 8 * ((lane & 15) ^ (4 * j + (lane >> 4)));
+    }
+    const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(ring)) +
+                           static_cast<unsigned>(wv * S * kTok1Slot);
+    auto issue = [&](int g) {
+      const unsigned sl = ring0 + static_cast<unsigned>((g % S) * kTok1Slot);
+      const int64_t k0 = kbeg + static_cast<int64_t>(g) * kGroup;
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) copy16_to_lds(wj[j] + k0, sl + j * 1024);
+      copy4_to_lds(p.x + k0 + 2 * lane, sl + kSteps * 1024);
+    };
+    const int pre = ng < S ? ng : S;
+    for (int g = 0; g < pre; ++g) issue(g);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < ng; ++g) {
+      wait_groups<C>(min(S - 1, ng - 1 - g));  // the groups issued after g
+      const unsigned char* sl = ring + (wv * S + g % S) * kTok1Slot;
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const uint4 a = *reinterpret_cast<const uint4*>(sl + 16 * (16 * li + ((4 * lq + u) ^ li)));
+        const uint4 xb = *reinterpret_cast<const uint4*>(sl + kSteps * 1024 + lq * 64 + u * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, xb), acc, 0, 0, 0);
+      }
+      if (g + S < ng) {
+        // this wave's reads of the slot are complete before it is refilled
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        issue(g + S);
+      }
+    }
+    if (li == 0) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) red[wv * 16 + 4 * lq + rr] = acc[rr];
+    }
+  }
+  __syncthreads();
+  // w = beta . (sum over the rank waves in order)
+  if (tid < NQ * 16) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRankWaves; ++r) sum += pr[r * NQ * 16 + tid];
+    wfin[tid] = br < p.R ? f16_bits_to_f32(bt) * sum : 0.f;
+  }
+  __syncthreads();
+  if (owner) {
+    // lane oj of row oi takes ranks oj, oj + 16, ...; 16 lanes per row
+    float v = 0.f;
+#pragma unroll
+    for (int term = 0; term < L; ++term) {
+      float z = 0.f;
+#pragma unroll
+      for (int qr = 0; qr < QR; ++qr) {
+        const int rk = 16 * qr + oj;
+        const float wr = wfin[term * QR * 16 + rk];
+        const uint32_t word = rk < 32 ? b1w[term][0] : b1w[term][1];
+        z += ((word >> (rk & 31)) & 1u) ? wr : -wr;
+      }
+      v += f16_bits_to_f32(al[term]) * z;
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (oj == 0 && on < p.N) {
+      float base = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMainWaves; ++q) base += red[q * 16 + oi];
+      store_out(p.y, p.y_dtype, on, base + v, 0);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_multi_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs* adapters,
@@ -656,19 +957,45 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
       if (reinterpret_cast<uintptr_t>(t.b2[i]) % 16 != 0 ||
           reinterpret_cast<uintptr_t>(t.gamma[i]) % 4 != 0)
         sp.fast = 0;
-#define DBF_SM(L_, QR_)                                                              \
-  adapter_small<L_, QR_><<<dim3(m.nmain), kMainThreads, small_lds_bytes<L_, QR_>(), s>>>(sp)
+    // LDS above 64 KiB needs the kernel's attribute raised once (to the
+    // whole budget: the one-token kernel's LDS depends on M)
+    auto go = [&](auto kern, size_t lds, int threads) -> hipError_t {
+      static bool attr_set = false;  // per instantiation; idempotent if raced
+      if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kMaxLds));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      kern<<<dim3(m.nmain), threads, lds, s>>>(sp);
+      return hipGetLastError();
+    };
+    // one token on whole 128-feature groups (16-byte gamma, since it is
+    // copied 16 bytes at a time), when the rank inputs fit in LDS beside a
+    // ring of at least 2 groups per stream wave
+    bool tok1 = T == 1 && sp.fast && M % kGroup == 0 && t.n > 0 &&
+                tok1_rank_copies(t.n, static_cast<int>(qr), M) <= 63;
+    for (int i = 0; i < t.n; ++i)
+      if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) tok1 = false;
+#define DBF_SM(L_, QR_)                                                                     \
+  if constexpr (L_ > 0) {                                                                   \
+    if (tok1 && tok1_lds_bytes<L_, QR_>(3, M) <= kMaxLds)                                   \
+      return go(adapter_tok1<L_, QR_, 3>, tok1_lds_bytes<L_, QR_>(3, M), kTok1Threads);     \
+    if (tok1 && tok1_lds_bytes<L_, QR_>(2, M) <= kMaxLds)                                   \
+      return go(adapter_tok1<L_, QR_, 2>, tok1_lds_bytes<L_, QR_>(2, M), kTok1Threads);     \
+  }                                                                                         \
+  return go(adapter_small<L_, QR_>, small_lds_bytes<L_, QR_>(), kMainThreads)
     switch (t.n * 4 + static_cast<int>(qr)) {
-      case 0: DBF_SM(0, 1); break;
-      case 5: DBF_SM(1, 1); break;
-      case 6: DBF_SM(1, 2); break;
-      case 7: DBF_SM(1, 3); break;
-      case 8: DBF_SM(1, 4); break;
-      case 9: DBF_SM(2, 1); break;
-      default: DBF_SM(2, 2); break;
+      case 0: DBF_SM(0, 1);
+      case 5: DBF_SM(1, 1);
+      case 6: DBF_SM(1, 2);
+      case 7: DBF_SM(1, 3);
+      case 8: DBF_SM(1, 4);
+      case 9: DBF_SM(2, 1);
+      default: DBF_SM(2, 2);
     }
 #undef DBF_SM
-    return hipGetLastError();
   }
   const size_t main_lds = sizeof(float) * (kMainWaves * 16 * 16 + 16 * kRChunk);
   int n1 = 0;

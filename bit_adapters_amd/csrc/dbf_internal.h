@@ -47,6 +47,18 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __half_as_ushort(__float2half_rn(f));
 }
 
+// Power of two that brings the largest |v| of a set of values (a token's
+// |scale_in . x|, say) into [2^14, 2^15), so that fp16(sigma . v) neither
+// overflows nor leaves the normal range where it matters (a power of two
+// commutes with the fp16 rounding wherever the result is normal).  1 for an
+// all-zero (or non-finite) set.
+__device__ __forceinline__ float act_scale(float amax) {
+  if (!(amax > 0.f) || !(amax <= 3.0e38f)) return 1.f;
+  int e = 0;
+  frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1)
+  return ldexpf(1.f, max(-100, min(100, 15 - e)));
+}
+
 // Load element i of an activation array of dtype code dt (bf16, f16, or
 // f32 for the backward's fp32 intermediates) as fp32.
 __device__ __forceinline__ float load_act(const void* p, int dt, int64_t i) {
@@ -71,6 +83,36 @@ __device__ __forceinline__ void store_out(void* y, int dt, int64_t i, float v,
     *p = f32_to_f16_bits(o);
   }
 }
+
+// ---- global -> LDS copies -------------------------------------------------
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// s_waitcnt immediate for this wave's LDS operations only (lgkmcnt(0)).
+constexpr int lgkmcnt0_imm() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
+
+// Copy 16 (4) bytes per lane from global memory straight into LDS: lane l's
+// bytes land at LDS byte address lds + 16 l (lds + 4 l); M0 = lds
+// (global_load_lds_dwordx4 / global_load_lds_dword).  Written as inline asm
+// so that the compiler does not guard every later LDS read with a wait for
+// all such copies; the kernels wait for them themselves (s_waitcnt vmcnt)
+// before reading the bytes.  The instructions have no register result, and
+// their address registers are read when they issue.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; it is still clobbered
+__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // ---- kernel launchers (host, internal C++) -------------------------------
 // Each returns hipSuccess or the launch error; arguments are already

@@ -70,18 +70,6 @@ __device__ __forceinline__ float scale_from_bound(float b) {
   return ldexpf(1.f, max(-100, min(100, 14 - e)));
 }
 
-// Power of two that brings a token's largest |scale_in . x| into
-// [2^14, 2^15), so that fp16(sigma . scale_in . x) neither overflows nor
-// leaves the normal range where it matters (the products of scale_in and x
-// are exact in fp32, and a power of two commutes with the fp16 rounding
-// wherever the result is normal).  1 for an all-zero (or non-finite) row.
-__device__ __forceinline__ float act_scale(float amax) {
-  if (!(amax > 0.f) || !(amax <= 3.0e38f)) return 1.f;
-  int e = 0;
-  frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1)
-  return ldexpf(1.f, max(-100, min(100, 15 - e)));
-}
-
 // ---- prep: u = fp16(sigma_t gamma . x) in pair order, l1 norms, max |beta|
 //
 // sigma_t (act_scale of the token's largest |gamma_i . x| over every term) is
@@ -315,26 +303,6 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm("" : "+v"(v));
   return v;
 }
-
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// of this wave are outstanding (expcnt and lgkmcnt not waited on).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-// Copy 16 bytes per lane from global memory straight into LDS: lane l's
-// bytes land at LDS byte address lds + 16 l (global_load_lds_dwordx4, M0 =
-// lds).  Written as inline asm so that the compiler does not guard every
-// later LDS read with a wait for all such copies; the kernel waits for them
-// itself (wait_then_barrier) before reading a stage.  The instruction has no
-// register result, and its address registers are read when it issues.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; it is still clobbered
-__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Wait for this wave's vector-memory operations down to n outstanding, then
 // a workgroup barrier; the signal fences keep the compiler from moving

@@ -99,3 +99,39 @@ def test_adapter_deterministic():
     a = _run(layer, x)
     b = _run(layer, x)
     assert np.array_equal(a, b)
+
+
+# One token with M a multiple of 128 stages every operand through LDS: ragged
+# rows, waves with no group (small M), one and two terms, every rank-tile
+# count, and waves with many more groups than the ring holds (M = 12288 gives
+# 12 per wave).
+@pytest.mark.parametrize("N,M,R,L,lo", [(65, 256, 17, 2, 0.01), (50, 1280, 48, 1, 0.01),
+                                        (33, 128, 16, 1, 0.01), (300, 5120, 33, 1, 0.01),
+                                        (48, 12288, 64, 1, 0.01), (96, 2048, 32, 2, -0.05),
+                                        (17, 4096, 1, 2, -0.05)])
+def test_one_token_staged(N, M, R, L, lo):
+    # lo < 0: scales of both signs
+    print("adapter one token", N, M, R, L, lo, flush=True)
+    layer, x = S.make_custom(N, M, R, L, 1, seed=13, base=True, scale_lo=lo,
+                             scale_hi=0.05)
+    o = O.default()
+    xx = x64(x)
+    ad = o.forward(O.terms64(layer), xx)
+    base = o.dense(O.widen_bf16(layer["w0"]), xx)
+    assert_close(_run(layer, x), ad + base, what="full")
+    assert_close(_run(layer, x, zero_w0=True), ad, what="adapter only")
+    assert_close(_run(layer, x, n_terms=0), base, what="base only")
+
+
+def test_one_token_strided_x():
+    # x one row inside a wider buffer (ldx = 1152, still 16-byte rows)
+    layer, x = S.make_custom(70, 1024, 40, 1, 1, seed=5, base=True, scale_lo=0.01,
+                             scale_hi=0.05)
+    o = O.default()
+    ref = o.adapter(O.widen_bf16(layer["w0"]), O.terms64(layer), x64(x))
+    xd = torch.zeros((1, 1152), dtype=torch.bfloat16, device=DEV)
+    xd[:, :1024] = x_dev(x)
+    y = D.lordba_adapter_forward(bf16_dev(layer["w0"]), device_terms(layer), 70, 1024, 40,
+                                 xd[:, :1024])
+    torch.cuda.synchronize()
+    assert_close(to_np(y), ref)
