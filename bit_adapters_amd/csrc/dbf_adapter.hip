@@ -613,12 +613,13 @@ constexpr int kTok1Copies = kSteps + 1;  // DMA instructions per group
 // The rank inputs are copied in chunks of 4 groups (1 KiB of x, of gamma,
 // and of the B2 words of each rank tile); chunk c goes to rank wave c % 8.
 constexpr int kChunkGroups = 4;
+constexpr int kTok1MaxChunks = 4;  // chunks per rank wave (M <= 16384)
 __host__ __device__ inline int64_t tok1_padded_groups(int64_t M) {
   return (M / kGroup + kChunkGroups - 1) / kChunkGroups * kChunkGroups;
 }
 
-// LDS of adapter_tok1: sign-mask table [256][16 B] | stream ring [8][S]
-// [slot] | base partials [8][16] | rank inputs, over Gp = the groups
+// LDS of adapter_tok1: sign-mask table [16 nibbles][32 copies][8 B] |
+// stream ring [8][S][slot] | base partials [8][16] | rank inputs, over Gp = the groups
 // rounded up to whole chunks: x [Gp * 128] (bf16, then the rank wave's
 // scaled fp16), gamma [L][Gp * 128], B2 words [NQ][Gp][64] | rank partials
 // [8][NQ * 16] | w [NQ * 16].
@@ -692,8 +693,32 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
   const int64_t br = 16 * (bq % QR) + (tid & 15);
   const uint16_t bt = p.t.beta[bq / QR][min(br, p.R - 1)];
 
-  // the rank waves' inputs go first, ahead of the W0 stream in the CU's
-  // memory pipeline (the stream waves issue nothing before the barrier)
+  // the stream waves' share of W0 and their ring (state of every wave;
+  // used by waves 0-7)
+  const int64_t kbeg = static_cast<int64_t>(wv) * p.kq;
+  const int64_t kend = min(M, kbeg + p.kq);
+  const int ng = kend > kbeg ? static_cast<int>((kend - kbeg) / kGroup) : 0;
+  const uint16_t* wj[kSteps];  // W0 row 4j + lane / 16 (rows past N read row 0)
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    const int64_t rw = n0 + 4 * j + (lane >> 4);
+    wj[j] = p.w0 + (rw < p.N ? rw : 0) * p.ldw + 8 * ((lane & 15) ^ (4 * j + (lane >> 4)));
+  }
+  const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(ring)) +
+                         static_cast<unsigned>(wv * S * kTok1Slot);
+  auto issue = [&](int g) {
+    const unsigned sl = ring0 + static_cast<unsigned>((g % S) * kTok1Slot);
+    const int64_t k0 = kbeg + static_cast<int64_t>(g) * kGroup;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) copy16_to_lds(wj[j] + k0, sl + j * 1024);
+    copy4_to_lds(p.x + k0 + 2 * lane, sl + kSteps * 1024);
+  };
+  const int pre = ng < S ? ng : S;
+
+  // Order of issue: a CU serves its memory requests in order, so the rank
+  // waves' inputs go first and the stream waves issue nothing before the
+  // barrier below (measured: with the stream's first groups ahead of them,
+  // rank 16 took 10.8 instead of 10.1 us).
   const int64_t nchunk = Gp / kChunkGroups;
   if (wv >= kMainWaves) {
     const unsigned rx0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(rx));
@@ -716,10 +741,13 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
                       rb0 + static_cast<unsigned>(256 * q * Gp) + off);
     }
   }
-  // the sign-mask table of adapter_small
+  // sign masks by nibble: entry n (two dwords, four fp16 lanes) flips lane
+  // h where bit h of n is clear; 32 interleaved copies, copy c of entry n
+  // at 8-byte slot 32 n + c, so the 8-byte reads of 32 lanes (copy = lane
+  // % 32) hit 32 different bank pairs whatever the nibbles
   for (int e = tid; e < 1024; e += kTok1Threads) {
-    const uint32_t nb = ~static_cast<uint32_t>(e >> 2);
-    const int d = e & 3;
+    const uint32_t nb = ~static_cast<uint32_t>(e >> 6);
+    const int d = e & 1;
     lut[e] = (((nb >> (2 * d)) & 1u) << 15) | (((nb >> (2 * d + 1)) & 1u) << 31);
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -737,10 +765,16 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
     // value is at least 2^-17 (x has 8 significant bits), so below 2^-31 of
     // the largest only; every product with gamma (fp16) is then exact in the
     // fp32 accumulator, and 1 / sigma is applied to the wave's partial
+    // (each lane's 16 bytes of each chunk stay in registers between the
+    // two passes: one LDS round trip, not two)
+    uint4 xv[kTok1MaxChunks];
     float amax = 0.f;
-    for (int64_t c = r; c < nchunk; c += kRankWaves) {
-      const uint4 v = reinterpret_cast<const uint4*>(rx + c * kChunkGroups * 256)[lane];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < kTok1MaxChunks; ++i) {
+      const int64_t c = r + i * kRankWaves;
+      xv[i] = c < nchunk ? reinterpret_cast<const uint4*>(rx + c * kChunkGroups * 256)[lane]
+                         : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w4[h] << 16)),
@@ -749,44 +783,68 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     const float sig = act_scale(amax);
-    for (int64_t c = r; c < nchunk; c += kRankWaves) {
-      uint4* vp = reinterpret_cast<uint4*>(rx + c * kChunkGroups * 256) + lane;
-      const uint4 v = *vp;
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < kTok1MaxChunks; ++i) {
+      const int64_t c = r + i * kRankWaves;
+      if (c >= nchunk) break;
+      const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
       uint32_t o[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         o[h] = f32_to_f16_bits(sig * __uint_as_float(w4[h] << 16)) |
                (static_cast<uint32_t>(f32_to_f16_bits(sig * __uint_as_float(w4[h] & 0xFFFF0000u))) << 16);
-      *vp = make_uint4(o[0], o[1], o[2], o[3]);
+      reinterpret_cast<uint4*>(rx + c * kChunkGroups * 256)[lane] = make_uint4(o[0], o[1], o[2], o[3]);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     floatx4 wacc[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) wacc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // Each step's operands come from LDS (x', gamma, and a sign mask per
+    // rank tile picked by the lane's B2 byte); they are read one step
+    // ahead of the MFMAs that use them, so a step's LDS round trip overlaps
+    // the previous step's work (read just in time, every tile waited for
+    // its own round trip).
+    struct StepOps {
+      uint4 x, g[L], m[NQ];
+    };
+    const uint32_t* mylut = lut + 2 * (lane & 31);
     for (int64_t c = r; c < nchunk; c += kRankWaves)
     for (int64_t g = c * kChunkGroups; g < min(G, (c + 1) * kChunkGroups); ++g) {
       uint32_t bw[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) bw[q] = rb[(q * Gp + g) * 64 + 4 * li + lq];
+      auto load_step = [&](int u, StepOps& o) {
+        const int64_t k = g * kGroup + lq * 32 + u * 8;
+        o.x = *reinterpret_cast<const uint4*>(rx + 2 * k);
+#pragma unroll
+        for (int term = 0; term < L; ++term)
+          o.g[term] = *reinterpret_cast<const uint4*>(rg + 2 * MP * term + 2 * k);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const uint32_t byte = bw[q] >> (8 * u);
+          const uint2 lo = *reinterpret_cast<const uint2*>(mylut + 64 * (byte & 15u));
+          const uint2 hi = *reinterpret_cast<const uint2*>(mylut + 64 * ((byte >> 4) & 15u));
+          o.m[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      };
+      StepOps cur, nxt;
+      load_step(0, cur);
 #pragma unroll
       for (int u = 0; u < kSteps; ++u) {
-        const int64_t k = g * kGroup + lq * 32 + u * 8;
-        const uint4 xb = *reinterpret_cast<const uint4*>(rx + 2 * k);
+        if (u + 1 < kSteps) load_step(u + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int term = 0; term < L; ++term) {
-          const uint4 g4 = *reinterpret_cast<const uint4*>(rg + 2 * MP * term + 2 * k);
-#pragma unroll
-          for (int qr = 0; qr < QR; ++qr) {
-            // 16 ranks x 16 tokens of (+-gamma) . x': the lane's eight B2 bits
-            // pick sign masks from the table, which flip its eight gammas
-            const int q = term * QR + qr;
-            const uint4 m = *reinterpret_cast<const uint4*>(lut + 4 * ((bw[q] >> (8 * u)) & 0xFFu));
-            const uint4 a = make_uint4(g4.x ^ m.x, g4.y ^ m.y, g4.z ^ m.z, g4.w ^ m.w);
-            wacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                             __builtin_bit_cast(f16x8, xb), wacc[q], 0, 0, 0);
-          }
+        for (int q = 0; q < NQ; ++q) {
+          // 16 ranks x 16 tokens of (+-gamma) . x': the mask flips the signs
+          // of the lane's eight gammas where its B2 bits are 0
+          const uint4& g4 = cur.g[q / QR];
+          const uint4 a = make_uint4(g4.x ^ cur.m[q].x, g4.y ^ cur.m[q].y, g4.z ^ cur.m[q].z,
+                                     g4.w ^ cur.m[q].w);
+          wacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                           __builtin_bit_cast(f16x8, cur.x), wacc[q], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < kSteps) cur = nxt;
       }
     }
     const float isig = 1.f / sig;  // exact: sig is a power of two
@@ -800,25 +858,6 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
     }
   } else {
     // ---- stream role: the wave's share of W0 through the ring ----------
-    const int64_t kbeg = static_cast<int64_t>(wv) * p.kq;
-    const int64_t kend = min(M, kbeg + p.kq);
-    const int ng = kend > kbeg ? static_cast<int>((kend - kbeg) / kGroup) : 0;
-    const uint16_t* wj[kSteps];  // W0 row 4j + lane / 16 (rows past N read row 0)
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      const int64_t rw = n0 + 4 * j + (lane >> 4);
-      wj[j] = p.w0 + (rw < p.N ? rw : 0) * p.ldw + 8 * ((lane & 15) ^ (4 * j + (lane >> 4)));
-    }
-    const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(ring)) +
-                           static_cast<unsigned>(wv * S * kTok1Slot);
-    auto issue = [&](int g) {
-      const unsigned sl = ring0 + static_cast<unsigned>((g % S) * kTok1Slot);
-      const int64_t k0 = kbeg + static_cast<int64_t>(g) * kGroup;
-#pragma unroll
-      for (int j = 0; j < kSteps; ++j) copy16_to_lds(wj[j] + k0, sl + j * 1024);
-      copy4_to_lds(p.x + k0 + 2 * lane, sl + kSteps * 1024);
-    };
-    const int pre = ng < S ? ng : S;
     for (int g = 0; g < pre; ++g) issue(g);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < ng; ++g) {
@@ -975,6 +1014,7 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
     // copied 16 bytes at a time), when the rank inputs fit in LDS beside a
     // ring of at least 2 groups per stream wave
     bool tok1 = T == 1 && sp.fast && M % kGroup == 0 && t.n > 0 &&
+                tok1_padded_groups(M) / kChunkGroups <= kRankWaves * kTok1MaxChunks &&
                 tok1_rank_copies(t.n, static_cast<int>(qr), M) <= 63;
     for (int i = 0; i < t.n; ++i)
       if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) tok1 = false;
