@@ -192,13 +192,15 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   const int64_t nch = p.mpad / 8;  // chunks of the padded row
   constexpr int64_t kRoundCh = 256 * kPrepRound;
   // one round covers this thread's whole row: its values stay in registers
-  // from the max pass to the conversion
-  const bool single = p.L == 1 && nch <= kRoundCh && p.mpad <= kPrepSeg;
+  // from the max pass to the conversion (the max pass takes the terms in
+  // the order term + 1, ..., term, so the last one is this workgroup's own)
+  const bool single = nch <= kRoundCh && p.mpad <= kPrepSeg;
   float keep[kPrepRound][8];
 
   // pass 1: the token's largest |gamma_i . x| over every term
   float amx = 0.f;
-  for (int i = 0; i < p.L; ++i)
+  for (int ii = 0; ii < p.L; ++ii) {
+    const int i = (term + 1 + ii) % p.L;
     for (int64_t cs = tid; cs < nch; cs += kRoundCh) {
       prep_round(p, i, tok, cs, keep);
 #pragma unroll
@@ -206,6 +208,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) amx = fmaxf(amx, fabsf(keep[j][e]));
     }
+  }
   const float sig = act_scale(block_reduce(amx, false, red));
   if (term == 0 && tid == 0) p.sig[tok] = sig;
 
