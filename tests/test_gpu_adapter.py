@@ -123,6 +123,34 @@ def test_one_token_staged(N, M, R, L, lo):
     assert_close(_run(layer, x, n_terms=0), base, what="base only")
 
 
+# The one-token kernel's LDS limit: rank 64 fits with M = 7168 (ring of two
+# groups per stream wave) and not with M = 7296 (the older kernel runs);
+# rank 16 at M = 8192 fits with a ring of three.
+@pytest.mark.parametrize("M,R", [(7168, 64), (7296, 64), (8192, 16)])
+def test_one_token_lds_limits(M, R):
+    print("adapter one token, LDS limit", M, R, flush=True)
+    layer, x = S.make_custom(40, M, R, 1, 1, seed=21, base=True, scale_lo=0.01, scale_hi=0.05)
+    o = O.default()
+    xx = x64(x)
+    ref = o.forward(O.terms64(layer), xx) + o.dense(O.widen_bf16(layer["w0"]), xx)
+    assert_close(_run(layer, x), ref)
+
+
+def test_one_token_gamma_not_16_byte_aligned():
+    # gamma is copied 16 bytes at a time; an offset gamma takes the older kernel
+    layer, x = S.make_custom(64, 1024, 32, 1, 1, seed=22, base=True, scale_lo=0.01,
+                             scale_hi=0.05)
+    o = O.default()
+    ref = o.adapter(O.widen_bf16(layer["w0"]), O.terms64(layer), x64(x))
+    t = device_terms(layer)[0]
+    g = torch.zeros(1024 + 8, dtype=torch.float16, device=DEV)
+    g[4:4 + 1024] = t.gamma
+    shifted = D.DbfTerm(t.b1, t.b2, t.alpha, t.beta, g[4:4 + 1024])
+    y = D.lordba_adapter_forward(bf16_dev(layer["w0"]), [shifted], 64, 1024, 32, x_dev(x))
+    torch.cuda.synchronize()
+    assert_close(to_np(y), ref)
+
+
 def test_one_token_strided_x():
     # x one row inside a wider buffer (ldx = 1152, still 16-byte rows)
     layer, x = S.make_custom(70, 1024, 40, 1, 1, seed=5, base=True, scale_lo=0.01,
