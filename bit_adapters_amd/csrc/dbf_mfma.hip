@@ -173,22 +173,56 @@ __device__ __forceinline__ float block_reduce(float v, bool sum, float* red) {
   return r;
 }
 
+// Feature e of a 16-byte chunk of x as loaded: 8 fp32 values in x0, x1
+// (X32) or 8 fp16 / bf16 values in x0.
+template <bool X32>
+__device__ __forceinline__ float chunk_x(const PrepArgs& p, const uint4& x0, const uint4& x1, int e) {
+  if constexpr (X32) {
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    return __uint_as_float(w[e]);
+  }
+  const uint32_t w[4] = {x0.x, x0.y, x0.z, x0.w};
+  const uint16_t b = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+  return p.x_dtype == DBF_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+__device__ __forceinline__ float chunk_g(const uint4& g, int e) {
+  const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+  return f16_bits_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
+}
+
+// Term slots whose gamma rows the fast path of prep_kernel loads per round
+// trip: 0 = the workgroup's own term only (one term), else 2 or 4.  X32: x
+// is fp32 read with 16-byte loads (vec == 2).  Both are template parameters
+// so that no load of the fast path sits under a branch.
+template <int LG, bool X32>
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   __shared__ float red[4];
   __shared__ __align__(16) _Float16 useg[kPrepSeg];
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x;
-  const int64_t nrow = static_cast<int64_t>(p.L) * p.T;
-  if (blk >= nrow) {
-    const int term = static_cast<int>(blk - nrow);
+  // the L max|beta| workgroups come first, so that they start early
+  if (blk < p.L) {
+    const int term = static_cast<int>(blk);
+    const uint16_t* bt = p.beta[term];
     float m = 0.f;
-    for (int64_t r = tid; r < p.R; r += 256) m = fmaxf(m, fabsf(f16_bits_to_f32(p.beta[term][r])));
+    if (p.R > 0) {
+      // 16 loads in flight per thread; indices past R repeat the last value
+      constexpr int kU = 16;
+      for (int64_t r0 = 0; r0 < p.R; r0 += 256 * kU) {
+        uint16_t b[kU];
+#pragma unroll
+        for (int k = 0; k < kU; ++k) b[k] = bt[min<int64_t>(r0 + 256 * k + tid, p.R - 1)];
+#pragma unroll
+        for (int k = 0; k < kU; ++k) m = fmaxf(m, fabsf(f16_bits_to_f32(b[k])));
+      }
+    }
     m = block_reduce(m, false, red);
     if (tid == 0) p.bmax[term] = m;
     return;
   }
-  const int term = static_cast<int>(blk / p.T);
-  const int64_t tok = blk - static_cast<int64_t>(term) * p.T;
+  const int64_t row = blk - p.L;  // term * T + token
+  const int term = static_cast<int>(row / p.T);
+  const int64_t tok = row - static_cast<int64_t>(term) * p.T;
   const int64_t nch = p.mpad / 8;  // chunks of the padded row
   constexpr int64_t kRoundCh = 256 * kPrepRound;
   // one round covers this thread's whole row: its values stay in registers
@@ -199,14 +233,77 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
 
   // pass 1: the token's largest |gamma_i . x| over every term
   float amx = 0.f;
-  for (int ii = 0; ii < p.L; ++ii) {
-    const int i = (term + 1 + ii) % p.L;
-    for (int64_t cs = tid; cs < nch; cs += kRoundCh) {
-      prep_round(p, i, tok, cs, keep);
+  if (single && p.vec == (X32 ? 2 : 1) && p.M % 8 == 0) {
+    // Fast path: every chunk is whole or past M.  max_i |gamma_i[m] x[m]|
+    // = |x[m]| max_i |gamma_i[m]| holds for the rounded products too
+    // (rounding is monotonic; fmaxf skips a NaN gamma like the per-term
+    // maximum does), so x and the own term's gamma are loaded once and the
+    // terms' gamma rows LG at a time, each group in one round trip.
+    const int64_t nfull = p.M / 8;
+    const uint16_t* gown = p.gamma[term];
+    uint4 xr[kPrepRound][2], gr[kPrepRound];
+    int64_t k0[kPrepRound];
 #pragma unroll
-      for (int j = 0; j < kPrepRound; ++j)
+    for (int j = 0; j < kPrepRound; ++j) {
+      k0[j] = 8 * min(tid + 256 * j, nfull - 1);
+      if constexpr (X32) {
+        const float* xf32 = static_cast<const float*>(p.x) + tok * p.ldx + k0[j];
+        xr[j][0] = *reinterpret_cast<const uint4*>(xf32);
+        xr[j][1] = *reinterpret_cast<const uint4*>(xf32 + 4);
+      } else {
+        xr[j][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + tok * p.ldx + k0[j]);
+        xr[j][1] = make_uint4(0u, 0u, 0u, 0u);  // unused
+      }
+      gr[j] = *reinterpret_cast<const uint4*>(gown + k0[j]);
+    }
+    // the own term's gamma is folded in last: no use of it stands between
+    // its loads and those of the first group
+    float gm[kPrepRound][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amx = fmaxf(amx, fabsf(keep[j][e]));
+    for (int j = 0; j < kPrepRound; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm[j][e] = 0.f;
+    if constexpr (LG > 0) {
+      for (int g0 = 0; g0 < p.L; g0 += LG) {
+        uint4 gs[LG][kPrepRound];
+#pragma unroll
+        for (int i = 0; i < LG; ++i) {
+          const uint16_t* gi = p.gamma[min(g0 + i, p.L - 1)];
+#pragma unroll
+          for (int j = 0; j < kPrepRound; ++j) gs[i][j] = *reinterpret_cast<const uint4*>(gi + k0[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < LG; ++i)
+#pragma unroll
+          for (int j = 0; j < kPrepRound; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gm[j][e] = fmaxf(gm[j][e], fabsf(chunk_g(gs[i][j], e)));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPrepRound; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm[j][e] = fmaxf(gm[j][e], fabsf(chunk_g(gr[j], e)));
+#pragma unroll
+    for (int j = 0; j < kPrepRound; ++j) {
+      const bool live = tid + 256 * j < nfull;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = chunk_x<X32>(p, xr[j][0], xr[j][1], e);
+        keep[j][e] = live ? chunk_g(gr[j], e) * xv : 0.f;
+        if (live) amx = fmaxf(amx, gm[j][e] * fabsf(xv));
+      }
+    }
+  } else {
+    for (int ii = 0; ii < p.L; ++ii) {
+      const int i = (term + 1 + ii) % p.L;
+      for (int64_t cs = tid; cs < nch; cs += kRoundCh) {
+        prep_round(p, i, tok, cs, keep);
+#pragma unroll
+        for (int j = 0; j < kPrepRound; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amx = fmaxf(amx, fabsf(keep[j][e]));
+      }
     }
   }
   const float sig = act_scale(block_reduce(amx, false, red));
@@ -217,7 +314,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   // chunk of the pair order (positions 2 j and 2 j + 1 hold features j and
   // j + 16 of a 32-feature group)
   float acc = 0.f;
-  _Float16* out = p.u + blk * p.mpad;
+  _Float16* out = p.u + row * p.mpad;
   for (int64_t seg = 0; seg < p.mpad; seg += kPrepSeg) {
     const int64_t segn = min<int64_t>(kPrepSeg, p.mpad - seg);
     const int64_t c0 = seg / 8, c1 = c0 + segn / 8;
@@ -257,7 +354,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
   }
   // sum_m |u| at the true scale (sigma is a power of two: exact)
   acc = block_reduce(acc, true, red);
-  if (tid == 0) p.l1[blk] = acc / sig;
+  if (tid == 0) p.l1[row] = acc / sig;
 }
 
 // ---- the two products -------------------------------------------------
@@ -630,49 +727,79 @@ struct Reduce1Args {
   _Float16* v;
 };
 
+// The largest bmax_i * l1_i[tok] over the terms.  Every term slot is loaded
+// (slots past L repeat the last term, which leaves the maximum unchanged), so
+// no load waits behind a loop branch.
+__device__ __forceinline__ float term_bound(const float* bmax, const float* l1, int L, int64_t T,
+                                            int64_t tok) {
+  float b[DBF_MAX_TERMS], l[DBF_MAX_TERMS];
+#pragma unroll
+  for (int i = 0; i < DBF_MAX_TERMS; ++i) {
+    const int ii = min(i, L - 1);
+    b[i] = bmax[ii];
+    l[i] = l1[static_cast<int64_t>(ii) * T + tok];
+  }
+  float bnd = 0.f;
+#pragma unroll
+  for (int i = 0; i < DBF_MAX_TERMS; ++i) bnd = fmaxf(bnd, b[i] * l[i]);
+  return bnd;
+}
+
+// NS = nsplit.  A thread's loads (scales, every split's partials, beta) are
+// all issued before the first of them is used, with addresses clamped into
+// the buffers instead of branches around the loads, so that the kernel
+// waits for memory once.
+// Grid: (ceil(T * vp / 8 / 256), L); the term is the grid row, so its beta
+// pointer is a scalar load.
+template <int NS>
 __global__ void __launch_bounds__(256) reduce1_kernel(Reduce1Args p) {
   const int64_t nch = p.vp / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= p.L * p.T * nch) return;
-  const int64_t row = idx / nch;  // term * T + token
-  const int64_t c = idx - row * nch;
-  const int term = static_cast<int>(row / p.T);
-  const int64_t tok = row - static_cast<int64_t>(term) * p.T;
-  float bnd = 0.f;
-  for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
-  const float sc = scale_from_bound(bnd) / p.sig[tok];
+  if (idx >= p.T * nch) return;
+  const int term = static_cast<int>(blockIdx.y);
+  const int64_t tok = idx / nch;
+  const int64_t c = idx - tok * nch;
+  const int64_t row = static_cast<int64_t>(term) * p.T + tok;
   const int64_t r0[2] = {32 * (c >> 2) + 4 * (c & 3), 32 * (c >> 2) + 16 + 4 * (c & 3)};
   const int64_t sstride = static_cast<int64_t>(p.L) * p.T * p.ldp;
-  // all splits' loads in flight at once, then the sums in split order
-  float4 q[kMaxSplit][2];
+  // a chunk that starts past R reads the row's last chunk (its outputs are
+  // zero); one that starts below R lies inside the row (ldp = R rounded up to 4)
+  float4 q[NS][2];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp)
+  for (int sp = 0; sp < NS; ++sp)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
-      q[sp][hh] = (sp < p.nsplit && r0[hh] < p.R)
-                      ? *reinterpret_cast<const float4*>(p.part + sp * sstride + row * p.ldp + r0[hh])
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      q[sp][hh] = *reinterpret_cast<const float4*>(p.part + sp * sstride + row * p.ldp +
+                                                   min(r0[hh], p.ldp - 4));
+  const uint16_t* bt = p.beta[term];
+  uint16_t bb[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bb[hh][e] = bt[min(r0[hh] + e, p.R - 1)];
+  const float sig = p.sig[tok];
+  const float sc = scale_from_bound(term_bound(p.bmax, p.l1, p.L, p.T, tok)) / sig;
+  // the sums in split order
   float sum[2][4] = {};
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp)
+  for (int sp = 0; sp < NS; ++sp)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      if (sp < p.nsplit) {
-        sum[hh][0] += q[sp][hh].x; sum[hh][1] += q[sp][hh].y;
-        sum[hh][2] += q[sp][hh].z; sum[hh][3] += q[sp][hh].w;
-      }
+    for (int hh = 0; hh < 2; ++hh) {
+      sum[hh][0] += q[sp][hh].x; sum[hh][1] += q[sp][hh].y;
+      sum[hh][2] += q[sp][hh].z; sum[hh][3] += q[sp][hh].w;
+    }
+  // positions past R are zeroed with a mask the optimizer cannot see through:
+  // a select there would become a branch with the loads sunk into it
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    _Float16 hv[2];
+    uint32_t hb[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int64_t r = r0[hh] + e;
-      hv[hh] = r < p.R ? static_cast<_Float16>(sc * f16_bits_to_f32(p.beta[term][r]) * sum[hh][e])
-                       : static_cast<_Float16>(0.f);
+      const _Float16 hv = static_cast<_Float16>(sc * f16_bits_to_f32(bb[hh][e]) * sum[hh][e]);
+      hb[hh] = __builtin_bit_cast(uint16_t, hv) & opaque(r0[hh] + e < p.R ? 0xFFFFu : 0u);
     }
-    o[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[0])) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[1])) << 16);
+    o[e] = hb[0] | (hb[1] << 16);
   }
   *reinterpret_cast<uint4*>(p.v + row * p.vp + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -694,32 +821,87 @@ struct Reduce2Args {
   int accumulate;
 };
 
+// NS = nsplit; loads issued as in reduce1_kernel.  Four whole columns are
+// written with one store when y's layout allows it.
+template <int NS>
 __global__ void __launch_bounds__(256) reduce2_kernel(Reduce2Args p) {
   const int64_t nch = (p.N + 3) / 4;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= p.T * nch) return;
   const int64_t tok = idx / nch;
-  const int64_t n0 = 4 * (idx - tok * nch);
-  float bnd = 0.f;
-  for (int i = 0; i < p.L; ++i) bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
-  const float sc = scale_from_bound(bnd) * (p.sig_div ? p.sig[tok] : 1.f);
-  float4 q[kMaxSplit];
+  const int64_t n0 = 4 * (idx - tok * nch);  // n0 + 4 <= ldp (N rounded up to 4)
+  float4 q[NS];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp)
-    q[sp] = sp < p.nsplit ? *reinterpret_cast<const float4*>(p.part + (sp * p.T + tok) * p.ldp + n0)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < NS; ++sp)
+    q[sp] = *reinterpret_cast<const float4*>(p.part + (sp * p.T + tok) * p.ldp + n0);
+  uint16_t ab[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ab[e] = p.alpha[min(n0 + e, p.N - 1)];
+  const float sg = p.sig[tok];
+  const float sc = scale_from_bound(term_bound(p.bmax, p.l1, p.L, p.T, tok)) * (p.sig_div ? sg : 1.f);
   float sum[4] = {};
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp)
-    if (sp < p.nsplit) {
-      sum[0] += q[sp].x; sum[1] += q[sp].y; sum[2] += q[sp].z; sum[3] += q[sp].w;
+  for (int sp = 0; sp < NS; ++sp) {
+    sum[0] += q[sp].x; sum[1] += q[sp].y; sum[2] += q[sp].z; sum[3] += q[sp].w;
+  }
+  // alpha with one term, else 1, chosen by a mask (a select would become a
+  // branch with the alpha loads sunk into it)
+  const uint32_t one_term = opaque(p.L == 1 ? 0xFFFFu : 0u);
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = f16_bits_to_f32(static_cast<uint16_t>((ab[e] & one_term) | (0x3C00u & ~one_term))) * sum[e] / sc;
+  const int64_t at = tok * p.ldy + n0;
+  if (!p.accumulate && n0 + 4 <= p.N) {
+    if (p.y_dtype == DBF_F32) {
+      float* dst = static_cast<float*>(p.y) + at;
+      if (reinterpret_cast<uintptr_t>(dst) % 16 == 0) {
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        return;
+      }
+    } else {
+      uint16_t* dst = static_cast<uint16_t*>(p.y) + at;
+      if (reinterpret_cast<uintptr_t>(dst) % 8 == 0) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t lo = p.y_dtype == DBF_BF16 ? f32_to_bf16_bits(o[2 * h]) : f32_to_f16_bits(o[2 * h]);
+          const uint32_t hi = p.y_dtype == DBF_BF16 ? f32_to_bf16_bits(o[2 * h + 1])
+                                                    : f32_to_f16_bits(o[2 * h + 1]);
+          w[h] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+        return;
+      }
     }
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int64_t n = n0 + e;
-    if (n >= p.N) break;
-    const float a = p.L == 1 ? f16_bits_to_f32(p.alpha[n]) : 1.f;
-    store_out(p.y, p.y_dtype, tok * p.ldy + n, a * sum[e] / sc, p.accumulate);
+    if (n0 + e >= p.N) break;
+    store_out(p.y, p.y_dtype, at + e, o[e], p.accumulate);
+  }
+}
+
+// Launch the reduction instantiated for the split count (2 .. kMaxSplit).
+template <int NS = 2>
+hipError_t launch_reduce1(const Reduce1Args& r, dim3 grid, hipStream_t s) {
+  if constexpr (NS > kMaxSplit) {
+    return hipErrorInvalidValue;
+  } else {
+    if (r.nsplit != NS) return launch_reduce1<NS + 1>(r, grid, s);
+    reduce1_kernel<NS><<<grid, 256, 0, s>>>(r);
+    return hipGetLastError();
+  }
+}
+
+template <int NS = 2>
+hipError_t launch_reduce2(const Reduce2Args& r, dim3 grid, hipStream_t s) {
+  if constexpr (NS > kMaxSplit) {
+    return hipErrorInvalidValue;
+  } else {
+    if (r.nsplit != NS) return launch_reduce2<NS + 1>(r, grid, s);
+    reduce2_kernel<NS><<<grid, 256, 0, s>>>(r);
+    return hipGetLastError();
   }
 }
 
@@ -823,6 +1005,23 @@ Plan make_plan(int64_t N, int64_t M, int64_t R, int L, int64_t T) {
   return pl;
 }
 
+// prep: L max|beta| workgroups, then one per (term, token)
+hipError_t launch_prep(const PrepArgs& pa, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(pa.L * pa.T + pa.L));
+  const bool x32 = pa.vec == 2;
+  if (pa.L == 1) {
+    if (x32) prep_kernel<0, true><<<grid, 256, 0, s>>>(pa);
+    else prep_kernel<0, false><<<grid, 256, 0, s>>>(pa);
+  } else if (pa.L == 2) {
+    if (x32) prep_kernel<2, true><<<grid, 256, 0, s>>>(pa);
+    else prep_kernel<2, false><<<grid, 256, 0, s>>>(pa);
+  } else {
+    if (x32) prep_kernel<4, true><<<grid, 256, 0, s>>>(pa);
+    else prep_kernel<4, false><<<grid, 256, 0, s>>>(pa);
+  }
+  return hipGetLastError();
+}
+
 struct WsLayout {
   size_t u, v, l1, bmax, sig, part, total;
 };
@@ -909,8 +1108,7 @@ hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void*
     pa.gamma[i] = t.gamma[i];
     pa.beta[i] = nullptr;
   }
-  prep_kernel<<<dim3(static_cast<unsigned>(t.n * T + t.n)), 256, 0, s>>>(pa);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_prep(pa, s);
   if (e != hipSuccess) return e;
 
   GemmArgs b{};
@@ -929,8 +1127,7 @@ hipError_t launch_bool_mfma(const TermPtrs& t, int64_t N, int64_t M, const void*
   r.part = part; r.ldp = b.ldp; r.T = T; r.N = N; r.L = t.n; r.nsplit = lay.tl.nsplit;
   r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax; r.sig = sig; r.sig_div = 1;
   r.y = y; r.y_dtype = y_dtype; r.ldy = ldy; r.accumulate = accumulate;
-  reduce2_kernel<<<dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), 256, 0, s>>>(r);
-  return hipGetLastError();
+  return launch_reduce2(r, dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), s);
 }
 
 hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
@@ -957,8 +1154,7 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
     pa.gamma[i] = t.gamma[i];
     pa.beta[i] = t.beta[i];
   }
-  prep_kernel<<<dim3(static_cast<unsigned>(t.n * T + t.n)), 256, 0, s>>>(pa);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_prep(pa, s);
   if (e != hipSuccess) return e;
 
   GemmArgs a{};
@@ -977,9 +1173,7 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
     r.part = part; r.ldp = a.ldp; r.T = T; r.R = R; r.vp = a.vp; r.L = t.n;
     r.nsplit = pl.t1.nsplit; r.l1 = l1; r.bmax = bmax; r.sig = sig; r.v = v;
     for (int i = 0; i < t.n; ++i) r.beta[i] = t.beta[i];
-    const int64_t n = t.n * T * (a.vp / 8);
-    reduce1_kernel<<<dim3(static_cast<unsigned>(cdiv(n, 256))), 256, 0, s>>>(r);
-    e = hipGetLastError();
+    e = launch_reduce1(r, dim3(static_cast<unsigned>(cdiv(T * (a.vp / 8), 256)), t.n), s);
     if (e != hipSuccess) return e;
   }
 
@@ -999,8 +1193,7 @@ hipError_t launch_mfma(const TermPtrs& t, int64_t N, int64_t M, int64_t R,
   r.part = part; r.ldp = b.ldp; r.T = T; r.N = N; r.L = t.n; r.nsplit = pl.t2.nsplit;
   r.alpha = t.alpha[0]; r.l1 = l1; r.bmax = bmax; r.sig = sig; r.sig_div = 0;
   r.y = y; r.y_dtype = y_dtype; r.ldy = ldy; r.accumulate = accumulate;
-  reduce2_kernel<<<dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), 256, 0, s>>>(r);
-  return hipGetLastError();
+  return launch_reduce2(r, dim3(static_cast<unsigned>(cdiv(T * cdiv(N, 4), 256))), s);
 }
 
 }  // namespace dbf
