@@ -126,8 +126,8 @@ def auto_bool_path(T, K):
 def auto_dbf_path(N, M, R, L, T):
     # the library's automatic choice for the double-binary forward
     # (dbf_abi.hip, resolve_dbf_path): decode while T <= 4 or the sign work
-    # of the 4-token blocks is at most 1.0e8 lookups
-    return "decode" if T <= 4 or L * ((T + 3) // 4) * R * (N + M) <= 1.0e8 else "mfma"
+    # of the 4-token blocks is at most 8.0e7 lookups
+    return "decode" if T <= 4 or L * ((T + 3) // 4) * R * (N + M) <= 8.0e7 else "mfma"
 
 
 def main():

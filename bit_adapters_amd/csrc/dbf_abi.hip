@@ -28,24 +28,22 @@ bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0
 // or its sign work, n_terms * ceil(T / 4) * R * (N + M) sign lookups (every
 // 4-token block runs both products of every term), is at most
 // kAutoDecodeWork; else the MFMA products, whose cost at these token counts
-// is nearly flat.  Measured, decode vs MFMA, each path forced:
-//   512 x 512, R 256: decode faster through 64 tokens (10.9 vs 17.8 us);
-//   4096 x 4096, R 2048: faster through 20 tokens (25.9 vs 27.4 us), even at
-//     28 (28.5 vs 28.7 us), slower at 24 by 3% (27.0 vs 27.8 us, the one
-//     measured point the rule gets wrong) and from 30 (29.7 vs 28.7 us);
-//   the same with two terms: slower from 12 tokens (34.1 vs 28.8 us);
-//   11008 x 4096, R 2048, three terms: faster at 4 tokens (30.8 vs 40.8 us),
-//     slower from 5 (44.9 vs 41.2 us);
-//   8192 x 8192, R 6144: faster at 4 tokens (29.6 vs 46.5 us); at 8 the
-//     16-wave decode edges ahead (45.2 vs 46.7 us) while the rule picks MFMA.
+// is nearly flat.  Measured, decode vs MFMA, each path forced (us per call):
+//   512 x 512, R 256: decode faster through 64 tokens (12.0 vs 20.7);
+//   4096 x 4096, R 2048: faster through 16 tokens (20.3 vs 25.1), slower
+//     from 20 (26.9 vs 26.1, sign work 8.4e7);
+//   11008 x 4096, R 2048, three terms: faster at 4 tokens (31.3 vs 32.7),
+//     slower from 5 (45.7 vs 32.7);
+//   8192 x 8192, R 6144: faster at 4 tokens (28.6 vs 33.2), slower at 8
+//     (46.4 vs 33.7).
 // The boolean kernels (one product each, over a full N x M sign matrix):
 // decode while its launch has one token block (up to 2 tokens) or K times
 // its token blocks (of 1, 2 or 4 tokens) is at most 4.  Measured: two
-// 4096 x 4096 kernels, decode faster through 4 tokens (13.7 vs 16.8 us),
-// within 3% at 6 and 8, slower from 12 (27.1 vs 17.3 us); three 11008 x
-// 4096 kernels, faster through 2 tokens (22.4 vs 26.5 us), slower from 3
-// (33.4 vs 26.7 us).
-constexpr double kAutoDecodeWork = 1.0e8;
+// 4096 x 4096 kernels, decode faster through 4 tokens (14.8 vs 18.3 us),
+// within 3% at 6 and 8 (17.8 vs 18.4, 18.1 vs 18.4 us); three 11008 x 4096
+// kernels, faster through 2 tokens (23.1 vs 28.2 us), slower from 3 (33.8
+// vs 28.3 us).
+constexpr double kAutoDecodeWork = 8.0e7;
 constexpr int64_t kAutoBoolDecodeBlocks = 4;
 
 int resolve_path(int path, int64_t T, int n_terms, int64_t blocks) {

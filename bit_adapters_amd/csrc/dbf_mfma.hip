@@ -70,6 +70,24 @@ __device__ __forceinline__ float scale_from_bound(float b) {
   return ldexpf(1.f, max(-100, min(100, 14 - e)));
 }
 
+// The largest bmax_i * l1_i[tok] over the terms.  Every term slot is loaded
+// (slots past L repeat the last term, which leaves the maximum unchanged), so
+// no load waits behind a loop branch.
+__device__ __forceinline__ float term_bound(const float* bmax, const float* l1, int L, int64_t T,
+                                            int64_t tok) {
+  float b[DBF_MAX_TERMS], l[DBF_MAX_TERMS];
+#pragma unroll
+  for (int i = 0; i < DBF_MAX_TERMS; ++i) {
+    const int ii = min(i, L - 1);
+    b[i] = bmax[ii];
+    l[i] = l1[static_cast<int64_t>(ii) * T + tok];
+  }
+  float bnd = 0.f;
+#pragma unroll
+  for (int i = 0; i < DBF_MAX_TERMS; ++i) bnd = fmaxf(bnd, b[i] * l[i]);
+  return bnd;
+}
+
 // ---- prep: u = fp16(sigma_t gamma . x) in pair order, l1 norms, max |beta|
 //
 // sigma_t (act_scale of the token's largest |gamma_i . x| over every term) is
@@ -449,20 +467,22 @@ gemm_kernel(GemmArgs p) {
   const int term_first = STAGE == 1 ? static_cast<int>(blockIdx.y) : 0;
   const int term_end = STAGE == 1 ? term_first + 1 : p.L;
 
-  if (tid < BM) {
-    // stage 1: the factor s_t / sigma_t of v; stage 2: the divisor s_t of y
-    // (s_t sigma_t when the A operand is u itself)
-    const int64_t tok = tok0 + tid;
-    float ts = 1.f;
-    if (tok < p.T) {
-      float bnd = 0.f;
-      for (int i = 0; i < p.L; ++i)
-        bnd = fmaxf(bnd, p.bmax[i] * p.l1[static_cast<int64_t>(i) * p.T + tok]);
-      ts = scale_from_bound(bnd);
-      if (STAGE == 1) ts /= p.sig[tok];
-      else if (p.sig_div) ts *= p.sig[tok];
+  // Inputs of the epilogue's per-token scale (stage 1: the factor s_t /
+  // sigma_t of v; stage 2: the divisor s_t of y, s_t sigma_t when the A
+  // operand is u itself).  Every thread loads them here (token clamped, term
+  // slots past L repeating the last) and they are used only after the K
+  // loop, so no wait for them stands before the first copies.  A K split
+  // writes raw partial sums and does not use them.
+  float tl1[DBF_MAX_TERMS], tbm[DBF_MAX_TERMS], tsig = 1.f;
+  if (p.nsplit == 1) {
+    const int64_t ttok = min<int64_t>(tok0 + tid % BM, p.T - 1);
+#pragma unroll
+    for (int i = 0; i < DBF_MAX_TERMS; ++i) {
+      const int ii = min(i, p.L - 1);
+      tbm[i] = p.bmax[ii];
+      tl1[i] = p.l1[static_cast<int64_t>(ii) * p.T + ttok];
     }
-    tokscale[tid] = ts;
+    tsig = p.sig[ttok];
   }
 
   const int spt = static_cast<int>(p.kp / BK);  // K steps per term
@@ -525,6 +545,22 @@ gemm_kernel(GemmArgs p) {
   // sign operand is +-1 as in stage 1 (fewer toggling operand bits: the
   // matrix cores run measurably faster on them).
   const bool fold_alpha = STAGE == 2 && p.L > 1;
+  // Column scales with the column clamped (zero past ncols is applied where
+  // they are used), loaded ahead of their use: the epilogue's (beta in
+  // stage 1, alpha of a single term in stage 2) before the K loop, and with
+  // several terms the next term's alpha for the sign fold when a term
+  // starts, so that a term change inside the loop does not wait for memory.
+  int64_t ccol[CB];
+  uint16_t cscale[CB], anext[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    ccol[cb] = min<int64_t>(bcol[cb], p.ncols - 1);
+    cscale[cb] = p.colscale[STAGE == 1 ? term_first : 0][ccol[cb]];
+  }
+  auto load_alpha = [&](int term) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) anext[cb] = p.colscale[min(term, p.L - 1)][ccol[cb]];
+  };
   auto set_term = [&](int term) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -532,7 +568,7 @@ gemm_kernel(GemmArgs p) {
         flip[cb] = 0xFFFFFFFFu;           // bit 1 (+1) -> sign bit 0
         mag[cb] = opaque(0x3C003C00u);    // 1.0, 1.0
       } else {
-        const uint16_t a = bcol[cb] < p.ncols ? p.colscale[term][bcol[cb]] : uint16_t(0);
+        const uint16_t a = bcol[cb] < p.ncols ? anext[cb] : uint16_t(0);
         flip[cb] = (a & 0x8000u) ? 0u : 0xFFFFFFFFu;
         const uint32_t m = a & 0x7FFFu;
         mag[cb] = opaque(m | (m << 16));
@@ -553,7 +589,9 @@ gemm_kernel(GemmArgs p) {
   for (int j = 0; j < NB - 1; ++j)
     if (j < nsteps) issue(j);
   int cterm = term_first + lo / spt, cks = lo % spt;  // compute cursor
+  if (fold_alpha) load_alpha(cterm);
   set_term(cterm);
+  if (fold_alpha) load_alpha(cterm + 1);
   for (int step = 0; step < nsteps; ++step) {
     // this step's copies are done once at most (later steps issued) * LPS
     // of this wave's loads are still in flight; then all waves' are
@@ -611,7 +649,10 @@ gemm_kernel(GemmArgs p) {
     }
     if (STAGE == 2 && ++cks == spt) {
       cks = 0;
-      if (++cterm < term_end) set_term(cterm);
+      if (++cterm < term_end) {
+        set_term(cterm);
+        if (fold_alpha) load_alpha(cterm + 1);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -620,11 +661,23 @@ gemm_kernel(GemmArgs p) {
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the 32 x 32 block.  Each wave
   // stages one 32-column block at a time in its own LDS slice (the stage
   // buffers are free now) and writes it out as 16-byte row chunks.
-  __syncthreads();  // every wave is done with the stage buffers
+  const bool partial = p.nsplit > 1;
+  if (!partial && tid < BM) {
+    float bnd = 0.f;
+#pragma unroll
+    for (int i = 0; i < DBF_MAX_TERMS; ++i) bnd = fmaxf(bnd, tbm[i] * tl1[i]);
+    float ts = 1.f;
+    if (tok0 + tid < p.T) {
+      ts = scale_from_bound(bnd);
+      if (STAGE == 1) ts /= tsig;
+      else if (p.sig_div) ts *= tsig;
+    }
+    tokscale[tid] = ts;
+  }
+  __syncthreads();  // every wave is done with the stage buffers; tokscale written
   unsigned char* wbuf = smem_raw + wv * (BM * 32 * 4);
   // staged element: fp16 v; y as stored, or fp32 when adding to y (one
   // rounding of old + new); fp32 partial sums when K is split
-  const bool partial = p.nsplit > 1;
   const int esize = partial ? 4 : (STAGE == 1 ? 2 : ((p.y_dtype == DBF_F32 || p.accumulate) ? 4 : 2));
   const int cpr = 32 * esize / 16;  // 16-byte chunks per staged row
   const bool vec_y = STAGE == 2 && !p.accumulate && (p.ldy * esize) % 16 == 0;
@@ -641,7 +694,7 @@ gemm_kernel(GemmArgs p) {
         }
     } else if constexpr (STAGE == 1) {
       // v = fp16(s_t * beta_r * acc) at the pair-order position of r
-      const float bsc = bcol[cb] < p.ncols ? f16_bits_to_f32(p.colscale[term_first][bcol[cb]]) : 0.f;
+      const float bsc = bcol[cb] < p.ncols ? f16_bits_to_f32(cscale[cb]) : 0.f;
       const int pos = li < 16 ? 2 * li : 2 * (li - 16) + 1;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -652,7 +705,7 @@ gemm_kernel(GemmArgs p) {
               static_cast<_Float16>(tokscale[rl] * bsc * acc[rb][cb][r]);
         }
     } else {
-      const float asc = (!fold_alpha && bcol[cb] < p.ncols) ? f16_bits_to_f32(p.colscale[0][bcol[cb]]) : 1.f;
+      const float asc = (!fold_alpha && bcol[cb] < p.ncols) ? f16_bits_to_f32(cscale[cb]) : 1.f;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -726,24 +779,6 @@ struct Reduce1Args {
   const float* sig;
   _Float16* v;
 };
-
-// The largest bmax_i * l1_i[tok] over the terms.  Every term slot is loaded
-// (slots past L repeat the last term, which leaves the maximum unchanged), so
-// no load waits behind a loop branch.
-__device__ __forceinline__ float term_bound(const float* bmax, const float* l1, int L, int64_t T,
-                                            int64_t tok) {
-  float b[DBF_MAX_TERMS], l[DBF_MAX_TERMS];
-#pragma unroll
-  for (int i = 0; i < DBF_MAX_TERMS; ++i) {
-    const int ii = min(i, L - 1);
-    b[i] = bmax[ii];
-    l[i] = l1[static_cast<int64_t>(ii) * T + tok];
-  }
-  float bnd = 0.f;
-#pragma unroll
-  for (int i = 0; i < DBF_MAX_TERMS; ++i) bnd = fmaxf(bnd, b[i] * l[i]);
-  return bnd;
-}
 
 // NS = nsplit.  A thread's loads (scales, every split's partials, beta) are
 // all issued before the first of them is used, with addresses clamped into
