@@ -81,6 +81,20 @@ def test_odd_shapes(N, M, K, T, path):
     assert_close(y, ref)
 
 
+# one column tile at one to three tokens: K split 6, 5, 10 and 16 ways on
+# the MFMA path (the split sums are instantiated per count)
+SPLITS = [(100, 768, 2, 3), (128, 1280, 1, 1), (128, 896, 3, 1), (128, 4096, 2, 1)]
+
+
+@pytest.mark.parametrize("N,M,K,T", SPLITS)
+def test_split_counts(N, M, K, T):
+    print("bool split", N, M, K, T, flush=True)
+    layer, x = S.make_custom_bool(N, M, K, T, seed=5 * N + M + K)
+    y = to_np(run(layer, x, MF))
+    ref = O.default().bool_forward(oracle_kernels(layer), x64(x))
+    assert_close(y, ref)
+
+
 @pytest.mark.parametrize("path", [DEC, MF])
 def test_output_dtypes_accumulate_strides(path):
     N, M, K, T = 301, 900, 2, 12

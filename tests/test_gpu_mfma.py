@@ -182,6 +182,26 @@ def test_split_k(N, M, R, L, T):
     assert np.array_equal(a, to_np(run(layer, x)))
 
 
+# The split sums are instantiated per split count (2 .. 16).  Shapes that
+# give every count in the first product (M = 256 s at one token: s splits of
+# two K steps) and in the second (the rest; found with the tile rule at the
+# time of writing), each checked against the oracle with a bf16 output.
+EVERY_SPLIT = ([(128, 256 * s, 128, 1, 1) for s in range(2, 17)] +
+               [(128, 256, 256, 2, 1), (128, 256, 256, 3, 1), (128, 256, 512, 2, 1),
+                (128, 256, 640, 2, 1), (128, 256, 512, 3, 1), (128, 256, 640, 3, 1),
+                (128, 256, 1024, 2, 1), (128, 256, 768, 3, 1), (128, 256, 1280, 2, 1),
+                (2816, 256, 1024, 3, 33), (128, 256, 1024, 3, 1), (2432, 256, 1280, 3, 33),
+                (2304, 256, 1280, 3, 33), (128, 256, 1280, 3, 1), (128, 256, 2048, 2, 1)])
+
+
+@pytest.mark.parametrize("N,M,R,L,T", EVERY_SPLIT)
+def test_every_split_count(N, M, R, L, T):
+    print("mfma every split", N, M, R, L, T, flush=True)
+    layer, x = S.make_custom(N, M, R, L, T, seed=3 * N + M + R + L)
+    ref = O.default().forward(O.terms64(layer), x64(x))
+    assert_close_bf16(to_np(run(layer, x, y_dtype=torch.bfloat16)), ref)
+
+
 def test_split_k_output_dtypes_accumulate_strides():
     N, M, R, L, T = 301, 3000, 300, 2, 20
     layer, x = S.make_custom(N, M, R, L, T, seed=5)
