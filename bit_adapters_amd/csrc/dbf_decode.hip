@@ -361,7 +361,8 @@ __device__ __forceinline__ void stage2_role_waves(const Stage2& p, int64_t bid2,
       const int ent = lane + 64 * e;
       if (ent < TB * G) {
         const int tok = ent / G, g = ent - tok * G;
-        build_signed16<float>(v[e][0], v[e][1], v[e][2], v[e][3], wtbl + (tok * G + g) * 16);
+        build_signed16<float>(v[e][0], v[e][1], v[e][2], v[e][3], wtbl + (tok * G + g) * 16,
+                              tok * G + g);
       }
     }
     wave_lds_sync();

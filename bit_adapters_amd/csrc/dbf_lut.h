@@ -73,14 +73,28 @@ __device__ __forceinline__ V4 load_shared4(const E* p) {
   return v;
 }
 
+// The 16 entries of group gi of a table, E[n] = P[n % 4] + Q[n / 4], written
+// at e = tbl + 16 gi as four 16-byte chunks (entries 4 j .. 4 j + 3 = chunk j).
+// Consecutive lanes build consecutive groups, 64 bytes apart, so chunk j of
+// every lane would fall on the same few banks: each lane writes its chunks in
+// the order j = (c + rot(gi)) % 4, c = 0..3, with rot(gi) = (gi / 2 + gi / 8)
+// % 4.  Any 8 (16) consecutive groups then cover 8 (16) distinct 16-byte bank
+// slots of 32 (64) banks per write, and the layout the lookups read is the
+// plain one.
 template <typename A>
-__device__ __forceinline__ void build_signed16(A a0, A a1, A a2, A a3, A* e) {
+__device__ __forceinline__ void build_signed16(A a0, A a1, A a2, A a3, A* e, int gi) {
+  typedef A A4 __attribute__((ext_vector_type(4)));
   const A p0 = -a0 - a1, p1 = a0 - a1, p2 = a1 - a0, p3 = a0 + a1;
   const A q0 = -a2 - a3, q1 = a2 - a3, q2 = a3 - a2, q3 = a2 + a3;
-  e[0] = p0 + q0;  e[1] = p1 + q0;  e[2] = p2 + q0;  e[3] = p3 + q0;
-  e[4] = p0 + q1;  e[5] = p1 + q1;  e[6] = p2 + q1;  e[7] = p3 + q1;
-  e[8] = p0 + q2;  e[9] = p1 + q2;  e[10] = p2 + q2; e[11] = p3 + q2;
-  e[12] = p0 + q3; e[13] = p1 + q3; e[14] = p2 + q3; e[15] = p3 + q3;
+  const int rot = ((gi >> 1) + (gi >> 3)) & 3;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j = (c + rot) & 3;
+    const A q = (j & 2) ? ((j & 1) ? q3 : q2) : ((j & 1) ? q1 : q0);
+    A4 v;
+    v.x = p0 + q; v.y = p1 + q; v.z = p2 + q; v.w = p3 + q;
+    *reinterpret_cast<A4*>(e + 4 * j) = v;
+  }
 }
 
 template <int KW>
@@ -156,7 +170,7 @@ __device__ __forceinline__ void tables_and_lookups_v(
     const int e = threadIdx.x + i * 64 * NW;
     if (e < TB * ng) {
       const int tok = e / ng, g = e - tok * ng;
-      build_signed16<A>(v[i][0], v[i][1], v[i][2], v[i][3], tbl + (tok * gpp + g) * 16);
+      build_signed16<A>(v[i][0], v[i][1], v[i][2], v[i][3], tbl + (tok * gpp + g) * 16, tok * gpp + g);
     }
   }
   __syncthreads();
