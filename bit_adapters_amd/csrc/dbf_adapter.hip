@@ -18,7 +18,8 @@
 // the base's one, needs no other workgroup, no workspace and no wait, and the
 // wavefronts load one group of features ahead of their MFMAs.  One token
 // (decode) has a kernel of its own, adapter_tok1: stream waves copy W0 into
-// LDS by DMA while rank waves derive w beside them (see there).
+// LDS by DMA (or, for four rank tiles, read it into registers) while rank
+// waves derive w beside them (see there).
 //
 // Larger adapters: workgroups [0, n1) run the decode path's stage 1
 // (dbf_lut.h) for B2 and publish w; the row workgroups stream the base, then
@@ -609,6 +610,11 @@ constexpr int kTok1Threads = 64 * (kMainWaves + kRankWaves);
 // group (128 features).
 constexpr int kTok1Slot = kSteps * 1024 + 256;
 constexpr int kTok1Copies = kSteps + 1;  // DMA instructions per group
+// Stream waves reading W0 into registers: loads of 512 features per row
+// (M up to kVSFeatures)
+constexpr int kVSLoads = 8;
+constexpr int64_t kVSFeatures = 512 * kVSLoads;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // The rank inputs are copied in chunks of 4 groups (1 KiB of x, of gamma,
 // and of the B2 words of each rank tile); chunk c goes to rank wave c % 8.
@@ -655,7 +661,9 @@ template <int L, int QR, int S>
 __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
   constexpr int NQ = L * QR;
   constexpr int C = kTok1Copies;
-  static_assert(L >= 1 && S >= 1 && S <= 3, "terms, ring depth");
+  // S = 0: the stream waves read W0 into registers (M <= kVSFeatures), no ring
+  constexpr bool VS = S == 0;
+  static_assert(L >= 1 && S >= 0 && S <= 3, "terms, ring depth");
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t M = p.M, G = M / kGroup, Gp = tok1_padded_groups(M);
   const int64_t MP = Gp * kGroup;  // features of the padded rank inputs
@@ -707,7 +715,7 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
   const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(ring)) +
                          static_cast<unsigned>(wv * S * kTok1Slot);
   auto issue = [&](int g) {
-    const unsigned sl = ring0 + static_cast<unsigned>((g % S) * kTok1Slot);
+    const unsigned sl = ring0 + static_cast<unsigned>((g % (S > 0 ? S : 1)) * kTok1Slot);
     const int64_t k0 = kbeg + static_cast<int64_t>(g) * kGroup;
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) copy16_to_lds(wj[j] + k0, sl + j * 1024);
@@ -856,6 +864,57 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) pr[(r * NQ + q) * 16 + 4 * lq + rr] = wacc[q][rr] * isig;
     }
+  } else if constexpr (VS) {
+    // ---- stream role, registers: rows 2 wv and 2 wv + 1 of the 16 ------
+    // Each load of a wave reads 1 KiB of one row (512 features, 16 bytes a
+    // lane, consecutive lanes consecutive), as a plain streaming read does;
+    // x of the same features is held in registers, and the row's dot
+    // product is summed over the lanes at the end.  Every load is issued
+    // from an in-bounds address (features past M and rows past N read
+    // feature 0 / row 0) and masked where it is used.
+    const int nl = static_cast<int>((M + 511) / 512);
+    uint4 xr[kVSLoads], wr[2][kVSLoads];
+    const uint16_t* wrow[2];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int64_t rw = n0 + 2 * wv + rr;
+      wrow[rr] = p.w0 + (rw < p.N ? rw : 0) * p.ldw;
+    }
+#pragma unroll
+    for (int j = 0; j < kVSLoads; ++j) {
+      const int64_t k = 512 * j + 8 * lane;
+      const int64_t kc = j < nl && k < M ? k : 0;
+      xr[j] = *reinterpret_cast<const uint4*>(p.x + kc);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int j = 0; j < kVSLoads; ++j) {
+        const int64_t k = 512 * j + 8 * lane;
+        const int64_t kc = j < nl && k < M ? k : 0;
+        wr[rr][j] = *reinterpret_cast<const uint4*>(wrow[rr] + kc);
+      }
+    float sr[2] = {0.f, 0.f};
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int j = 0; j < kVSLoads; ++j) {
+        const bool in = j < nl && 512 * j + 8 * lane < M;
+        const uint4 w = wr[rr][j], xv = xr[j];
+        const uint32_t wa[4] = {w.x, w.y, w.z, w.w}, xa[4] = {xv.x, xv.y, xv.z, xv.w};
+        float d = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa[h]),
+                                              __builtin_bit_cast(bf16x2, xa[h]), d, false);
+        sr[rr] += in ? d : 0.f;
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sr[0] += __shfl_xor(sr[0], off);
+      sr[1] += __shfl_xor(sr[1], off);
+    }
+    if (lane < 16) red[wv * 16 + lane] = lane == 2 * wv ? sr[0] : (lane == 2 * wv + 1 ? sr[1] : 0.f);
   } else {
     // ---- stream role: the wave's share of W0 through the ring ----------
     for (int g = 0; g < pre; ++g) issue(g);
@@ -1012,7 +1071,12 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
     };
     // one token on whole 128-feature groups (16-byte gamma, since it is
     // copied 16 bytes at a time), when the rank inputs fit in LDS beside a
-    // ring of at least 2 groups per stream wave
+    // ring of at least 2 groups per stream wave.  With four rank tiles the
+    // stream waves read W0 into registers instead (no ring; M <= 4096):
+    // there the rank waves bound the call, and they no longer share the
+    // LDS with the ring's copies and reads (measured on 4096^2, one token:
+    // rank 64 10.86 -> 10.19 us; rank 16 9.42 -> 9.67, rank 32 and 48
+    // level, so those keep the ring)
     bool tok1 = T == 1 && sp.fast && M % kGroup == 0 && t.n > 0 &&
                 tok1_padded_groups(M) / kChunkGroups <= kRankWaves * kTok1MaxChunks &&
                 tok1_rank_copies(t.n, static_cast<int>(qr), M) <= 63;
@@ -1020,6 +1084,8 @@ hipError_t launch_adapter(const uint16_t* w0, int64_t ldw, const TermPtrs& t,
       if (reinterpret_cast<uintptr_t>(t.gamma[i]) % 16 != 0) tok1 = false;
 #define DBF_SM(L_, QR_)                                                                     \
   if constexpr (L_ > 0) {                                                                   \
+    if (tok1 && L_ * QR_ >= 4 && M <= kVSFeatures && tok1_lds_bytes<L_, QR_>(0, M) <= kMaxLds) \
+      return go(adapter_tok1<L_, QR_, 0>, tok1_lds_bytes<L_, QR_>(0, M), kTok1Threads);     \
     if (tok1 && tok1_lds_bytes<L_, QR_>(3, M) <= kMaxLds)                                   \
       return go(adapter_tok1<L_, QR_, 3>, tok1_lds_bytes<L_, QR_>(3, M), kTok1Threads);     \
     if (tok1 && tok1_lds_bytes<L_, QR_>(2, M) <= kMaxLds)                                   \

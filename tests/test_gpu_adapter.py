@@ -123,6 +123,24 @@ def test_one_token_staged(N, M, R, L, lo):
     assert_close(_run(layer, x, n_terms=0), base, what="base only")
 
 
+# With four rank tiles and M <= 4096 the one-token kernel's stream waves read
+# W0 rows into registers, 512 features a load: M not a multiple of 512 (a last
+# load with idle lanes), M = 128 (one partial load), ragged rows (N not a
+# multiple of 16), one or two terms.
+@pytest.mark.parametrize("N,M,R,L", [(37, 640, 64, 1), (130, 3968, 64, 1), (20, 128, 50, 1),
+                                     (64, 4096, 32, 2), (16, 4096, 64, 1)])
+def test_one_token_register_stream(N, M, R, L):
+    print("adapter one token, register stream", N, M, R, L, flush=True)
+    layer, x = S.make_custom(N, M, R, L, 1, seed=31, base=True, scale_lo=-0.05, scale_hi=0.05)
+    o = O.default()
+    xx = x64(x)
+    ad = o.forward(O.terms64(layer), xx)
+    base = o.dense(O.widen_bf16(layer["w0"]), xx)
+    assert_close(_run(layer, x), ad + base, what="full")
+    assert_close(_run(layer, x, zero_w0=True), ad, what="adapter only")
+    assert_close(_run(layer, x, n_terms=0), base, what="base only")
+
+
 # The one-token kernel's LDS limit: rank 64 fits with M = 7168 (ring of two
 # groups per stream wave) and not with M = 7296 (the older kernel runs);
 # rank 16 at M = 8192 fits with a ring of three.
