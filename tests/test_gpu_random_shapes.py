@@ -100,3 +100,47 @@ def test_backward(N, M, R, L, T, path):
         assert_close(to_np(da), rda[i], what="dalpha %d" % i)
         assert_close(to_np(db), rdb[i], what="dbeta %d" % i)
         assert_close(to_np(dg), rdg[i], what="dgamma %d" % i)
+
+
+INT8 = [(_size(600), _size(1500), _size(300), int(_g.integers(1, 4)), _size(40))
+        for _ in range(16)]
+MULTI = [(_size(300), _size(1200), _size(64), int(_g.integers(1, 9)), _size(24))
+         for _ in range(12)]
+
+
+@pytest.mark.parametrize("N,M,R,L,T", INT8)
+def test_int8_exact(N, M, R, L, T):
+    # int8 activations, beta = 1: S1 and S2 must match the oracle bit for bit
+    print("random int8", N, M, R, L, T, flush=True)
+    layer, xq = S.make_custom(N, M, R, L, T, seed=N + M + 7 * R + T, x_kind="i8")
+    terms = device_terms(layer, gamma=False, beta=False)
+    xd = torch.from_numpy(xq).to("cuda:0")
+    s1 = torch.empty((L, T, R), dtype=torch.int32, device="cuda:0")
+    s2 = torch.empty((L, T, N), dtype=torch.int32, device="cuda:0")
+    D.dbf_linear_forward_i8(terms, N, M, R, xd, s1=s1, s2=s2)
+    torch.cuda.synchronize()
+    r1, r2 = O.default().forward_int(layer["terms"], xq)
+    assert np.array_equal(s1.cpu().numpy(), r1)
+    assert np.array_equal(s2.cpu().numpy(), r2)
+
+
+@pytest.mark.parametrize("N,M,R,K,T", MULTI)
+def test_multi_adapter(N, M, R, K, T):
+    # token t on adapter idx[t] in [-1, K): -1 is the base alone
+    print("random multi-adapter", N, M, R, K, T, flush=True)
+    ads = [S.make_custom(N, M, R, 1, 1, seed=N * 3 + a, scale_lo=-0.05, scale_hi=0.05)[0]
+           for a in range(K)]
+    layer, x = S.make_custom(N, M, R, 1, T, seed=M + T, base=True)
+    idx = np.random.default_rng([0xDBF, 109, N, T]).integers(-1, K, T).astype(np.int32)
+    adapters = [device_terms(a)[0] for a in ads]
+    it = torch.from_numpy(idx).to("cuda:0")
+    o = O.default()
+    for zero in (False, True):
+        w0 = bf16_dev(layer["w0"])
+        if zero:
+            w0 = torch.zeros_like(w0)
+        y = D.lordba_multi_adapter_forward(w0, adapters, N, M, R, it, x_dev(x))
+        torch.cuda.synchronize()
+        w = np.zeros((N, M)) if zero else O.widen_bf16(layer["w0"])
+        ref = o.multi_adapter(w, [O.terms64(a)[0] for a in ads], idx, x64(x))
+        assert_close(to_np(y), ref, what="W0 = 0" if zero else "with base")
