@@ -724,9 +724,18 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
   const int pre = ng < S ? ng : S;
 
   // Order of issue: a CU serves its memory requests in order, so the rank
-  // waves' inputs go first and the stream waves issue nothing before the
-  // barrier below (measured: with the stream's first groups ahead of them,
-  // rank 16 took 10.8 instead of 10.1 us).
+  // waves' inputs go ahead of most of the stream: the stream waves issue the
+  // rest of their ring only after the barrier below.  With one rank tile the
+  // rank work is short enough to start behind one group of W0 per stream
+  // wave, which then starts the stream a barrier earlier (measured on 4096^2
+  // rank 16, same box, four runs each: 10.05-10.43 -> 9.50-9.73 us; with
+  // the whole ring ahead, 10.3-10.4; with two or more rank tiles even one
+  // group ahead was level or slower).
+  constexpr int kEarly = (!VS && NQ == 1) ? 1 : 0;
+  if constexpr (kEarly > 0) {
+    if (wv < kMainWaves)
+      for (int g = 0; g < min(kEarly, pre); ++g) issue(g);
+  }
   const int64_t nchunk = Gp / kChunkGroups;
   if (wv >= kMainWaves) {
     const unsigned rx0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(rx));
@@ -917,7 +926,7 @@ __global__ void __launch_bounds__(kTok1Threads) adapter_tok1(Small p) {
     if (lane < 16) red[wv * 16 + lane] = lane == 2 * wv ? sr[0] : (lane == 2 * wv + 1 ? sr[1] : 0.f);
   } else {
     // ---- stream role: the wave's share of W0 through the ring ----------
-    for (int g = 0; g < pre; ++g) issue(g);
+    for (int g = min(kEarly, pre); g < pre; ++g) issue(g);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < ng; ++g) {
       wait_groups<C>(min(S - 1, ng - 1 - g));  // the groups issued after g
